@@ -1,0 +1,217 @@
+/*
+ * moe_routed.h -- C ABI of the routed-expert hot path of a block-FP8
+ * Mixture-of-Experts layer, for AMD Instinct MI355X (gfx950).
+ *
+ * Library: libmoe_routed.so (moe_routed_expert_amd/libmoe_routed.so).
+ *
+ * Number formats used by every entry point:
+ *   - fp8 means the OCP e4m3fn byte (bias 7, max 448, 0x7F/0xFF NaN);
+ *   - an activation row of K fp8 bytes carries ceil(K/128) fp32 scales, one
+ *     per 1x128 group; a weight matrix [N][K] carries one fp32 scale per
+ *     128x128 block, laid out [ceil(N/128)][ceil(K/128)];
+ *   - the dequantized value is code * scale, and a scale is amax/448.
+ *
+ * Sources ("page" = one of the descriptions this library is built from):
+ *   [inactive]  "perf(moe): skip inactive block-fp8 decode routes", opening
+ *               section and Validation: a negative slot id marks an inactive
+ *               route; its GEMM output tile is written as zero and nothing
+ *               else of it is read; launch shapes stay fixed and the same
+ *               captured graph must serve all-active, mixed and all-inactive
+ *               steps with inputs changed in place.
+ *   [gather]    "[MoE] Gather the cutlass MoE activation and its scales in
+ *               one launch", Motivation / Modifications / Accuracy Tests:
+ *               one pass over a dst2src map copies the fp8 row bytes and
+ *               the row's k//128 fp32 scales; row bases in 64-bit; tails
+ *               masked (k = 896 has 7 scale groups); an empty map is a no-op.
+ *   [tile]      "perf(dsfp4): pick the grouped-prefill tile from route
+ *               density on sm_89", Measurements / What is not the mechanism /
+ *               Testing: the best M tile follows rows per expert (16, 32,
+ *               128 at about 6, 24, 96 rows) and BLOCK_K is 128; the picker
+ *               is a pure function of route and expert counts.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates, frees and copies nothing, never synchronizes the stream and
+ *     never reads device data on the host, so every call can be captured into
+ *     a hipGraph.  `stream` is a hipStream_t (NULL = the null stream).
+ *   - Sizes and strides are in ELEMENTS of the buffer they describe (bytes for
+ *     fp8 buffers, floats for scale buffers), 64-bit.
+ *   - Every output element named in a call is overwritten; outputs never need
+ *     to be cleared by the caller.
+ *   - Argument checks are host-side and look at scalars and pointers only.
+ *     Device contents are not validated: a slot id >= the number of slots, a
+ *     map entry >= n_src, or offsets that disagree with m_rows are undefined
+ *     behaviour.
+ *   - A call with no work (zero rows) returns MOE_OK without launching.
+ *   - Results are deterministic: no floating-point atomics are used.
+ */
+#ifndef MOE_ROUTED_H
+#define MOE_ROUTED_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,      /* a required pointer is NULL */
+    MOE_ERR_SHAPE = -2,     /* a size, stride, mode or enum is out of range */
+    MOE_ERR_DTYPE = -3,     /* unsupported element type for this argument */
+    MOE_ERR_WORKSPACE = -4, /* workspace too small */
+    MOE_ERR_ALIGN = -5,     /* a pointer or stride breaks the required alignment */
+    MOE_ERR_HIP = -6        /* the HIP runtime rejected the launch */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_F16 = 2 } moe_dtype;
+typedef enum { MOE_ACT_IDENTITY = 0, MOE_ACT_SILU_MUL = 1 } moe_act;
+typedef enum { MOE_MODE_GROUPED = 0, MOE_MODE_SLOT = 1 } moe_gemm_mode;
+
+/* Version of this header the library was built from (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Human-readable text for a moe_status value (static storage). */
+const char* moe_status_string(int status);
+
+/* Text of the last HIP error seen by a launch in this process (static storage). */
+const char* moe_last_hip_error(void);
+
+/*
+ * moe_gather_rows_scales  [gather]
+ *   for i in [0, n_dst):  src = dst2src[i]
+ *     src >= 0: dst_q[i, 0:k] = src_q[src, 0:k]   (bytes, never decoded)
+ *               dst_s[i, 0:g] = src_s[src, 0:g]   (raw 32-bit words)
+ *     src <  0: dst_q[i, 0:k] = 0 and dst_s[i, 0:g] = +0.0
+ *   src_q  [n_src][src_q_stride] bytes;  src_s [n_src][src_s_stride] fp32
+ *   dst_q  [n_dst][dst_q_stride] bytes;  dst_s [n_dst][dst_s_stride] fp32
+ *   g is passed explicitly (normally ceil(k/128)).  Strides >= widths.
+ *   Alignment: none required; 16-byte aligned rows take the vector path.
+ *   n_dst == 0 returns MOE_OK with no launch.
+ */
+int moe_gather_rows_scales(const void* src_q, int64_t src_q_stride,
+                           const float* src_s, int64_t src_s_stride,
+                           int64_t n_src, int64_t k, int64_t g,
+                           const int32_t* dst2src, int64_t n_dst,
+                           void* dst_q, int64_t dst_q_stride,
+                           float* dst_s, int64_t dst_s_stride,
+                           void* stream);
+
+/*
+ * moe_act_quant  -- per-row 1x128 fp8 quantization, optionally of SiLU(gate)*up
+ *   act = MOE_ACT_IDENTITY: v = in[r, c] for c in [0, n)
+ *   act = MOE_ACT_SILU_MUL: in row is [gate(0:n) | up(n:2n)], v = gate/(1+exp(-gate)) * up, fp32
+ *   per group of 128 columns of v (last group may be shorter):
+ *     s = max|v| / 448 (fp32, correctly rounded);  q = (s == 0) ? 0x00 : e4m3_rne(v / s)
+ *   in    [rows][in_stride] of in_dt (MOE_BF16, MOE_F16 or MOE_F32)
+ *   out_q [rows][q_stride] bytes, out_s [rows][s_stride] fp32 (ceil(n/128) used)
+ *   Inputs must be finite.  IDENTITY mode is bit-exact with a correctly
+ *   rounded division and round-to-nearest-even e4m3 encoding; SILU_MUL uses
+ *   the device expf, so its codes may differ by one e4m3 step from a host
+ *   evaluation.  An all-zero group gives s = +0 and q = 0x00 (a zeroed
+ *   inactive-route tile stays zero, [inactive] opening section).
+ */
+int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, int64_t n, int act,
+                  uint8_t* out_q, int64_t q_stride, float* out_s, int64_t s_stride, void* stream);
+
+/*
+ * moe_pick_block_m  [tile]
+ *   The M tile of the grouped GEMM for `routes` routed rows over `experts`
+ *   experts: next power of two of ceil(routes/experts), clamped to [16, 128]
+ *   (about 6, 24, 96 rows per expert give 16, 32, 128).  Pure function.
+ *   Returns 16 when routes or experts is <= 0.
+ */
+int moe_pick_block_m(int64_t routes, int64_t experts);
+
+/*
+ * moe_bf8_grouped_gemm  -- block-FP8 GEMM for the gate/up and the down projections
+ *   ("bf8" = block-FP8 with e4m3 operands.)
+ *   out[r, n] = sum_kb ( sum_{k in kb} A[ar, k] * W[e, n, k] ) * a_s[ar, kb] * w_s[e, n/128, kb]
+ *   with fp8 products exact and fp32 accumulation; one 128-wide K block per scale pair.
+ *   a_q  [*][a_stride] fp8,   a_s [*][a_s_stride] fp32 (K/128 used)
+ *   w_q  [n_experts] x [N][K] fp8: element (e,n,k) at e*w_stride_e + n*w_stride_n + k
+ *   w_s  fp32: block (e,nb,kb) at e*w_s_stride_e + nb*w_s_stride_n + kb
+ *   out  [m_rows][out_stride] of out_dt (MOE_BF16, MOE_F16 or MOE_F32)
+ *   mode MOE_MODE_GROUPED (prefill, [tile]): rows sorted by expert; rows
+ *        [expert_offsets[e], expert_offsets[e+1]) use expert e and A row r;
+ *        expert_offsets is a DEVICE int32 array of n_experts+1 entries with
+ *        expert_offsets[0] = 0 and expert_offsets[n_experts] <= m_rows (rows
+ *        beyond it are left untouched).  block_m = 0 picks the M tile with
+ *        moe_pick_block_m(m_rows, n_experts); 16, 32, 64 or 128 forces it.
+ *   mode MOE_MODE_SLOT (decode, [inactive]): row r uses slot slot_ids[r]
+ *        (DEVICE int32 [m_rows]) and A row r / a_row_div; a negative slot
+ *        writes a +0 output row and reads no A, W or scales of that row.
+ *        Meant for decode-sized row counts (every row streams its expert).
+ *   Requirements: K % 128 == 0, N % 16 == 0; w_q, a_q and their strides
+ *   16-byte aligned (MOE_ERR_ALIGN otherwise).  n_experts == 0 with NULL
+ *   w_q/w_s is allowed in slot mode (an empty bank: every slot must be < 0).
+ */
+int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                         const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
+                         const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n,
+                         int64_t n_experts, int64_t N, int64_t K,
+                         int mode, const int32_t* expert_offsets, const int32_t* slot_ids,
+                         int64_t m_rows, int64_t a_row_div, int32_t block_m,
+                         void* out, int out_dt, int64_t out_stride, void* stream);
+
+/*
+ * moe_topk_reduce  -- routing-weighted sum over each token's top-k routes
+ *   out[t, h] = bf16_rne( sum_{j = 0..topk-1, slot_ids[t,j] >= 0} weights[t,j] * y[row(t,j), h] )
+ *   summed in fp32 in ascending j from +0; row(t,j) = route_rows[t*topk + j]
+ *   (DEVICE int32) or t*topk + j when route_rows is NULL.  The weight of an
+ *   inactive route is never read ([inactive] opening section).  A token with
+ *   no active route gets +0.0.
+ *   y [*][y_stride] of y_dt;  slot_ids, weights [T][topk];  out [T][out_stride] bf16.
+ */
+int moe_topk_reduce(const void* y, int y_dt, int64_t y_stride,
+                    const int32_t* slot_ids, const int32_t* route_rows, const float* weights,
+                    int64_t T, int64_t topk, int64_t H, uint16_t* out_bf16, int64_t out_stride,
+                    void* stream);
+
+/*
+ * Fused decode workspace.  Layout (byte offsets written to offsets[0..7]):
+ *   [0] xq   T x H            fp8 of the quantized token rows
+ *   [1] xs   T x ceil(H/128)  fp32
+ *   [2] c1   R x 2I           fp32 gate/up output (R = T*topk routes)
+ *   [3] aq   R x I            fp8 activation
+ *   [4] as   R x ceil(I/128)  fp32
+ *   [5] c2   R x H            fp32 down output
+ *   [6] ctl  control words (arrival counters)
+ *   [7] total size
+ * Regions [0]..[5] may hold anything between calls (they are fully rewritten;
+ * inactive routes' c1/aq/as/c2 rows become exact zeros).  The control region
+ * must be cleared once with moe_fused_decode_workspace_init before the first
+ * call; every call leaves it cleared again.
+ */
+size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk);
+int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[8]);
+int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes, int64_t T, int64_t H, int64_t I,
+                                    int64_t topk, void* stream);
+
+/*
+ * moe_fused_decode  -- one decode step of the routed experts  [inactive]
+ *   x (T x H bf16) -> 1x128 fp8 quant -> gate/up GEMM per route (slot mode,
+ *   A row = token) -> SiLU(gate)*up + 1x128 requant -> down GEMM per route
+ *   -> routing-weighted top-k reduce -> out (T x H bf16).
+ *   slot_ids, weights: DEVICE [T][topk]; slot < 0 = inactive route (zero
+ *   c1/act/c2 tiles, no reads of its weights, scales or routing weight).
+ *   w13_q [n_slots][2I][H] fp8 (gate rows 0..I-1, up rows I..2I-1), contiguous;
+ *   w13_s [n_slots][ceil(2I/128)][ceil(H/128)] fp32;  w2_q [n_slots][H][I];
+ *   w2_s [n_slots][ceil(H/128)][ceil(I/128)].
+ *   Requirements: H % 128 == 0, I % 128 == 0, 1 <= topk <= 64; 16-byte
+ *   aligned weights and workspace.  Launch shapes depend on (T, H, I, topk)
+ *   only, so one captured graph serves any slot/weight/x contents.
+ */
+int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk,
+                     const int32_t* slot_ids, const float* weights, int64_t n_slots,
+                     const uint8_t* w13_q, const float* w13_s,
+                     const uint8_t* w2_q, const float* w2_s,
+                     void* workspace, size_t ws_bytes, uint16_t* out_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_ROUTED_H */
