@@ -172,22 +172,21 @@ int moe_topk_reduce(const void* y, int y_dt, int64_t y_stride,
                     void* stream);
 
 /*
- * Fused decode workspace.  Layout (byte offsets written to offsets[0..7]):
- *   [0] xq   T x H            fp8 of the quantized token rows
- *   [1] xs   T x ceil(H/128)  fp32
- *   [2] c1   R x 2I           fp32 gate/up output (R = T*topk routes)
- *   [3] aq   R x I            fp8 activation
- *   [4] as   R x ceil(I/128)  fp32
- *   [5] c2   R x H            fp32 down output
- *   [6] ctl  control words (arrival counters)
- *   [7] total size
- * Regions [0]..[5] may hold anything between calls (they are fully rewritten;
- * inactive routes' c1/aq/as/c2 rows become exact zeros).  The control region
- * must be cleared once with moe_fused_decode_workspace_init before the first
- * call; every call leaves it cleared again.
+ * Fused decode workspace.  Layout (byte offsets written to offsets[0..5]):
+ *   [0] c1   R x 2I           fp32 gate/up output (R = T*topk routes)
+ *   [1] aq   R x I            fp8 activation
+ *   [2] as   R x ceil(I/128)  fp32 activation scales
+ *   [3] c2   R x H            fp32 down output
+ *   [4] ctl  control words
+ *   [5] total size in bytes
+ * Regions [0]..[3] may hold anything between calls: every call rewrites them
+ * completely, and an inactive route's c1/aq/as/c2 rows become exact zeros.
+ * The control region must be cleared once with moe_fused_decode_workspace_init
+ * before the first call; calls leave it cleared.  Size 0 / MOE_ERR_SHAPE for
+ * shapes moe_fused_decode rejects.
  */
 size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk);
-int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[8]);
+int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[6]);
 int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes, int64_t T, int64_t H, int64_t I,
                                     int64_t topk, void* stream);
 
@@ -201,8 +200,8 @@ int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes, int64_t T,
  *   w13_q [n_slots][2I][H] fp8 (gate rows 0..I-1, up rows I..2I-1), contiguous;
  *   w13_s [n_slots][ceil(2I/128)][ceil(H/128)] fp32;  w2_q [n_slots][H][I];
  *   w2_s [n_slots][ceil(H/128)][ceil(I/128)].
- *   Requirements: H % 128 == 0, I % 128 == 0, 1 <= topk <= 64; 16-byte
- *   aligned weights and workspace.  Launch shapes depend on (T, H, I, topk)
+ *   Requirements: H % 128 == 0, I % 128 == 0, 1 <= topk <= 64,
+ *   T * topk <= 65535; 16-byte aligned weights and workspace, 4-byte aligned x.  Launch shapes depend on (T, H, I, topk)
  *   only, so one captured graph serves any slot/weight/x contents.
  */
 int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk,

@@ -1,0 +1,195 @@
+// Host entry points of libmoe_routed that are not tied to one kernel file:
+// status text, the M-tile picker, argument checks of the block-FP8 GEMM, and
+// the fused decode step with its workspace.
+#include <string.h>
+
+#include "device.h"
+#include "host.h"
+
+namespace moe {
+
+int slot_gemm_launch(hipStream_t st, bool a_is_bf16, const void* a, int64_t a_stride, const float* a_s,
+                     int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
+                     const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int64_t N, int64_t K,
+                     const int32_t* slots, int64_t rows, int64_t a_row_div, void* out, int out_dt,
+                     int64_t out_stride);
+int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t a_stride, const float* a_s,
+                        int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
+                        const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int64_t E, int64_t N,
+                        int64_t K, const int32_t* offsets, int64_t m_rows, void* out, int out_dt,
+                        int64_t out_stride);
+int topk_reduce_launch(hipStream_t st, const void* y, int y_dt, int64_t y_stride, const int32_t* slot_ids,
+                       const int32_t* route_rows, const float* weights, int64_t T, int64_t topk, int64_t H,
+                       uint16_t* out, int64_t out_stride);
+
+static char g_last_hip_error[256] = "no HIP error recorded";
+
+void note_hip_error(hipError_t e) {
+    const char* s = hipGetErrorString(e);
+    strncpy(g_last_hip_error, s ? s : "unknown HIP error", sizeof(g_last_hip_error) - 1);
+    g_last_hip_error[sizeof(g_last_hip_error) - 1] = 0;
+}
+
+namespace {
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+struct DecodeLayout {
+    int64_t off[6];   // c1, aq, as, c2, ctl, total
+};
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+DecodeLayout decode_layout(int64_t T, int64_t H, int64_t I, int64_t topk) {
+    const int64_t R = T * topk;
+    DecodeLayout L;
+    int64_t o = 0;
+    L.off[0] = o; o = align256(o + R * 2 * I * 4);            // c1 f32
+    L.off[1] = o; o = align256(o + R * I);                    // aq fp8
+    L.off[2] = o; o = align256(o + R * ceil_div(I, 128) * 4); // as f32
+    L.off[3] = o; o = align256(o + R * H * 4);                // c2 f32
+    L.off[4] = o; o = align256(o + 256);                      // ctl
+    L.off[5] = o;
+    return L;
+}
+
+bool decode_shape_ok(int64_t T, int64_t H, int64_t I, int64_t topk) {
+    return T >= 0 && H > 0 && I > 0 && topk >= 1 && topk <= 64 && H % 128 == 0 && I % 128 == 0 &&
+           T * topk <= 65535;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+extern "C" const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "a required pointer is NULL";
+        case MOE_ERR_SHAPE: return "a size, stride, mode or enum is out of range";
+        case MOE_ERR_DTYPE: return "unsupported element type";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_ALIGN: return "a pointer or stride breaks the required 16-byte alignment";
+        case MOE_ERR_HIP: return "the HIP runtime rejected a launch (see moe_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char* moe_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" int moe_pick_block_m(int64_t routes, int64_t experts) {
+    if (routes <= 0 || experts <= 0) return 16;
+    const int64_t per = ceil_div(routes, experts);
+    int64_t bm = 16;
+    while (bm < per && bm < 128) bm <<= 1;
+    return (int)bm;
+}
+
+extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                                    const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
+                                    const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n,
+                                    int64_t n_experts, int64_t N, int64_t K,
+                                    int mode, const int32_t* expert_offsets, const int32_t* slot_ids,
+                                    int64_t m_rows, int64_t a_row_div, int32_t block_m,
+                                    void* out, int out_dt, int64_t out_stride, void* stream) {
+    if (mode != MOE_MODE_GROUPED && mode != MOE_MODE_SLOT) return MOE_ERR_SHAPE;
+    if (!dtype_ok(out_dt)) return MOE_ERR_DTYPE;
+    if (m_rows < 0 || n_experts < 0 || N <= 0 || K <= 0) return MOE_ERR_SHAPE;
+    if (K % 128 != 0 || N % 16 != 0) return MOE_ERR_SHAPE;
+    if (m_rows == 0) return MOE_OK;
+    if (!out) return MOE_ERR_NULL;
+    if (out_stride < N) return MOE_ERR_SHAPE;
+    const int64_t kb = K / 128, nb = ceil_div(N, 128);
+    const bool empty_bank = n_experts == 0;
+    if (!empty_bank) {
+        if (!w_q || !w_s || !a_q || !a_s) return MOE_ERR_NULL;
+        if (w_stride_n < K || a_stride < K || a_s_stride < kb || w_s_stride_n < kb) return MOE_ERR_SHAPE;
+        if (n_experts > 1 && (w_stride_e < N * w_stride_n || w_s_stride_e < nb * w_s_stride_n)) return MOE_ERR_SHAPE;
+        if (!aligned16(w_q) || !aligned16(a_q) || w_stride_n % 16 || w_stride_e % 16 || a_stride % 16)
+            return MOE_ERR_ALIGN;
+    }
+    auto st = as_stream(stream);
+    if (mode == MOE_MODE_SLOT) {
+        if (!slot_ids) return MOE_ERR_NULL;
+        if (a_row_div < 1) return MOE_ERR_SHAPE;
+        return slot_gemm_launch(st, false, a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, w_s,
+                                w_s_stride_e, w_s_stride_n, N, K, slot_ids, m_rows, a_row_div, out, out_dt,
+                                out_stride);
+    }
+    if (empty_bank) return MOE_ERR_SHAPE;
+    if (!expert_offsets) return MOE_ERR_NULL;
+    if (N % 128 != 0) return MOE_ERR_SHAPE;
+    int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
+    if (bm != 16 && bm != 32 && bm != 64 && bm != 128) return MOE_ERR_SHAPE;
+    return grouped_gemm_launch(st, bm, a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, w_s,
+                               w_s_stride_e, w_s_stride_n, n_experts, N, K, expert_offsets, m_rows, out, out_dt,
+                               out_stride);
+}
+
+extern "C" size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk) {
+    if (!decode_shape_ok(T, H, I, topk)) return 0;
+    return (size_t)decode_layout(T, H, I, topk).off[5];
+}
+
+extern "C" int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[6]) {
+    if (!offsets) return MOE_ERR_NULL;
+    if (!decode_shape_ok(T, H, I, topk)) return MOE_ERR_SHAPE;
+    DecodeLayout L = decode_layout(T, H, I, topk);
+    for (int i = 0; i < 6; i++) offsets[i] = L.off[i];
+    return MOE_OK;
+}
+
+extern "C" int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes, int64_t T, int64_t H, int64_t I,
+                                               int64_t topk, void* stream) {
+    if (!decode_shape_ok(T, H, I, topk)) return MOE_ERR_SHAPE;
+    if (!workspace) return MOE_ERR_NULL;
+    DecodeLayout L = decode_layout(T, H, I, topk);
+    if ((int64_t)ws_bytes < L.off[5]) return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MOE_ERR_ALIGN;
+    const int64_t words = (L.off[5] - L.off[4]) / 4;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, as_stream(stream),
+                       (uint32_t*)((char*)workspace + L.off[4]), words, 0u);
+    return launch_status();
+}
+
+extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk,
+                                const int32_t* slot_ids, const float* weights, int64_t n_slots,
+                                const uint8_t* w13_q, const float* w13_s,
+                                const uint8_t* w2_q, const float* w2_s,
+                                void* workspace, size_t ws_bytes, uint16_t* out_bf16, void* stream) {
+    if (!decode_shape_ok(T, H, I, topk) || n_slots < 0) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    if (!x_bf16 || !slot_ids || !weights || !workspace || !out_bf16) return MOE_ERR_NULL;
+    if (n_slots > 0 && (!w13_q || !w13_s || !w2_q || !w2_s)) return MOE_ERR_NULL;
+    DecodeLayout L = decode_layout(T, H, I, topk);
+    if ((int64_t)ws_bytes < L.off[5]) return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace) || (n_slots > 0 && (!aligned16(w13_q) || !aligned16(w2_q))) ||
+        (reinterpret_cast<uintptr_t>(x_bf16) & 3u))
+        return MOE_ERR_ALIGN;
+    const int64_t R = T * topk;
+    char* ws = (char*)workspace;
+    float* c1 = (float*)(ws + L.off[0]);
+    uint8_t* aq = (uint8_t*)(ws + L.off[1]);
+    float* as = (float*)(ws + L.off[2]);
+    float* c2 = (float*)(ws + L.off[3]);
+    const int64_t gH = H / 128, gI = I / 128, g2I = 2 * I / 128;
+    auto st = as_stream(stream);
+    // 1) gate/up per route, quantizing the bf16 token row on the fly
+    int rc = slot_gemm_launch(st, true, x_bf16, H, nullptr, 0, w13_q, 2 * I * H, H, w13_s, g2I * gH, gH, 2 * I, H,
+                              slot_ids, R, topk, c1, MOE_F32, 2 * I);
+    // 2) SiLU(gate)*up + 1x128 requant over every route (zero tiles stay zero)
+    if (rc == MOE_OK) rc = moe_act_quant(c1, MOE_F32, 2 * I, R, I, MOE_ACT_SILU_MUL, aq, I, as, gI, stream);
+    // 3) down per route
+    if (rc == MOE_OK)
+        rc = slot_gemm_launch(st, false, aq, I, as, gI, w2_q, H * I, I, w2_s, gH * gI, gI, H, I, slot_ids, R, 1, c2,
+                              MOE_F32, H);
+    // 4) routing-weighted reduce
+    if (rc == MOE_OK) rc = topk_reduce_launch(st, c2, MOE_F32, H, slot_ids, nullptr, weights, T, topk, H, out_bf16, H);
+    return rc;
+}

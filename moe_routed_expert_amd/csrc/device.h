@@ -1,0 +1,101 @@
+// Device-side helpers shared by the gfx950 kernels of libmoe_routed.
+//
+// fp8 here is the OCP e4m3fn byte.  gfx950's v_cvt_pk_fp8_f32 rounds to
+// nearest-even but turns magnitudes above 464 into NaN, so every encode
+// clamps to +-448 first; with finite inputs that gives round-to-nearest-even
+// with saturation.  v_cvt_pk_f32_fp8 decodes exactly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float clamp448(float v) {
+    return __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+}
+
+// Four fp32 values -> four e4m3 bytes packed little-endian into one word.
+__device__ __forceinline__ uint32_t enc4_e4m3(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+    return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint32_t enc2_e4m3(float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false) & 0xFFFFu;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+    uint32_t x = __float_as_uint(v);
+    if ((x & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((x >> 16) | 0x40u);
+    x += 0x7FFFu + ((x >> 16) & 1u);
+    return (uint16_t)(x >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float v) {
+    _Float16 h = (_Float16)v;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Element types of 16/32-bit float buffers (values of moe_dtype).
+enum : int { kBF16 = 0, kF32 = 1, kF16 = 2 };
+
+template <int DT>
+__device__ __forceinline__ float load_as_f32(const void* p, int64_t i) {
+    if constexpr (DT == kF32) return ((const float*)p)[i];
+    else if constexpr (DT == kBF16) return bf16_to_f32(((const uint16_t*)p)[i]);
+    else return f16_to_f32(((const uint16_t*)p)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_from_f32(void* p, int64_t i, float v) {
+    if constexpr (DT == kF32) ((float*)p)[i] = v;
+    else if constexpr (DT == kBF16) ((uint16_t*)p)[i] = f32_to_bf16(v);
+    else ((uint16_t*)p)[i] = f32_to_f16(v);
+}
+
+// Max over aligned groups of 2^LOG lanes (butterfly; every lane gets the group max).
+template <int LOG>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (int m = 1; m < (1 << LOG); m <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, m, kWave));
+    return v;
+}
+
+// 16x16x128 fp8 x fp8 -> fp32 MFMA (e4m3 operands, no block exponent scaling).
+// Operand layout (checked on gfx950): lane l holds row (A) / column (B) l%16 and
+// 32 K values for K-quarter l/16; both operands use the same K order, so any
+// fixed assignment of 32 K positions per K-quarter works as long as A and B
+// agree.  Result: lane l, element i = C[4*(l/16)+i][l%16].
+__device__ __forceinline__ v4f mfma16x16x128_e4m3(const v8i& a, const v8i& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Orders this wave's LDS accesses before/after the call (compiler and memory
+// model, wavefront scope).  Valid only for data written and read by one wave.
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace moe

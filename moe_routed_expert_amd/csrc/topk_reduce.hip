@@ -1,0 +1,80 @@
+// Routing-weighted reduce of each token's top-k route outputs ("perf(moe):
+// skip inactive block-fp8 decode routes", opening section: the reduction reads
+// the route buffers, and a negative slot's routing weight is never read).
+//
+// MI355X design: HBM-bound elementwise pass.  A thread owns 4 consecutive
+// hidden columns of one token, walks the top-k routes in ascending order with
+// an fp32 accumulator (the order is fixed, so results are deterministic), and
+// writes 4 bf16 values with one 8-byte store.  Slot ids and routing weights of
+// the token are wave-uniform loads.
+#include "device.h"
+#include "host.h"
+
+namespace moe {
+namespace {
+
+template <int DT>
+__global__ void __launch_bounds__(256)
+topk_reduce_kernel(const void* __restrict__ y, int64_t y_stride, const int32_t* __restrict__ slot_ids,
+                   const int32_t* __restrict__ route_rows, const float* __restrict__ weights, int64_t T,
+                   int64_t topk, int64_t H, uint16_t* __restrict__ out, int64_t out_stride) {
+    const int64_t chunks = ceil_div(H, 4);
+    const int64_t t = blockIdx.y;
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T || c >= chunks) return;
+    const int64_t h0 = c * 4;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t j = 0; j < topk; j++) {
+        const int64_t rt = t * topk + j;
+        if (slot_ids[rt] < 0) continue;           // inactive: weight and rows untouched
+        const float w = weights[rt];
+        const int64_t row = route_rows ? (int64_t)route_rows[rt] : rt;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+            if (h0 + i < H) acc[i] += w * load_as_f32<DT>(y, row * y_stride + h0 + i);
+    }
+    uint16_t* o = out + t * out_stride + h0;
+    if (h0 + 4 <= H && (reinterpret_cast<uintptr_t>(o) & 7u) == 0) {
+        const uint32_t lo = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+        *reinterpret_cast<uint2*>(o) = make_uint2(lo, hi);
+    } else {
+        for (int i = 0; i < 4 && h0 + i < H; i++) o[i] = f32_to_bf16(acc[i]);
+    }
+}
+
+}  // namespace
+
+int topk_reduce_launch(hipStream_t st, const void* y, int y_dt, int64_t y_stride, const int32_t* slot_ids,
+                       const int32_t* route_rows, const float* weights, int64_t T, int64_t topk, int64_t H,
+                       uint16_t* out, int64_t out_stride) {
+    const int64_t chunks = ceil_div(H, 4);
+    dim3 grid((unsigned)ceil_div(chunks, 256), (unsigned)T);
+    if (y_dt == MOE_F32)
+        hipLaunchKernelGGL(topk_reduce_kernel<kF32>, grid, dim3(256), 0, st, y, y_stride, slot_ids, route_rows,
+                           weights, T, topk, H, out, out_stride);
+    else if (y_dt == MOE_BF16)
+        hipLaunchKernelGGL(topk_reduce_kernel<kBF16>, grid, dim3(256), 0, st, y, y_stride, slot_ids, route_rows,
+                           weights, T, topk, H, out, out_stride);
+    else
+        hipLaunchKernelGGL(topk_reduce_kernel<kF16>, grid, dim3(256), 0, st, y, y_stride, slot_ids, route_rows,
+                           weights, T, topk, H, out, out_stride);
+    return launch_status();
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" int moe_topk_reduce(const void* y, int y_dt, int64_t y_stride, const int32_t* slot_ids,
+                               const int32_t* route_rows, const float* weights, int64_t T, int64_t topk,
+                               int64_t H, uint16_t* out_bf16, int64_t out_stride, void* stream) {
+    if (T < 0 || topk < 0 || H < 0) return MOE_ERR_SHAPE;
+    if (!dtype_ok(y_dt)) return MOE_ERR_DTYPE;
+    if (T == 0 || H == 0) return MOE_OK;
+    if (!out_bf16 || (topk > 0 && (!slot_ids || !weights || !y))) return MOE_ERR_NULL;
+    if (out_stride < H || (topk > 0 && y_stride < H)) return MOE_ERR_SHAPE;
+    if (T > 65535) return MOE_ERR_SHAPE;
+    return topk_reduce_launch(as_stream(stream), y, y_dt, y_stride, slot_ids, route_rows, weights, T, topk, H,
+                              out_bf16, out_stride);
+}

@@ -1,0 +1,136 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before any launch."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import moe_routed_expert_amd as m
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_routed.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("moe_gather_rows_scales", "moe_bf8_grouped_gemm", "moe_act_quant", "moe_topk_reduce",
+                 "moe_fused_decode", "moe_pick_block_m", "moe_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = m.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(m.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    assert m.abi_version() == 1
+    L = m.lib()
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert L.moe_status_string(st).decode() not in ("", "unknown status")
+    assert L.moe_status_string(7).decode() == "unknown status"
+
+
+def test_pick_block_m_reproduces_the_page_table():
+    spec = json.load(open(os.path.join(ROOT, "tests", "golden", "tile_picker_density.json")))
+    for c in spec["cases"]:
+        assert m.pick_block_m(c["routes"], spec["experts"]) == c["block_m"], c
+    # monotone in density and clamped to [16, 128]
+    last = 0
+    for r in range(0, 100000, 97):
+        bm = m.pick_block_m(r, 256)
+        assert bm in (16, 32, 64, 128) and bm >= last
+        last = bm
+    assert m.pick_block_m(0, 256) == 16 and m.pick_block_m(10, 0) == 16
+    assert m.pick_block_m(256 * 1000, 256) == 128
+
+
+P = ctypes.c_void_p
+FAKE = P(0x1000)       # never dereferenced: every call below fails validation first
+
+
+def gemm(**kw):
+    a = dict(a_q=FAKE, a_stride=256, a_s=FAKE, a_s_stride=2, w_q=FAKE, w_stride_e=256 * 256, w_stride_n=256,
+             w_s=FAKE, w_s_stride_e=4, w_s_stride_n=2, n_experts=4, N=256, K=256, mode=1, expert_offsets=FAKE,
+             slot_ids=FAKE, m_rows=8, a_row_div=1, block_m=0, out=FAKE, out_dt=1, out_stride=256, stream=None)
+    a.update(kw)
+    return m.lib().moe_bf8_grouped_gemm(*a.values())
+
+
+def test_gemm_argument_checks():
+    assert gemm(K=200) == m.MOE_ERR_SHAPE          # K % 128
+    assert gemm(N=200) == m.MOE_ERR_SHAPE          # N % 16
+    assert gemm(mode=5) == m.MOE_ERR_SHAPE
+    assert gemm(out_dt=9) == m.MOE_ERR_DTYPE
+    assert gemm(m_rows=0) == m.MOE_OK              # no work, no launch
+    assert gemm(out=None) == m.MOE_ERR_NULL
+    assert gemm(w_q=None) == m.MOE_ERR_NULL
+    assert gemm(slot_ids=None) == m.MOE_ERR_NULL
+    assert gemm(a_row_div=0) == m.MOE_ERR_SHAPE
+    assert gemm(w_q=P(0x1001)) == m.MOE_ERR_ALIGN
+    assert gemm(a_stride=264, w_stride_n=264, w_stride_e=264 * 256) == m.MOE_ERR_ALIGN
+    assert gemm(w_stride_n=128) == m.MOE_ERR_SHAPE  # stride < K
+    assert gemm(out_stride=100) == m.MOE_ERR_SHAPE
+    assert gemm(mode=0, expert_offsets=None) == m.MOE_ERR_NULL
+    assert gemm(mode=0, N=144) == m.MOE_ERR_SHAPE  # grouped mode needs N % 128
+    assert gemm(mode=0, block_m=48) == m.MOE_ERR_SHAPE
+    assert gemm(mode=0, n_experts=0, w_q=None, w_s=None) == m.MOE_ERR_SHAPE
+
+
+def test_gather_act_reduce_argument_checks():
+    L = m.lib()
+    # empty map: OK without launching, even with NULL buffers
+    assert L.moe_gather_rows_scales(None, 0, None, 0, 0, 7168, 56, None, 0, None, 0, None, 0, None) == m.MOE_OK
+    assert L.moe_gather_rows_scales(FAKE, 16, FAKE, 1, 4, 32, 1, None, 8, FAKE, 32, FAKE, 1, None) == m.MOE_ERR_NULL
+    assert L.moe_gather_rows_scales(FAKE, 16, FAKE, 1, 4, 32, 1, FAKE, 8, FAKE, 32, FAKE, 1, None) == m.MOE_ERR_SHAPE
+    assert L.moe_gather_rows_scales(FAKE, 32, FAKE, 1, 0, 32, 1, FAKE, 8, FAKE, 32, FAKE, 1, None) == m.MOE_ERR_SHAPE
+    assert L.moe_act_quant(FAKE, 7, 256, 4, 256, 0, FAKE, 256, FAKE, 2, None) == m.MOE_ERR_DTYPE
+    assert L.moe_act_quant(FAKE, 0, 256, 4, 256, 3, FAKE, 256, FAKE, 2, None) == m.MOE_ERR_SHAPE
+    assert L.moe_act_quant(FAKE, 0, 256, 4, 256, 1, FAKE, 256, FAKE, 2, None) == m.MOE_ERR_SHAPE  # SILU needs 2n
+    assert L.moe_act_quant(FAKE, 0, 256, 0, 256, 0, None, 256, None, 2, None) == m.MOE_OK
+    assert L.moe_act_quant(FAKE, 0, 256, 4, 256, 0, None, 256, FAKE, 2, None) == m.MOE_ERR_NULL
+    assert L.moe_topk_reduce(FAKE, 1, 64, FAKE, None, FAKE, 4, 8, 128, FAKE, 128, None) == m.MOE_ERR_SHAPE
+    assert L.moe_topk_reduce(FAKE, 5, 128, FAKE, None, FAKE, 4, 8, 128, FAKE, 128, None) == m.MOE_ERR_DTYPE
+    assert L.moe_topk_reduce(FAKE, 1, 128, FAKE, None, FAKE, 0, 8, 128, FAKE, 128, None) == m.MOE_OK
+
+
+def test_fused_decode_workspace_and_checks():
+    L = m.lib()
+    lay = m.fused_decode_workspace_layout(1, 2048, 768, 8)
+    assert lay["c1"] == 0
+    assert lay["aq"] >= 8 * 1536 * 4 and lay["as"] >= lay["aq"] + 8 * 768
+    assert lay["c2"] >= lay["as"] + 8 * 6 * 4 and lay["ctl"] >= lay["c2"] + 8 * 2048 * 4
+    assert lay["total"] == m.fused_decode_workspace_size(1, 2048, 768, 8)
+    assert all(v % 256 == 0 for v in lay.values())
+    assert m.fused_decode_workspace_size(1, 2000, 768, 8) == 0          # H % 128
+    assert m.fused_decode_workspace_size(1, 2048, 768, 0) == 0          # topk >= 1
+    size = lay["total"]
+    args = [FAKE, 1, 2048, 768, 8, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, size, FAKE, None]
+    a = list(args); a[13] = size - 1
+    assert L.moe_fused_decode(*a) == m.MOE_ERR_WORKSPACE
+    a = list(args); a[12] = P(0x1008)
+    assert L.moe_fused_decode(*a) == m.MOE_ERR_ALIGN
+    a = list(args); a[0] = None
+    assert L.moe_fused_decode(*a) == m.MOE_ERR_NULL
+    a = list(args); a[2] = 2000
+    assert L.moe_fused_decode(*a) == m.MOE_ERR_SHAPE
+    a = list(args); a[1] = 0
+    assert L.moe_fused_decode(*a) == m.MOE_OK
+    assert L.moe_fused_decode_workspace_init(FAKE, size - 1, 1, 2048, 768, 8, None) == m.MOE_ERR_WORKSPACE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(m, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        m.lib()

@@ -1,0 +1,172 @@
+"""GPU parity of the fused decode step against the CPU oracle, including inactive (-1)
+routes, NaN-poisoned workspaces and hipGraph replay with inputs changed in place
+("perf(moe): skip inactive block-fp8 decode routes", Validation)."""
+import numpy as np
+import pytest
+import torch
+
+import moe_routed_expert_amd as m
+import oracle
+import workloads as wl
+from gpu_util import assert_bf16_close, assert_close, assert_within_bound, dev, gemm_abs_bound, to_dev, u16
+
+
+pytestmark = pytest.mark.gpu
+
+
+class DevDecode:
+    """A decode case resident on the GPU, with its workspace and output."""
+
+    def __init__(self, c: wl.DecodeCase):
+        d = dev()
+        self.c = c
+        self.x = c.x.to(d)
+        self.slots = to_dev(c.slot_ids)
+        self.w = to_dev(c.weights)
+        self.wts = [t.to(d) for t in (c.w13_q, c.w13_s, c.w2_q, c.w2_s)]
+        self.ws = m.fused_decode_workspace(c.T, c.H, c.I, c.topk, device=d)
+        self.lay = m.fused_decode_workspace_layout(c.T, c.H, c.I, c.topk)
+        self.out = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=d)
+
+    def run(self):
+        m.fused_decode(self.x, self.slots, self.w, *self.wts, self.ws, self.out)
+
+    def region(self, name, dtype, shape):
+        nbytes = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        return self.ws[self.lay[name]:self.lay[name] + nbytes].view(dtype).view(shape)
+
+    def poison(self):
+        self.ws[:self.lay["ctl"]].fill_(0xFF)          # NaN in every fp32 word, 0xFF codes
+        self.out.fill_(float("nan"))
+
+
+def oracle_decode(c: wl.DecodeCase, slots=None, weights=None, host_weights=None):
+    xb = c.x.view(torch.int16).numpy().view(np.uint16)
+    hw = host_weights or [t.cpu().numpy() for t in (c.w13_q, c.w13_s, c.w2_q, c.w2_s)]
+    return oracle.fused_decode(xb, c.slot_ids if slots is None else slots, c.weights if weights is None else weights,
+                               *hw, intermediates=True)
+
+
+def check_against_oracle(dd: DevDecode, ref, im, host_weights=None):
+    c = dd.c
+    R = c.T * c.topk
+    got = u16(dd.out)
+    assert_bf16_close(got, ref, what="fused decode out")
+    c1 = dd.region("c1", torch.float32, (R, 2 * c.I)).cpu().numpy()
+    c2 = dd.region("c2", torch.float32, (R, c.H)).cpu().numpy()
+    aq = dd.region("aq", torch.uint8, (R, c.I)).cpu().numpy()
+    as_ = dd.region("as", torch.float32, (R, c.I // 128)).cpu().numpy()
+    inactive = c.slot_ids.reshape(-1) < 0
+    for name, arr in (("c1", c1), ("c2", c2), ("as", as_)):
+        assert np.all(arr[inactive].view(np.uint32) == 0), name + ": inactive rows must be +0.0"
+    assert np.all(aq[inactive] == 0)
+    if (~inactive).any():
+        hw = host_weights or [t.cpu().numpy() for t in (c.w13_q, c.w13_s)]
+        bound = gemm_abs_bound(im["xq"], im["xs"], hw[0], hw[1], c.slot_ids.reshape(-1), np.arange(R) // c.topk)
+        assert_within_bound(c1, im["c1"], bound, what="c1")
+        assert_close(c2[~inactive], im["c2"][~inactive], what="c2")
+
+
+@pytest.mark.parametrize("active", [1])
+def test_fused_decode_tiny(orc, active):
+    c = wl.decode_case(H=256, I=128, topk=2, n_slots=8, active=active, seed=0)
+    dd = DevDecode(c)
+    dd.poison()
+    dd.run()
+    torch.cuda.synchronize()
+    ref, im = oracle_decode(c)
+    check_against_oracle(dd, ref, im)
+
+
+@pytest.mark.parametrize("H,I", [(2048, 768), (4096, 1024)])
+@pytest.mark.parametrize("active", [8, 4, 2, 0])
+def test_fused_decode_full_configs(orc, H, I, active):
+    print("fused decode H=%d I=%d active=%d/8" % (H, I, active), flush=True)
+    c = wl.decode_case(H=H, I=I, topk=8, n_slots=64, active=active, seed=H + active, device="cuda")
+    host = [t.cpu().numpy() for t in (c.w13_q, c.w13_s, c.w2_q, c.w2_s)]
+    c.x = c.x.cpu()
+    dd = DevDecode(c)
+    dd.poison()
+    dd.run()
+    torch.cuda.synchronize()
+    ref, im = oracle_decode(c, host_weights=host)
+    check_against_oracle(dd, ref, im, host_weights=host)
+    if active == 0:
+        assert np.all(u16(dd.out) == 0)
+
+
+def test_fused_decode_batch_of_tokens(orc):
+    c = wl.decode_case(H=512, I=256, topk=4, n_slots=10, active=3, seed=11, T=5)
+    dd = DevDecode(c)
+    dd.poison()
+    dd.run()
+    torch.cuda.synchronize()
+    ref, im = oracle_decode(c)
+    check_against_oracle(dd, ref, im)
+
+
+def test_negative_slots_match_clamped_zero_weight_path_on_gpu(orc):
+    """The old path (inactive -> slot 0, weight 0) gives exactly the same output."""
+    c = wl.decode_case(H=2048, I=768, topk=8, n_slots=16, active=2, seed=21)
+    dd = DevDecode(c)
+    dd.run()
+    torch.cuda.synchronize()
+    new = u16(dd.out).copy()
+    dd.slots.copy_(to_dev(np.where(c.slot_ids < 0, 0, c.slot_ids).astype(np.int32)))
+    dd.w.copy_(to_dev(np.where(c.slot_ids < 0, 0.0, c.weights).astype(np.float32)))
+    dd.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(dd.out), new)
+
+
+def test_inactive_routing_weights_never_read(orc):
+    c = wl.decode_case(H=2048, I=768, topk=8, n_slots=16, active=3, seed=22)
+    dd = DevDecode(c)
+    dd.run()
+    torch.cuda.synchronize()
+    base = u16(dd.out).copy()
+    w = c.weights.copy()
+    w[c.slot_ids < 0] = np.nan
+    dd.w.copy_(to_dev(w))
+    dd.run()
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(dd.out), base)
+
+
+def test_graph_replay_with_changing_inputs_and_poison(orc):
+    """One captured graph serves all-active, mixed and all-inactive steps; inputs change in place,
+    workspaces are NaN-poisoned before each replay, and every replay equals the eager result."""
+    H, I, S, topk = 2048, 768, 32, 8
+    base = wl.decode_case(H=H, I=I, topk=topk, n_slots=S, active=8, seed=31)
+    dd = DevDecode(base)
+    host_w = [t.cpu().numpy() for t in (base.w13_q, base.w13_s, base.w2_q, base.w2_s)]
+    steps = []
+    for i, active in enumerate((8, 3, 0, 5, 8, 1)):
+        x = wl.bf16_normal((1, H), seed=100 + i)
+        slots, w = wl.decode_slots(1, topk, S, active, seed=200 + i, tail=(i == 3))
+        steps.append((x, slots, w))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    dd.run()                                   # warm-up outside capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        dd.run()
+    for i, (x, slots, w) in enumerate(steps):
+        dd.x.copy_(x.to(dev()))
+        dd.slots.copy_(to_dev(slots))
+        dd.w.copy_(to_dev(w))
+        dd.poison()
+        g.replay()
+        torch.cuda.synchronize()
+        replay_out = u16(dd.out).copy()
+        c = wl.DecodeCase(1, H, I, topk, S, x, slots, w, base.w13_q, base.w13_s, base.w2_q, base.w2_s)
+        dd.c = c
+        ref, im = oracle_decode(c, host_weights=host_w)
+        check_against_oracle(dd, ref, im, host_weights=host_w)
+        dd.poison()
+        dd.run()                               # eager, same inputs
+        torch.cuda.synchronize()
+        assert np.array_equal(u16(dd.out), replay_out), "replay %d differs from eager" % i
+        if (slots < 0).all():
+            assert np.all(replay_out == 0)

@@ -1,0 +1,159 @@
+"""GPU parity of the gather, the 1x128 quantizer and the top-k reduce against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import moe_routed_expert_amd as m
+import oracle
+import workloads as wl
+from gpu_util import assert_bf16_close, assert_close, dev, to_dev, u16
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ gather ---
+
+@pytest.mark.parametrize("k,tokens", [(7168, 1), (2048, 1), (7168, 8), (7168, 64), (7168, 1024),
+                                      (896, 16), (896, 1), (4096, 100), (100, 7), (16, 33)])
+def test_gather_bit_exact(orc, k, tokens):
+    print("gather k=%d tokens=%d" % (k, tokens), flush=True)
+    src_q, src_s, mp = wl.gather_case(k, tokens, 8, seed=1000 + k + tokens)
+    g = src_s.shape[1]
+    ref_q, ref_s = orc.gather_rows_scales(src_q, src_s.view(np.float32), mp)
+    dq = torch.full((len(mp), k), 0xAB, dtype=torch.uint8, device=dev())
+    ds = torch.full((len(mp), g), -1, dtype=torch.int32, device=dev())
+    m.gather_rows_scales(to_dev(src_q), to_dev(src_s).view(torch.float32), to_dev(mp), dq, ds.view(torch.float32))
+    torch.cuda.synchronize()
+    assert np.array_equal(dq.cpu().numpy(), ref_q)
+    assert np.array_equal(ds.cpu().numpy(), ref_s.view(np.int32))
+    assert np.array_equal(dq.cpu().numpy(), src_q[mp])     # the plain-indexing oracle too
+
+
+def test_gather_strided_negative_and_empty(orc):
+    k, tokens = 896, 5
+    src_q, src_s, _ = wl.gather_case(k, tokens, 8, seed=77)
+    mp = np.array([4, -1, 0, 0, 3, -7, 2, 1], np.int32)
+    # destination rows padded to 1024 bytes and 9 scale words
+    dq = torch.full((8, 1024), 0xCD, dtype=torch.uint8, device=dev())
+    ds = torch.full((8, 9), 12345, dtype=torch.int32, device=dev())
+    m.gather_rows_scales(to_dev(src_q), to_dev(src_s).view(torch.float32), to_dev(mp),
+                         dq, ds.view(torch.float32), k=k, g=7)
+    torch.cuda.synchronize()
+    ref_q, ref_s = orc.gather_rows_scales(src_q, src_s.view(np.float32), mp)
+    hq, hs = dq.cpu().numpy(), ds.cpu().numpy()
+    assert np.array_equal(hq[:, :k], ref_q) and np.all(hq[:, k:] == 0xCD)
+    assert np.array_equal(hs[:, :7], ref_s.view(np.int32)) and np.all(hs[:, 7:] == 12345)
+    # empty map: nothing written
+    e = torch.zeros(0, dtype=torch.int32, device=dev())
+    m.gather_rows_scales(to_dev(src_q), to_dev(src_s).view(torch.float32), e, dq, ds.view(torch.float32))
+    torch.cuda.synchronize()
+    assert np.array_equal(dq.cpu().numpy(), hq)
+
+
+def test_gather_unaligned_source_takes_byte_path(orc):
+    k, tokens = 256, 6
+    src_q, src_s, mp = wl.gather_case(k, tokens, 8, seed=78)
+    big = torch.zeros(tokens * k + 1, dtype=torch.uint8, device=dev())
+    big[1:] = to_dev(src_q).reshape(-1)
+    src_view = big[1:].view(tokens, k)                       # 1-byte misaligned base
+    dq = torch.empty((len(mp), k), dtype=torch.uint8, device=dev())
+    ds = torch.empty((len(mp), 2), dtype=torch.float32, device=dev())
+    m.gather_rows_scales(src_view, to_dev(src_s).view(torch.float32), to_dev(mp), dq, ds)
+    torch.cuda.synchronize()
+    assert np.array_equal(dq.cpu().numpy(), src_q[mp])
+
+
+# --------------------------------------------------------------- act quant ---
+
+def _ref_quant(orc, x_host):
+    return orc.quant_groups(x_host)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("rows,n", [(1, 2048), (1, 4096), (7, 768), (3, 896), (5, 200), (2, 7), (64, 1024)])
+def test_act_quant_identity_bit_exact(orc, dtype, rows, n):
+    print("act_quant identity %s %dx%d" % (dtype, rows, n), flush=True)
+    g = torch.Generator().manual_seed(rows * 10007 + n)
+    x = (torch.randn((rows, n), generator=g) * torch.exp2(torch.randint(-8, 8, (rows, 1), generator=g).float()))
+    x = x.to(dtype)
+    if rows > 2:
+        x[1] = 0
+    host = x.view(torch.int16).numpy().view(np.uint16) if dtype == torch.bfloat16 else x.numpy()
+    ref_q, ref_s = orc.quant_groups(host)
+    gq = (n + 127) // 128
+    q = torch.full((rows, n), 0x55, dtype=torch.uint8, device=dev())
+    s = torch.full((rows, gq), float("nan"), dtype=torch.float32, device=dev())
+    m.act_quant(x.to(dev()), q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), ref_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_act_quant_identity_rounding_edges(orc):
+    # rows whose values sit exactly on e4m3 rounding midpoints after scaling by s = 448/448 = 1
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    vals = orc.e4m3_decode(codes).astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    row = np.zeros(128 * 2, np.float32)
+    row[0] = 448.0
+    row[1:1 + len(mids)] = mids
+    row[128] = -448.0
+    row[129:129 + len(mids)] = -mids
+    x = np.stack([row, row * 0.75, row * 1e-3])
+    ref_q, ref_s = orc.quant_groups(x)
+    q = torch.empty((3, 256), dtype=torch.uint8, device=dev())
+    s = torch.empty((3, 2), dtype=torch.float32, device=dev())
+    m.act_quant(to_dev(x), q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), ref_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,n", [(8, 768), (8, 1024), (37, 1024), (4, 200)])
+def test_act_quant_silu_mul_within_one_step(orc, dtype, rows, n):
+    g = torch.Generator().manual_seed(rows + n)
+    c1 = (torch.randn((rows, 2 * n), generator=g) * 2).to(dtype)
+    c1[0] = 0                                                       # an inactive route's zero tile
+    host = c1.view(torch.int16).numpy().view(np.uint16) if dtype == torch.bfloat16 else c1.numpy()
+    ref_q, ref_s = orc.silu_mul_quant(host)
+    gq = (n + 127) // 128
+    q = torch.empty((rows, n), dtype=torch.uint8, device=dev())
+    s = torch.empty((rows, gq), dtype=torch.float32, device=dev())
+    m.act_quant(c1.to(dev()), q, s, act=m.MOE_ACT_SILU_MUL)
+    torch.cuda.synchronize()
+    hq, hs = q.cpu().numpy(), s.cpu().numpy()
+    assert np.all(hq[0] == 0) and np.all(hs[0].view(np.uint32) == 0)   # zero tile stays exactly zero
+    assert np.allclose(hs, ref_s, rtol=1e-6, atol=0)
+    # device expf may differ from libm by an ulp: codes differ by at most one step, rarely
+    dec = lambda c: orc.e4m3_decode(c).astype(np.float64)
+    diff = hq != ref_q
+    assert diff.mean() < 2e-3
+    d = np.abs(dec(hq) - dec(ref_q))[diff]
+    assert np.all(d <= np.abs(dec(ref_q))[diff] * 0.125 + 2.0 ** -9)
+
+
+# ------------------------------------------------------------------ reduce ---
+
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
+def test_topk_reduce(orc, ydt):
+    rng = np.random.default_rng(5)
+    T, topk, H = 6, 8, 2048
+    y = torch.from_numpy(rng.standard_normal((T * topk, H)).astype(np.float32)).to(ydt)
+    slots = rng.integers(0, 64, size=(T, topk)).astype(np.int32)
+    slots[1, [0, 3, 5]] = -1
+    slots[2, :] = -1
+    w = rng.random((T, topk)).astype(np.float32)
+    w[slots < 0] = np.nan                                     # never read
+    perm = rng.permutation(T * topk).astype(np.int32).reshape(T, topk)
+    host_y = y.view(torch.int16).numpy().view(np.uint16) if ydt == torch.bfloat16 else y.numpy()
+    for rr in (None, perm):
+        ref = orc.topk_reduce(host_y, slots, w, route_rows=rr)
+        out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev())
+        m.topk_reduce(y.to(dev()), to_dev(slots), to_dev(w), out, route_rows=None if rr is None else to_dev(rr))
+        torch.cuda.synchronize()
+        got = u16(out)
+        assert np.all(got[2] == 0)
+        assert_bf16_close(got, ref, what="topk_reduce")
+        # fp32 sums in the same order: at most one bf16 ulp apart
+        assert np.abs(got.astype(np.int64) - ref.astype(np.int64)).max() <= 1

@@ -1,0 +1,174 @@
+"""GPU parity of the block-FP8 GEMM (slot mode and grouped mode) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import moe_routed_expert_amd as m
+import oracle
+import workloads as wl
+from gpu_util import assert_bf16_close, assert_close, assert_within_bound, dev, gemm_abs_bound, to_dev, u16
+
+pytestmark = pytest.mark.gpu
+
+NP_OUT = {torch.float32: np.float32, torch.bfloat16: np.uint16, torch.float16: np.float16}
+
+
+def host_out(t):
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().astype(np.float64)
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def ref_as_f64(ref, dtype):
+    if dtype == torch.bfloat16:
+        return oracle.bf16_decode(ref).astype(np.float64)
+    return ref.astype(np.float64)
+
+
+# --------------------------------------------------------------- slot mode ---
+
+@pytest.mark.parametrize("N,K,rows,topk", [(256, 256, 2, 2), (1536, 2048, 8, 8), (2048, 768, 8, 1),
+                                           (2048, 4096, 16, 8), (64, 1024, 5, 1)])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16, torch.float16])
+def test_slot_gemm_vs_oracle(orc, N, K, rows, topk, odt):
+    print("slot gemm N=%d K=%d rows=%d %s" % (N, K, rows, odt), flush=True)
+    E = 6
+    w_q, w_s = wl.block_fp8_weights(E, N, K, seed=N + K)
+    T = max(1, rows // topk)
+    a_q, a_s = wl.fp8_rows(T, K, seed=K)
+    rng = np.random.default_rng(N)
+    slots = rng.integers(-1, E, size=rows).astype(np.int32)
+    slots[0] = 2
+    ref = orc.block_gemm(a_q.numpy(), a_s.numpy(), w_q.numpy(), w_s.numpy(), mode=orc.MODE_SLOT,
+                         slot_ids=slots, a_row_div=topk, out_dtype=NP_OUT[odt])
+    out = torch.full((rows, N), float("nan"), dtype=odt, device=dev())
+    m.bf8_grouped_gemm(a_q.to(dev()), a_s.to(dev()), w_q.to(dev()), w_s.to(dev()), out, mode=m.MOE_MODE_SLOT,
+                       slot_ids=to_dev(slots), a_row_div=topk)
+    torch.cuda.synchronize()
+    got = host_out(out)
+    inactive = slots < 0
+    assert np.all(got[inactive] == 0) and not np.any(np.signbit(got[inactive]))
+    if odt == torch.float32:
+        bound = gemm_abs_bound(a_q.numpy(), a_s.numpy(), w_q.numpy(), w_s.numpy(), slots, np.arange(rows) // topk)
+        assert_within_bound(got, ref, bound, what="slot gemm f32")
+    assert_close(got, ref_as_f64(ref, odt), what="slot gemm")
+
+
+def test_slot_gemm_integer_case_bit_exact(orc):
+    E, N, K, rows = 3, 512, 1024, 6
+    a_q, a_s, w_q, w_s = wl.powers_of_two_case(E, N, K, rows, seed=9)
+    slots = np.array([0, 2, -1, 1, 1, 0], np.int32)
+    ref = orc.block_gemm(a_q, a_s, w_q, w_s, mode=orc.MODE_SLOT, slot_ids=slots)
+    out = torch.empty((rows, N), dtype=torch.float32, device=dev())
+    m.bf8_grouped_gemm(to_dev(a_q), to_dev(a_s), to_dev(w_q), to_dev(w_s), out, mode=m.MOE_MODE_SLOT,
+                       slot_ids=to_dev(slots))
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_slot_gemm_empty_bank_all_inactive():
+    K, N = 256, 128
+    a_q = torch.zeros((1, K), dtype=torch.uint8, device=dev())
+    a_s = torch.zeros((1, 2), dtype=torch.float32, device=dev())
+    out = torch.full((4, N), float("nan"), dtype=torch.float32, device=dev())
+    slots = torch.full((4,), -1, dtype=torch.int32, device=dev())
+    st = m.lib().moe_bf8_grouped_gemm(a_q.data_ptr(), K, a_s.data_ptr(), 2, None, 0, K, None, 0, 2, 0, N, K,
+                                      m.MOE_MODE_SLOT, None, slots.data_ptr(), 4, 4, 0, out.data_ptr(), m.MOE_F32,
+                                      N, m._stream())
+    assert st == m.MOE_OK
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
+# ------------------------------------------------------------ grouped mode ---
+
+def grouped_case(E, N, K, counts, seed):
+    w_q, w_s = wl.block_fp8_weights(E, N, K, seed=seed)
+    R = int(sum(counts))
+    a_q, a_s = wl.fp8_rows(R, K, seed=seed + 1)
+    offs = np.zeros(E + 1, np.int32)
+    offs[1:] = np.cumsum(counts)
+    return w_q, w_s, a_q, a_s, offs
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("odt", [torch.bfloat16, torch.float32])
+def test_grouped_gemm_vs_oracle(orc, bm, odt):
+    E, N, K = 5, 256, 512
+    counts = [3, 0, 40, 129, 17]        # empty expert, ragged tails, several M tiles
+    print("grouped gemm BM=%d %s" % (bm, odt), flush=True)
+    w_q, w_s, a_q, a_s, offs = grouped_case(E, N, K, counts, seed=bm)
+    ref = orc.block_gemm(a_q.numpy(), a_s.numpy(), w_q.numpy(), w_s.numpy(), mode=orc.MODE_GROUPED,
+                         expert_offsets=offs, out_dtype=NP_OUT[odt])
+    R = offs[-1]
+    out = torch.full((R + 3, N), float("nan"), dtype=odt, device=dev())   # 3 spare rows stay untouched
+    m.bf8_grouped_gemm(a_q.to(dev()), a_s.to(dev()), w_q.to(dev()), w_s.to(dev()), out, mode=m.MOE_MODE_GROUPED,
+                       expert_offsets=to_dev(offs), m_rows=R + 3, block_m=bm)
+    torch.cuda.synchronize()
+    got = host_out(out)
+    assert np.all(np.isnan(got[R:]))
+    if odt == torch.float32:
+        experts = np.repeat(np.arange(E), np.diff(offs))
+        bound = gemm_abs_bound(a_q.numpy(), a_s.numpy(), w_q.numpy(), w_s.numpy(), experts, np.arange(R))
+        assert_within_bound(got[:R], ref, bound, what="grouped gemm f32")
+    assert_close(got[:R], ref_as_f64(ref, odt), what="grouped gemm")
+
+
+def test_grouped_gemm_integer_case_bit_exact(orc):
+    E, N, K = 4, 384, 640
+    counts = [20, 1, 0, 33]
+    a_q, a_s, w_q, w_s = wl.powers_of_two_case(E, N, K, sum(counts), seed=10)
+    offs = np.zeros(E + 1, np.int32)
+    offs[1:] = np.cumsum(counts)
+    ref = orc.block_gemm(a_q, a_s, w_q, w_s, mode=orc.MODE_GROUPED, expert_offsets=offs)
+    for bm in (16, 32, 64, 128):
+        out = torch.empty((offs[-1], N), dtype=torch.float32, device=dev())
+        m.bf8_grouped_gemm(to_dev(a_q), to_dev(a_s), to_dev(w_q), to_dev(w_s), out, mode=m.MOE_MODE_GROUPED,
+                           expert_offsets=to_dev(offs), block_m=bm)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32)), bm
+
+
+def test_grouped_prefill_routes_chain(orc):
+    """gather -> grouped gate/up (bf16) -> SiLU-mul requant -> grouped down (bf16) -> reduce, small shape."""
+    T, E, topk, H, I = 64, 16, 4, 512, 256
+    rt = wl.prefill_routes(T, E, topk, seed=3)
+    x = wl.bf16_normal((T, H), seed=4)
+    w13_q, w13_s = wl.block_fp8_weights(E, 2 * I, H, seed=5)
+    w2_q, w2_s = wl.block_fp8_weights(E, H, I, seed=6)
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    # oracle chain
+    xq, xs = orc.quant_groups(xb)
+    gq, gs = orc.gather_rows_scales(xq, xs, rt.dst2src)
+    c1 = orc.block_gemm(gq, gs, w13_q.numpy(), w13_s.numpy(), mode=orc.MODE_GROUPED,
+                        expert_offsets=rt.expert_offsets, out_dtype=np.uint16)
+    aq, as_ = orc.silu_mul_quant(c1)
+    c2 = orc.block_gemm(aq, as_, w2_q.numpy(), w2_s.numpy(), mode=orc.MODE_GROUPED,
+                        expert_offsets=rt.expert_offsets, out_dtype=np.uint16)
+    ref = orc.topk_reduce(c2, rt.expert_ids, rt.weights, route_rows=rt.route_rows)
+    # device chain
+    R = T * topk
+    d = dev()
+    xq_d = torch.empty((T, H), dtype=torch.uint8, device=d)
+    xs_d = torch.empty((T, H // 128), dtype=torch.float32, device=d)
+    m.act_quant(x.to(d), xq_d, xs_d)
+    gq_d = torch.empty((R, H), dtype=torch.uint8, device=d)
+    gs_d = torch.empty((R, H // 128), dtype=torch.float32, device=d)
+    m.gather_rows_scales(xq_d, xs_d, to_dev(rt.dst2src), gq_d, gs_d)
+    c1_d = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=d)
+    offs = to_dev(rt.expert_offsets)
+    m.bf8_grouped_gemm(gq_d, gs_d, w13_q.to(d), w13_s.to(d), c1_d, mode=m.MOE_MODE_GROUPED, expert_offsets=offs)
+    aq_d = torch.empty((R, I), dtype=torch.uint8, device=d)
+    as_d = torch.empty((R, I // 128), dtype=torch.float32, device=d)
+    m.act_quant(c1_d, aq_d, as_d, act=m.MOE_ACT_SILU_MUL)
+    c2_d = torch.empty((R, H), dtype=torch.bfloat16, device=d)
+    m.bf8_grouped_gemm(aq_d, as_d, w2_q.to(d), w2_s.to(d), c2_d, mode=m.MOE_MODE_GROUPED, expert_offsets=offs)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+    m.topk_reduce(c2_d, to_dev(rt.expert_ids), to_dev(rt.weights), out, route_rows=to_dev(rt.route_rows))
+    torch.cuda.synchronize()
+    assert np.array_equal(xq_d.cpu().numpy(), xq)
+    assert np.array_equal(gq_d.cpu().numpy(), gq)
+    assert_bf16_close(u16(c1_d), c1, what="prefill c1")
+    assert_bf16_close(u16(out), ref, what="prefill out")
