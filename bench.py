@@ -1,19 +1,21 @@
 """Benchmark of the MI355X routed-expert hot path; prints ONE JSON line.
 
-Headline (value): batch-1 decode step, H=2048, I=768, a 64-slot expert pool,
-top-k 8 with 8/8 routes active: x quant -> gate/up -> SiLU*up requant -> down
--> top-k reduce, replayed from captured hipGraphs with a fresh input set each
-step (a ring of 16 graphs over 16 input sets already resident in HBM).  The
-Infinity Cache is flushed before every step (outside the timed events), so
-the expert weights come from HBM, and each step is bracketed by HIP events on
-the stream the kernels run on.
+Headline (value): one batch-1 decode step of the routed experts, H=2048,
+I=768, a 64-slot expert pool, top-k 8 with 8/8 routes active: x quant ->
+gate/up -> SiLU*up requant -> down -> top-k reduce.  Steps are timed the way
+they run inside a model: a captured hipGraph of L=16 chained decode layers
+(layer l+1 takes layer l's output as its token row), each layer with its own
+64-slot expert pool, so the 16 pools (4.8 GB) cannot sit in the 256 MB
+Infinity Cache and every step streams its experts from HBM.  HIP events on
+the stream bracket each graph replay; a step is replay time / 16.  Inputs
+are resident in HBM before the timed region.
 
-Also reported: the same at 4/2/0 active routes and for H=4096, I=1024 (time
-vs active routes), warm-cache times, the fused gather (k=7168, 8192 rows),
-the grouped prefill GEMMs at 24576 routes (E=256, top-6, H=4096, I=1024) in
+Also reported: 4/2/0 active routes and H=4096, I=1024 (time vs active
+routes), the fused gather (k=7168; 8, 512, 8192 rows) timed the same way, the
+grouped prefill GEMMs at 24576 routes (E=256, top-6, H=4096, I=1024) in
 TFLOP/s against the fp8 dense peak and against the HBM roofline, the
-roofline of the dominant decode kernel, and the CPU oracle timed on a bounded
-sample of the headline workload.
+roofline of the dominant kernel (the single fused decode kernel), and the
+CPU oracle timed on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-prefill]
 """
@@ -32,7 +34,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, TFLOP/s
-FLUSH_BYTES = 1 << 30          # > 256 MB Infinity Cache + 8 x 4 MB L2
 
 
 def log(*a):
@@ -61,125 +62,101 @@ class Timer:
         return [a.elapsed_time(b) * 1000.0 for a, b in self.pairs]
 
 
-def make_flush(torch):
-    buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-    buf.zero_()
-
-    def flush():
-        buf.add_(1.0)
-    return flush
+LAYERS = 16
 
 
-def decode_bench(torch, m, wl, H, I, S, topk, active, steps, warmup, flush, ring=16, seed=1):
-    """Returns dict with cold/warm us per step for one (H, I, active)."""
+def decode_pools(torch, wl, H, I, S, seed):
     dev = torch.device("cuda")
-    w13_q, w13_s = wl.block_fp8_weights(S, 2 * I, H, seed * 7 + 11, device=dev)
-    w2_q, w2_s = wl.block_fp8_weights(S, H, I, seed * 7 + 13, device=dev)
-    sets = []
-    for i in range(ring):
-        x = wl.bf16_normal((1, H), seed=1000 + i, device=dev)
-        slots, w = wl.decode_slots(1, topk, S, active, seed=2000 + i)
-        sets.append((x, torch.from_numpy(slots).to(dev), torch.from_numpy(w).to(dev),
-                     torch.empty((1, H), dtype=torch.bfloat16, device=dev)))
+    pools = []
+    for l in range(LAYERS):
+        w13_q, w13_s = wl.block_fp8_weights(S, 2 * I, H, seed * 1000 + 2 * l, device=dev, chunk_experts=16)
+        w2_q, w2_s = wl.block_fp8_weights(S, H, I, seed * 1000 + 2 * l + 1, device=dev, chunk_experts=16)
+        pools.append((w13_q, w13_s, w2_q, w2_s))
+    return pools
+
+
+def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup):
+    """A graph of LAYERS chained decode steps; returns per-step times from HIP events."""
+    dev = torch.device("cuda")
+    x0 = wl.bf16_normal((1, H), seed=7, device=dev)
+    outs = [torch.empty((1, H), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
+    routes = []
+    for l in range(LAYERS):
+        sl, w = wl.decode_slots(1, topk, S, active, seed=5000 + 97 * l + active)
+        routes.append((torch.from_numpy(sl).to(dev), torch.from_numpy(w).to(dev)))
     ws = m.fused_decode_workspace(1, H, I, topk, device=dev)
+
+    def step_all():
+        x = x0
+        for l in range(LAYERS):
+            m.fused_decode(x, routes[l][0], routes[l][1], *pools[l], ws, outs[l])
+            x = outs[l]
+
+    step_all()
     torch.cuda.synchronize()
-    graphs = []
-    cap = torch.cuda.Stream()
-    for x, sl, w, out in sets:
-        m.fused_decode(x, sl, w, w13_q, w13_s, w2_q, w2_s, ws, out)      # eager warm-up
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            m.fused_decode(x, sl, w, w13_q, w13_s, w2_q, w2_s, ws, out)
-        graphs.append(g)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        step_all()
+    for _ in range(warmup):
+        g.replay()
     torch.cuda.synchronize()
-    for i in range(warmup):
-        graphs[i % ring].replay()
-    torch.cuda.synchronize()
-    # cold: flush before each step, events around the step only
     t = Timer(torch)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    for i in range(steps):
-        flush()
+    for _ in range(reps):
         t.start()
-        graphs[i % ring].replay()
+        g.replay()
         t.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    cold = t.us()
-    # warm: back-to-back replays, no flush
-    t2 = Timer(torch)
-    for i in range(steps):
-        t2.start()
-        graphs[i % ring].replay()
-        t2.stop()
-    warm = t2.us()
-    per_route = wl.nbytes_expert(H, I)
-    nbytes = active * per_route
-    res = dict(H=H, I=I, slots=S, topk=topk, active=active,
-               us_cold_mean=statistics.fmean(cold), us_cold_median=statistics.median(cold),
-               us_warm_median=statistics.median(warm), bytes_streamed=nbytes,
-               wall_ms_per_iter_incl_flush=wall * 1000.0 / steps)
-    res["hbm_gbs_cold"] = nbytes / (res["us_cold_mean"] * 1e-6) / 1e9 if nbytes else 0.0
-    res["hbm_frac_cold"] = res["hbm_gbs_cold"] / HBM_PEAK_GBS
-    del graphs, w13_q, w2_q
+    per_step = [u / LAYERS for u in t.us()]
+    nbytes = active * wl.nbytes_expert(H, I)
+    mean = statistics.fmean(per_step)
+    res = dict(H=H, I=I, slots=S, topk=topk, active=active, layers_per_graph=LAYERS, replays=reps,
+               us_per_step_mean=mean, us_per_step_median=statistics.median(per_step),
+               us_per_step_min=min(per_step), bytes_streamed=nbytes,
+               hbm_gbs=nbytes / (mean * 1e-6) / 1e9 if nbytes else 0.0,
+               wall_us_per_step=wall * 1e6 / (reps * LAYERS))
+    res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
+    del g
     return res
 
 
-def gateup_kernel_roofline(torch, m, wl, H, I, S, topk, steps, flush):
-    """Dominant decode kernel: the slot-mode block-FP8 gate/up GEMM over 8 active routes,
-    one launch per event pair, cold cache."""
+def gather_bench(torch, m, wl, k, tokens, topk, reps):
+    """16 gathers over 16 disjoint source/destination sets in one graph (cold by construction)."""
     dev = torch.device("cuda")
-    w13_q, w13_s = wl.block_fp8_weights(S, 2 * I, H, 77, device=dev)
-    a_q, a_s = wl.fp8_rows(1, H, seed=78, device=dev)
-    slot_sets = [torch.from_numpy(wl.decode_slots(1, topk, S, topk, seed=3000 + i)[0].reshape(-1)).to(dev)
-                 for i in range(16)]
-    out = torch.empty((topk, 2 * I), dtype=torch.float32, device=dev)
-    for i in range(5):
-        m.bf8_grouped_gemm(a_q, a_s, w13_q, w13_s, out, mode=m.MOE_MODE_SLOT, slot_ids=slot_sets[i % 16],
-                           a_row_div=topk)
-    t = Timer(torch)
-    for i in range(steps):
-        flush()
-        t.start()
-        m.bf8_grouped_gemm(a_q, a_s, w13_q, w13_s, out, mode=m.MOE_MODE_SLOT, slot_ids=slot_sets[i % 16],
-                           a_row_div=topk)
-        t.stop()
-    us = statistics.fmean(t.us())
-    per_route = 2 * I * H + 4 * math.ceil(2 * I / 128) * math.ceil(H / 128)
-    nbytes = topk * per_route
-    achieved = nbytes / (us * 1e-6) / 1e9
-    return dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s", frac=achieved / HBM_PEAK_GBS,
-                traffic=None, kernel="slot_gemv_kernel<f32, fp8 A> (gate/up, 8 routes, H=%d, 2I=%d)" % (H, 2 * I),
-                bytes_per_launch=nbytes, us_per_launch=us)
+    sets = []
+    for i in range(LAYERS):
+        src_q, src_s, mp = wl.gather_case(k, tokens, topk, seed=50 + i)
+        g = src_s.shape[1]
+        sets.append((torch.from_numpy(src_q).to(dev), torch.from_numpy(src_s).to(dev).view(torch.float32),
+                     torch.from_numpy(mp).to(dev), torch.empty((len(mp), k), dtype=torch.uint8, device=dev),
+                     torch.empty((len(mp), g), dtype=torch.float32, device=dev), mp))
 
+    def run_all():
+        for sq, ss, mp_d, dq, ds, _ in sets:
+            m.gather_rows_scales(sq, ss, mp_d, dq, ds)
 
-def gather_bench(torch, m, wl, k, tokens, topk, steps, flush):
-    dev = torch.device("cuda")
-    src_q, src_s, mp = wl.gather_case(k, tokens, topk, seed=5)
-    src_q = torch.from_numpy(src_q).to(dev)
-    src_s = torch.from_numpy(src_s).to(dev).view(torch.float32)
-    mp_d = torch.from_numpy(mp).to(dev)
-    g = src_s.shape[1]
-    dq = torch.empty((len(mp), k), dtype=torch.uint8, device=dev)
-    ds = torch.empty((len(mp), g), dtype=torch.float32, device=dev)
-    for _ in range(5):
-        m.gather_rows_scales(src_q, src_s, mp_d, dq, ds)
+    run_all()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=torch.cuda.Stream()):
+        run_all()
+    for _ in range(3):
+        gr.replay()
     t = Timer(torch)
-    for _ in range(steps):
-        flush()
+    for _ in range(reps):
         t.start()
-        m.gather_rows_scales(src_q, src_s, mp_d, dq, ds)
+        gr.replay()
         t.stop()
-    us = statistics.median(t.us())
-    row = k + 4 * g
+    us = statistics.median(t.us()) / LAYERS
+    row = k + 4 * sets[0][1].shape[1]
+    mp = sets[0][5]
     nbytes = len(mp) * row + len(set(mp.tolist())) * row
-    return dict(k=k, tokens=tokens, rows=len(mp), us_median=us, bytes=nbytes,
+    return dict(k=k, tokens=tokens, rows=len(mp), us_per_call=us, bytes=nbytes,
                 gbs=nbytes / (us * 1e-6) / 1e9, hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
 
-def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, flush):
+def prefill_bench(torch, m, wl, T, E, topk, H, I, steps):
     dev = torch.device("cuda")
     rt = wl.prefill_routes(T, E, topk, seed=9)
     R = T * topk
@@ -199,8 +176,7 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, flush):
         for _ in range(3):
             m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c, mode=m.MOE_MODE_GROUPED, expert_offsets=offs)
         t = Timer(torch)
-        for _ in range(steps):
-            flush()
+        for _ in range(steps):          # 2-3 GB of weights per call: cold by construction
             t.start()
             m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c, mode=m.MOE_MODE_GROUPED, expert_offsets=offs)
             t.stop()
@@ -238,8 +214,8 @@ def cpu_baseline(wl, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=320, help="decode steps timed (multiple of 16)")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed graph replays")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
@@ -252,44 +228,55 @@ def main():
     import workloads as wl
     m.lib()
     torch.cuda.init()
-    flush = make_flush(torch)
+    reps = max(1, args.steps // LAYERS)
+    steps = reps * LAYERS
 
+    log("decode H=2048 I=768: building %d layer pools" % LAYERS)
+    pools = decode_pools(torch, wl, 2048, 768, 64, seed=1)
     log("decode H=2048 I=768 8/8 (headline)")
-    head = decode_bench(torch, m, wl, 2048, 768, 64, 8, 8, args.steps, args.warmup, flush)
+    head = decode_bench(torch, m, wl, pools, 2048, 768, 64, 8, 8, reps, args.warmup)
     extra = {"decode": [head]}
-    roof = None
     if not args.only_headline:
-        for (H, I) in ((2048, 768), (4096, 1024)):
-            for active in ((4, 2, 0) if H == 2048 else (8, 4, 2, 0)):
-                log("decode H=%d I=%d %d/8" % (H, I, active))
-                extra["decode"].append(decode_bench(torch, m, wl, H, I, 64, 8, active, max(50, args.steps // 2),
-                                                    10, flush))
-        log("gate/up kernel roofline")
-        roof = gateup_kernel_roofline(torch, m, wl, 2048, 768, 64, 8, args.steps, flush)
+        for active in (4, 2, 0):
+            log("decode H=2048 I=768 %d/8" % active)
+            extra["decode"].append(decode_bench(torch, m, wl, pools, 2048, 768, 64, 8, active, reps, args.warmup))
+        del pools
+        torch.cuda.empty_cache()
+        log("decode H=4096 I=1024: building %d layer pools" % LAYERS)
+        pools = decode_pools(torch, wl, 4096, 1024, 64, seed=2)
+        for active in (8, 4, 2, 0):
+            log("decode H=4096 I=1024 %d/8" % active)
+            extra["decode"].append(decode_bench(torch, m, wl, pools, 4096, 1024, 64, 8, active, reps, args.warmup))
+        del pools
+        torch.cuda.empty_cache()
         log("gather")
-        extra["gather"] = [gather_bench(torch, m, wl, 7168, t, 8, 100, flush) for t in (1, 64, 1024)]
+        extra["gather"] = [gather_bench(torch, m, wl, 7168, t, 8, 20) for t in (1, 64, 1024)]
         if not args.skip_prefill:
             log("prefill 24576 routes")
-            extra["prefill"] = prefill_bench(torch, m, wl, 4096, 256, 6, 4096, 1024, 20, flush)
+            extra["prefill"] = prefill_bench(torch, m, wl, 4096, 256, 6, 4096, 1024, 10)
+    roof = dict(bound="hbm", kernel="fused_decode_kernel (one launch per decode step, H=2048, I=768, 8/8 active)",
+                bytes_per_launch=head["bytes_streamed"], us_per_launch=head["us_per_step_mean"],
+                achieved=head["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s", frac=head["hbm_frac"], traffic=None)
     cpu = None
     if not args.skip_cpu:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(wl)
     line = {
         "metric": "bs1 decode us/step & HBM GB/s (top-k 8); prefill fp8 TFLOP/s vs peak",
-        "value": round(head["us_cold_mean"], 3),
+        "value": round(head["us_per_step_mean"], 3),
         "unit": "us/step",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": head["us_cold_mean"] / 1000.0,
+        "ms_per_step": head["us_per_step_mean"] / 1000.0,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3",
         "data": "synthetic (seeded N(0,0.02) block-FP8 expert banks, N(0,1) bf16 activations)",
-        "config": {"workload": "decode bs=1, H=2048, I=768, 64-slot pool, top-k 8, 8/8 active, cold cache",
-                   "hbm_gbs": round(head["hbm_gbs_cold"], 1), "hbm_frac": round(head["hbm_frac_cold"], 4)},
+        "config": {"workload": "decode bs=1, H=2048, I=768, 64-slot pool per layer, top-k 8, 8/8 active; "
+                               "16 chained layers per graph, weights from HBM",
+                   "hbm_gbs": round(head["hbm_gbs"], 1), "hbm_frac": round(head["hbm_frac"], 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -22,6 +22,27 @@ int topk_reduce_launch(hipStream_t st, const void* y, int y_dt, int64_t y_stride
                        const int32_t* route_rows, const float* weights, int64_t T, int64_t topk, int64_t H,
                        uint16_t* out, int64_t out_stride);
 
+struct FusedDecodeArgs {
+    const uint16_t* x;
+    const int32_t* slots;
+    const float* weights;
+    const uint8_t* w13;
+    const float* w13s;
+    const uint8_t* w2;
+    const float* w2s;
+    float* c1;
+    uint8_t* aq;
+    float* as;
+    float* c2;
+    uint32_t* ctl;
+    uint16_t* out;
+    int T, H, I, topk;
+    int tiles_a;
+    int tiles_c;
+    int n_a;
+};
+int fused_decode_two_launch(hipStream_t st, const FusedDecodeArgs& a, int nt);
+
 static char g_last_hip_error[256] = "no HIP error recorded";
 
 void note_hip_error(hipError_t e) {
@@ -51,7 +72,7 @@ DecodeLayout decode_layout(int64_t T, int64_t H, int64_t I, int64_t topk) {
     L.off[1] = o; o = align256(o + R * I);                    // aq fp8
     L.off[2] = o; o = align256(o + R * ceil_div(I, 128) * 4); // as f32
     L.off[3] = o; o = align256(o + R * H * 4);                // c2 f32
-    L.off[4] = o; o = align256(o + 256);                      // ctl
+    L.off[4] = o; o = align256(o + 4 * (2 * R + T + 1));      // ctl: reserved control words
     L.off[5] = o;
     return L;
 }
@@ -180,6 +201,17 @@ extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, in
     float* c2 = (float*)(ws + L.off[3]);
     const int64_t gH = H / 128, gI = I / 128, g2I = 2 * I / 128;
     auto st = as_stream(stream);
+    if (gI <= 8) {
+        // gate/up launch + down/reduce launch
+        FusedDecodeArgs a;
+        a.x = x_bf16; a.slots = slot_ids; a.weights = weights;
+        a.w13 = w13_q; a.w13s = w13_s; a.w2 = w2_q; a.w2s = w2_s;
+        a.c1 = c1; a.aq = aq; a.as = as; a.c2 = c2; a.ctl = (uint32_t*)(ws + L.off[4]); a.out = out_bf16;
+        a.T = (int)T; a.H = (int)H; a.I = (int)I; a.topk = (int)topk;
+        a.tiles_a = (int)(2 * I / 16); a.tiles_c = (int)(H / 16); a.n_a = (int)(R * a.tiles_a);
+        return fused_decode_two_launch(st, a, 1);
+    }
+    // wider intermediate sizes: four launches
     // 1) gate/up per route, quantizing the bf16 token row on the fly
     int rc = slot_gemm_launch(st, true, x_bf16, H, nullptr, 0, w13_q, 2 * I * H, H, w13_s, g2I * gH, gH, 2 * I, H,
                               slot_ids, R, topk, c1, MOE_F32, 2 * I);

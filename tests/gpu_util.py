@@ -52,9 +52,11 @@ def _t_dec(codes: np.ndarray) -> torch.Tensor:
 def gemm_abs_bound(a_q, a_s, w_q, w_s, experts_of_rows, a_rows):
     """Per-element bound on |device - oracle| for an fp32 block-FP8 GEMM output.
 
-    Each side is within (K/128 + 130) * 2^-24 * sum_k |a_k w_k s| of the exact result (one rounding per
-    fp32 add inside a 128-block, one per block scale, one per block accumulate), so the two sides are
-    within twice that of each other."""
+    Recursive summation of n terms in any order, each addition rounded or truncated to fp32
+    (unit 2^-23), is within n * 2^-23 * sum|terms| of the exact sum.  Each output sums K exact
+    products plus two scale multiplies and one accumulate per 128-wide block, so each side is within
+    (K + 4K/128 + 4) * 2^-23 * sum_k |a_k w_k s| of the exact result; the MFMA's internal K reduction
+    is covered whatever its order or rounding.  The two sides are within twice that of each other."""
     E, N, K = w_q.shape
     A = _t_dec(a_q).abs() * torch.from_numpy(np.repeat(a_s, 128, axis=1)[:, :K]).double()
     out = np.zeros((len(experts_of_rows), N))
@@ -64,7 +66,7 @@ def gemm_abs_bound(a_q, a_s, w_q, w_s, experts_of_rows, a_rows):
         W = _t_dec(w_q[e]).abs() * torch.from_numpy(
             np.repeat(np.repeat(w_s[e], 128, axis=0), 128, axis=1)[:N, :K]).double()
         out[r] = (W @ A[a_rows[r]]).numpy()
-    return 2.0 * out * (K / 128 + 130) * 2.0 ** -24
+    return 2.0 * out * (K + 4 * K / 128 + 4) * 2.0 ** -23
 
 
 def assert_within_bound(got, ref, bound, what=""):

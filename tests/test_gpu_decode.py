@@ -60,6 +60,8 @@ def check_against_oracle(dd: DevDecode, ref, im, host_weights=None):
     for name, arr in (("c1", c1), ("c2", c2), ("as", as_)):
         assert np.all(arr[inactive].view(np.uint32) == 0), name + ": inactive rows must be +0.0"
     assert np.all(aq[inactive] == 0)
+    ctl = dd.ws[dd.lay["ctl"]:dd.lay["total"]].cpu().numpy()
+    assert np.all(ctl == 0), "control words must be clear after a call (and no wait timed out)"
     if (~inactive).any():
         hw = host_weights or [t.cpu().numpy() for t in (c.w13_q, c.w13_s)]
         bound = gemm_abs_bound(im["xq"], im["xs"], hw[0], hw[1], c.slot_ids.reshape(-1), np.arange(R) // c.topk)
@@ -170,3 +172,43 @@ def test_graph_replay_with_changing_inputs_and_poison(orc):
         assert np.array_equal(u16(dd.out), replay_out), "replay %d differs from eager" % i
         if (slots < 0).all():
             assert np.all(replay_out == 0)
+
+
+def test_chained_layers_in_one_graph_like_the_benchmark(orc):
+    """The benchmark's launch configuration: chained decode layers (each with its own 64-slot pool,
+    layer l+1 reading layer l's output) captured in one graph; every layer checked against the oracle
+    on the token row the device actually fed it."""
+    H, I, S, topk, L = 2048, 768, 64, 8, 4
+    d = dev()
+    pools = [wl.block_fp8_weights(S, 2 * I, H, 900 + 2 * l, device="cuda") +
+             wl.block_fp8_weights(S, H, I, 901 + 2 * l, device="cuda") for l in range(L)]
+    x0 = wl.bf16_normal((1, H), seed=5, device="cuda")
+    outs = [torch.empty((1, H), dtype=torch.bfloat16, device=d) for _ in range(L)]
+    routes = [wl.decode_slots(1, topk, S, (8, 3, 8, 0)[l], seed=40 + l) for l in range(L)]
+    routes_d = [(to_dev(sl), to_dev(w)) for sl, w in routes]
+    ws = m.fused_decode_workspace(1, H, I, topk, device=d)
+
+    def step_all():
+        x = x0
+        for l in range(L):
+            m.fused_decode(x, routes_d[l][0], routes_d[l][1], *pools[l], ws, outs[l])
+            x = outs[l]
+
+    step_all()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.Stream()):
+        step_all()
+    for o in outs:
+        o.fill_(float("nan"))
+    g.replay()
+    g.replay()
+    torch.cuda.synchronize()
+    x_in = u16(x0)
+    for l in range(L):
+        host = [t.cpu().numpy() for t in pools[l]]
+        ref = oracle.fused_decode(x_in, routes[l][0], routes[l][1], *host)
+        got = u16(outs[l])
+        assert_bf16_close(got, ref, what="layer %d" % l)
+        x_in = got
+    assert np.all(u16(outs[3]) == 0)                 # layer 3 has no active route
