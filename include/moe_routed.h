@@ -172,21 +172,23 @@ int moe_topk_reduce(const void* y, int y_dt, int64_t y_stride,
                     void* stream);
 
 /*
- * Fused decode workspace.  Layout (byte offsets written to offsets[0..5]):
+ * Fused decode workspace.  Layout (byte offsets written to offsets[0..6]):
  *   [0] c1   R x 2I           fp32 gate/up output (R = T*topk routes)
- *   [1] aq   R x I            fp8 activation
- *   [2] as   R x ceil(I/128)  fp32 activation scales
- *   [3] c2   R x H            fp32 down output
- *   [4] ctl  control words
- *   [5] total size in bytes
- * Regions [0]..[3] may hold anything between calls: every call rewrites them
- * completely, and an inactive route's c1/aq/as/c2 rows become exact zeros.
- * The control region must be cleared once with moe_fused_decode_workspace_init
- * before the first call; calls leave it cleared.  Size 0 / MOE_ERR_SHAPE for
- * shapes moe_fused_decode rejects.
+ *   [1] h    R x I            fp32 SiLU(gate)*up
+ *   [2] aq   R x I            fp8 activation (1x128 requant of h)
+ *   [3] as   R x ceil(I/128)  fp32 activation scales
+ *   [4] c2   R x H            fp32 down output
+ *   [5] ctl  reserved control words
+ *   [6] total size in bytes
+ * Regions [0]..[4] may hold anything between calls: every call rewrites them
+ * completely, and an inactive route's c1/h/aq/as/c2 rows become exact zeros
+ * (h is only written when I <= 1024; wider I runs the step as four launches
+ * that do not store h).  The control region must be cleared once with
+ * moe_fused_decode_workspace_init before the first call.  Size 0 /
+ * MOE_ERR_SHAPE for shapes moe_fused_decode rejects.
  */
 size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk);
-int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[6]);
+int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[7]);
 int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes, int64_t T, int64_t H, int64_t I,
                                     int64_t topk, void* stream);
 

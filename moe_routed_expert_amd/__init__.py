@@ -158,9 +158,9 @@ def fused_decode_workspace_size(T, H, I, topk) -> int:
 
 
 def fused_decode_workspace_layout(T, H, I, topk):
-    offs = (ctypes.c_int64 * 6)()
+    offs = (ctypes.c_int64 * 7)()
     _check("moe_fused_decode_workspace_layout", lib().moe_fused_decode_workspace_layout(T, H, I, topk, offs))
-    return dict(zip(("c1", "aq", "as", "c2", "ctl", "total"), list(offs)))
+    return dict(zip(("c1", "h", "aq", "as", "c2", "ctl", "total"), list(offs)))
 
 
 def fused_decode_workspace(T, H, I, topk, device="cuda", stream=None) -> torch.Tensor:

@@ -5,6 +5,7 @@
 
 #include "device.h"
 #include "host.h"
+#include "decode_args.h"
 
 namespace moe {
 
@@ -22,26 +23,7 @@ int topk_reduce_launch(hipStream_t st, const void* y, int y_dt, int64_t y_stride
                        const int32_t* route_rows, const float* weights, int64_t T, int64_t topk, int64_t H,
                        uint16_t* out, int64_t out_stride);
 
-struct FusedDecodeArgs {
-    const uint16_t* x;
-    const int32_t* slots;
-    const float* weights;
-    const uint8_t* w13;
-    const float* w13s;
-    const uint8_t* w2;
-    const float* w2s;
-    float* c1;
-    uint8_t* aq;
-    float* as;
-    float* c2;
-    uint32_t* ctl;
-    uint16_t* out;
-    int T, H, I, topk;
-    int tiles_a;
-    int tiles_c;
-    int n_a;
-};
-int fused_decode_two_launch(hipStream_t st, const FusedDecodeArgs& a, int nt);
+
 
 static char g_last_hip_error[256] = "no HIP error recorded";
 
@@ -59,7 +41,7 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
 }
 
 struct DecodeLayout {
-    int64_t off[6];   // c1, aq, as, c2, ctl, total
+    int64_t off[7];   // c1, h, aq, as, c2, ctl, total
 };
 
 int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -69,11 +51,12 @@ DecodeLayout decode_layout(int64_t T, int64_t H, int64_t I, int64_t topk) {
     DecodeLayout L;
     int64_t o = 0;
     L.off[0] = o; o = align256(o + R * 2 * I * 4);            // c1 f32
-    L.off[1] = o; o = align256(o + R * I);                    // aq fp8
-    L.off[2] = o; o = align256(o + R * ceil_div(I, 128) * 4); // as f32
-    L.off[3] = o; o = align256(o + R * H * 4);                // c2 f32
-    L.off[4] = o; o = align256(o + 4 * (2 * R + T + 1));      // ctl: reserved control words
-    L.off[5] = o;
+    L.off[1] = o; o = align256(o + R * I * 4);                // h f32
+    L.off[2] = o; o = align256(o + R * I);                    // aq fp8
+    L.off[3] = o; o = align256(o + R * ceil_div(I, 128) * 4); // as f32
+    L.off[4] = o; o = align256(o + R * H * 4);                // c2 f32
+    L.off[5] = o; o = align256(o + 256);                      // ctl: reserved control words
+    L.off[6] = o;
     return L;
 }
 
@@ -155,14 +138,14 @@ extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const 
 
 extern "C" size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk) {
     if (!decode_shape_ok(T, H, I, topk)) return 0;
-    return (size_t)decode_layout(T, H, I, topk).off[5];
+    return (size_t)decode_layout(T, H, I, topk).off[6];
 }
 
-extern "C" int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[6]) {
+extern "C" int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[7]) {
     if (!offsets) return MOE_ERR_NULL;
     if (!decode_shape_ok(T, H, I, topk)) return MOE_ERR_SHAPE;
     DecodeLayout L = decode_layout(T, H, I, topk);
-    for (int i = 0; i < 6; i++) offsets[i] = L.off[i];
+    for (int i = 0; i < 7; i++) offsets[i] = L.off[i];
     return MOE_OK;
 }
 
@@ -171,11 +154,11 @@ extern "C" int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes,
     if (!decode_shape_ok(T, H, I, topk)) return MOE_ERR_SHAPE;
     if (!workspace) return MOE_ERR_NULL;
     DecodeLayout L = decode_layout(T, H, I, topk);
-    if ((int64_t)ws_bytes < L.off[5]) return MOE_ERR_WORKSPACE;
+    if ((int64_t)ws_bytes < L.off[6]) return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MOE_ERR_ALIGN;
-    const int64_t words = (L.off[5] - L.off[4]) / 4;
+    const int64_t words = (L.off[6] - L.off[5]) / 4;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, as_stream(stream),
-                       (uint32_t*)((char*)workspace + L.off[4]), words, 0u);
+                       (uint32_t*)((char*)workspace + L.off[5]), words, 0u);
     return launch_status();
 }
 
@@ -189,16 +172,17 @@ extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, in
     if (!x_bf16 || !slot_ids || !weights || !workspace || !out_bf16) return MOE_ERR_NULL;
     if (n_slots > 0 && (!w13_q || !w13_s || !w2_q || !w2_s)) return MOE_ERR_NULL;
     DecodeLayout L = decode_layout(T, H, I, topk);
-    if ((int64_t)ws_bytes < L.off[5]) return MOE_ERR_WORKSPACE;
+    if ((int64_t)ws_bytes < L.off[6]) return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace) || (n_slots > 0 && (!aligned16(w13_q) || !aligned16(w2_q))) ||
         (reinterpret_cast<uintptr_t>(x_bf16) & 3u))
         return MOE_ERR_ALIGN;
     const int64_t R = T * topk;
     char* ws = (char*)workspace;
     float* c1 = (float*)(ws + L.off[0]);
-    uint8_t* aq = (uint8_t*)(ws + L.off[1]);
-    float* as = (float*)(ws + L.off[2]);
-    float* c2 = (float*)(ws + L.off[3]);
+    float* hbuf = (float*)(ws + L.off[1]);
+    uint8_t* aq = (uint8_t*)(ws + L.off[2]);
+    float* as = (float*)(ws + L.off[3]);
+    float* c2 = (float*)(ws + L.off[4]);
     const int64_t gH = H / 128, gI = I / 128, g2I = 2 * I / 128;
     auto st = as_stream(stream);
     if (gI <= 8) {
@@ -206,10 +190,10 @@ extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, in
         FusedDecodeArgs a;
         a.x = x_bf16; a.slots = slot_ids; a.weights = weights;
         a.w13 = w13_q; a.w13s = w13_s; a.w2 = w2_q; a.w2s = w2_s;
-        a.c1 = c1; a.aq = aq; a.as = as; a.c2 = c2; a.ctl = (uint32_t*)(ws + L.off[4]); a.out = out_bf16;
+        a.c1 = c1; a.h = hbuf; a.aq = aq; a.as = as; a.c2 = c2; a.out = out_bf16;
         a.T = (int)T; a.H = (int)H; a.I = (int)I; a.topk = (int)topk;
-        a.tiles_a = (int)(2 * I / 16); a.tiles_c = (int)(H / 16); a.n_a = (int)(R * a.tiles_a);
-        return fused_decode_two_launch(st, a, 1);
+        a.tiles_a = 0; a.tiles_c = (int)(H / 16); a.n_a = 0;
+        return fused_decode_two_launch(st, a);
     }
     // wider intermediate sizes: four launches
     // 1) gate/up per route, quantizing the bf16 token row on the fly

@@ -9,7 +9,7 @@
 //
 // MI355X design: one wavefront per (row, 512 columns); each lane owns 8
 // consecutive columns, 16 lanes form one 128-column group, and the group amax
-// is a 4-step butterfly inside the wave, so no LDS and no barrier is needed.
+// is four DPP row moves inside the wave, so no LDS and no barrier is needed.
 // The 8 codes of a lane leave as one 8-byte store.  The scale is amax/448 with
 // the correctly rounded fp32 division and each code is v/s rounded to nearest
 // even (clamped to +-448), matching the definition bit for bit in IDENTITY mode.
@@ -87,7 +87,7 @@ act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, i
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < kColsPerLane; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    amax = group_max<4>(amax);                 // 16 lanes = one 128-column group
+    amax = row16_max(amax);                    // 16 lanes = one 128-column group
     const float s = amax / 448.0f;
     uint32_t lo = 0, hi = 0;
     if (s != 0.0f) {

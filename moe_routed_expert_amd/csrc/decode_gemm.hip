@@ -46,7 +46,7 @@ __device__ __forceinline__ float quant_group_bf16_to_lds(const uint16_t* __restr
     const float v0 = bf16_to_f32((uint16_t)(pair & 0xFFFF));
     const float v1 = bf16_to_f32((uint16_t)(pair >> 16));
     float amax = __builtin_fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
-    amax = group_max<6>(amax);
+    amax = wave_max(amax);
     const float s = amax / 448.0f;
     const uint32_t codes = s != 0.0f ? enc2_e4m3(v0 / s, v1 / s) : 0u;
     reinterpret_cast<uint16_t*>(dst)[lane] = (uint16_t)codes;

@@ -79,6 +79,33 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// DPP lane moves (gfx9 encodings): quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror, row_bcast:15, row_bcast:31.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f32(float old, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                  __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                                                  0xF, false));
+}
+
+// Max over each row of 16 lanes, returned in every lane of the row (register-only DPP moves).
+__device__ __forceinline__ float row16_max(float v) {
+    v = __builtin_fmaxf(v, dpp_f32<0xB1>(v, v));    // quad_perm [1,0,3,2]
+    v = __builtin_fmaxf(v, dpp_f32<0x4E>(v, v));    // quad_perm [2,3,0,1]
+    v = __builtin_fmaxf(v, dpp_f32<0x141>(v, v));   // row_half_mirror: lane i <- 7-i within 8
+    v = __builtin_fmaxf(v, dpp_f32<0x140>(v, v));   // row_mirror: lane i <- 15-i within 16
+    return v;
+}
+
+// Max over the whole wave as a wave-uniform value: row maxima, then row_bcast:15 /
+// row_bcast:31 carry them into lane 63, which is read back as a scalar.
+__device__ __forceinline__ float wave_max(float v) {
+    v = row16_max(v);
+    v = __builtin_fmaxf(v, dpp_f32<0x142, 0xA>(v, v));   // rows 1,3 take lane 15 of rows 0,2
+    v = __builtin_fmaxf(v, dpp_f32<0x143, 0xC>(v, v));   // rows 2,3 take lane 31
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // 16x16x128 fp8 x fp8 -> fp32 MFMA (e4m3 operands, no block exponent scaling).
 // Operand layout (checked on gfx950): lane l holds row (A) / column (B) l%16 and
 // 32 K values for K-quarter l/16; both operands use the same K order, so any

@@ -10,23 +10,31 @@
 // (an L2 write-back and invalidate on this 8-XCD part) or device-scope
 // polling, both of which measured slower than one extra launch, so the step is:
 //
-//  * launch 1 (gate/up): route r, 16*NT rows of W13, all of K = H split over
-//    8 waves.  Each wave quantizes the 128-column groups of the bf16 token row
-//    it needs (amax/448, v/s -> e4m3) into LDS while its weight loads are in
-//    flight, runs one 16x16x128 e4m3 MFMA per K block and scales the block
-//    partial by a_s[kb] * w_s[n/128][kb].  Partials of the 8 waves are summed
-//    in LDS in wave order and the fp32 C1 rows are stored.
-//  * launch 2 (down + reduce): token t, 16 rows of W2 for all of t's routes;
-//    wave j owns route j.  It issues its W2 rows, rebuilds the route's
-//    activation from C1 itself (SiLU(gate)*up and the 1x128 requant of each
-//    128-column group, via LDS into MFMA operand order), multiplies, and parks
-//    the route's fp32 C2 rows in LDS and the workspace.  Wave 0 then sums the
-//    routes in ascending j with their routing weights and writes bf16 output.
+//  * launch 1 (gate/up + SiLU): route r, 8 activation columns.  The 16 MFMA
+//    columns of the tile are 8 gate rows of W13 and the 8 matching up rows, so
+//    after the split-K sum the tile forms h = SiLU(gate)*up for its columns.
+//    All of K = H is split over 8 waves; each wave quantizes the 128-column
+//    groups of the bf16 token row it needs (amax/448, v/s -> e4m3) into LDS
+//    while its weight loads are in flight, runs one 16x16x128 e4m3 MFMA per K
+//    block and scales the block partial by a_s[kb] * w_s[row/128][kb].  The
+//    8 waves' partials are summed in LDS in wave order; C1 and h are stored.
+//  * launch 2 (requant + down + reduce): token t, 16 rows of W2 for all of
+//    t's routes; wave j owns route j.  It loads the route's h (2 columns per
+//    lane per 128-group) before its W2 rows, so the 1x128 requant (amax/448,
+//    v/s -> e4m3, via LDS into MFMA operand order) runs while the weights are
+//    in flight, then multiplies and parks the route's fp32 C2 rows in LDS and
+//    the workspace.  Wave 0 sums the routes in ascending j with their routing
+//    weights and writes the bf16 output.
+//
+// Group maxima use DPP row moves and row broadcasts (no LDS round trips), and
+// every load a wave needs early (token row, h) is issued before its weight
+// loads, since loads retire in order.
 //
 // Results are deterministic: split-K partials and routes are combined in a
 // fixed order, and no floating-point atomics are used.
 #include "device.h"
 #include "host.h"
+#include "decode_args.h"
 
 namespace moe {
 
@@ -35,25 +43,6 @@ constexpr int kFdWaves = 8;
 constexpr int kFdUnroll = 2;
 constexpr int kFdMaxNkb2 = 8;          // I/128 handled with W2 rows held in registers
 
-struct FusedDecodeArgs {
-    const uint16_t* x;
-    const int32_t* slots;
-    const float* weights;
-    const uint8_t* w13;
-    const float* w13s;
-    const uint8_t* w2;
-    const float* w2s;
-    float* c1;
-    uint8_t* aq;
-    float* as;
-    float* c2;
-    uint32_t* ctl;     // reserved control words (unused by the two-launch form)
-    uint16_t* out;
-    int T, H, I, topk;
-    int tiles_a;       // 2I/16 gate/up tiles per route
-    int tiles_c;       // H/16 down tiles per token
-    int n_a;           // R * tiles_a
-};
 
 __device__ __forceinline__ v8i frag(uint4 lo, uint4 hi) {
     v8i f;
@@ -68,51 +57,58 @@ __device__ __forceinline__ v8i frag(v4i lo, v4i hi) {
 
 // Down tile 0 of every token also stores the activation rows it rebuilt.
 
-template <int NT>
+// Launch 1.  Tile = route r, act columns [8*j8, 8*j8+8): MFMA columns 0..7 are
+// gate rows 8*j8.., columns 8..15 the matching up rows I+8*j8.., so the tile
+// can form h = SiLU(gate)*up for its 8 columns after the split-K sum.
 __global__ void __launch_bounds__(kWave * kFdWaves) decode_gateup_kernel(FusedDecodeArgs a) {
-    constexpr int ROWS = kFdTile * NT;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int b = blockIdx.x;
     const int64_t r = b / a.tiles_a;
-    const int64_t n0 = (int64_t)(b % a.tiles_a) * ROWS;
+    const int64_t c0 = (int64_t)(b % a.tiles_a) * 8;            // first act column
     const int64_t N = 2 * (int64_t)a.I;
     const int slot = a.slots[r];
-    __shared__ float red[kFdWaves][ROWS];
+    __shared__ float red[kFdWaves][kFdTile];
     __shared__ __attribute__((aligned(16))) uint8_t xq[kFdWaves][kFdUnroll][128];
+    const int col = lane & 15;                                   // MFMA column of this lane
+    const int64_t wr = col < 8 ? c0 + col : a.I + c0 + (col - 8); // its W13 row
     if (slot < 0) {
-        if (threadIdx.x < ROWS) a.c1[r * N + n0 + threadIdx.x] = 0.0f;
+        if (threadIdx.x < kFdTile) {
+            const int64_t rr = threadIdx.x < 8 ? c0 + threadIdx.x : a.I + c0 + (threadIdx.x - 8);
+            a.c1[r * N + rr] = 0.0f;
+            if (threadIdx.x < 8) a.h[r * a.I + c0 + threadIdx.x] = 0.0f;
+        }
         return;
     }
     const int nkb = a.H / 128;
     const int kb0 = wave * nkb / kFdWaves, kb1 = (wave + 1) * nkb / kFdWaves;
     const int q16 = (lane / 16) * 16;
-    const uint8_t* wrow = a.w13 + (int64_t)slot * N * a.H + (n0 + (lane & 15)) * a.H + q16;
-    const float* wsrow = a.w13s + (int64_t)slot * (N / 128) * nkb + (n0 / 128) * nkb;
+    const uint8_t* wrow = a.w13 + (int64_t)slot * N * a.H + wr * a.H + q16;
+    const float* wsrow = a.w13s + (int64_t)slot * (N / 128) * nkb + (wr / 128) * nkb;  // per-lane scale row
     const uint16_t* xrow = a.x + (r / a.topk) * a.H;
-    v4f acc[NT];
-#pragma unroll
-    for (int c = 0; c < NT; c++) acc[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int kb = kb0; kb < kb1; kb += kFdUnroll) {
-        v4i blo[NT][kFdUnroll], bhi[NT][kFdUnroll], alo[kFdUnroll], ahi[kFdUnroll];
-        float sa[kFdUnroll];
+        v4i blo[kFdUnroll], bhi[kFdUnroll], alo[kFdUnroll], ahi[kFdUnroll];
+        float sa[kFdUnroll], sw[kFdUnroll];
+        uint32_t pair[kFdUnroll];
+        // token row first: its quantization then overlaps the weight stream (loads retire in order)
+#pragma unroll
+        for (int u = 0; u < kFdUnroll; u++)
+            if (kb + u < kb1) pair[u] = reinterpret_cast<const uint32_t*>(xrow + (int64_t)(kb + u) * 128)[lane];
 #pragma unroll
         for (int u = 0; u < kFdUnroll; u++) {
             if (kb + u < kb1) {
-#pragma unroll
-                for (int c = 0; c < NT; c++) {
-                    const uint8_t* wp = wrow + (int64_t)c * kFdTile * a.H + (int64_t)(kb + u) * 128;
-                    blo[c][u] = *reinterpret_cast<const v4i*>(wp);
-                    bhi[c][u] = *reinterpret_cast<const v4i*>(wp + 64);
-                }
+                const uint8_t* wp = wrow + (int64_t)(kb + u) * 128;
+                blo[u] = *reinterpret_cast<const v4i*>(wp);
+                bhi[u] = *reinterpret_cast<const v4i*>(wp + 64);
+                sw[u] = wsrow[kb + u];
             }
         }
 #pragma unroll
         for (int u = 0; u < kFdUnroll; u++) {
             if (kb + u < kb1) {
-                const uint32_t pair = reinterpret_cast<const uint32_t*>(xrow + (int64_t)(kb + u) * 128)[lane];
-                const float v0 = bf16_to_f32((uint16_t)(pair & 0xFFFF));
-                const float v1 = bf16_to_f32((uint16_t)(pair >> 16));
-                const float amax = group_max<6>(__builtin_fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
+                const float v0 = bf16_to_f32((uint16_t)(pair[u] & 0xFFFF));
+                const float v1 = bf16_to_f32((uint16_t)(pair[u] >> 16));
+                const float amax = wave_max(__builtin_fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
                 const float s = amax / 448.0f;
                 reinterpret_cast<uint16_t*>(xq[wave][u])[lane] = (uint16_t)(s != 0.0f ? enc2_e4m3(v0 / s, v1 / s) : 0u);
                 sa[u] = s;
@@ -129,44 +125,55 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_gateup_kernel(FusedDe
 #pragma unroll
         for (int u = 0; u < kFdUnroll; u++) {
             if (kb + u < kb1) {
-                const v8i af = frag(alo[u], ahi[u]);
-#pragma unroll
-                for (int c = 0; c < NT; c++) {
-                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f p = mfma16x16x128_e4m3(af, frag(blo[c][u], bhi[c][u]), z);
-                    acc[c] += p * (sa[u] * wsrow[kb + u]);
-                }
+                const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const v4f p = mfma16x16x128_e4m3(frag(alo[u], ahi[u]), frag(blo[u], bhi[u]), z);
+                acc += p * (sa[u] * sw[u]);
             }
         }
         wave_lds_fence();
     }
-    if (lane < kFdTile) {
-#pragma unroll
-        for (int c = 0; c < NT; c++) red[wave][c * kFdTile + lane] = acc[c][0];
-    }
+    if (lane < kFdTile) red[wave][lane] = acc[0];
     __syncthreads();
-    if (threadIdx.x < ROWS) {
+    if (threadIdx.x < kFdTile) {
         float t = red[0][threadIdx.x];
 #pragma unroll
         for (int w = 1; w < kFdWaves; w++) t += red[w][threadIdx.x];
-        a.c1[r * N + n0 + threadIdx.x] = t;
+        const int64_t rr = threadIdx.x < 8 ? c0 + threadIdx.x : a.I + c0 + (threadIdx.x - 8);
+        a.c1[r * N + rr] = t;
+        const float up = __shfl_down(t, 8, kFdTile);            // lanes 0..7 get their up value
+        if (threadIdx.x < 8) a.h[r * a.I + c0 + threadIdx.x] = (t / (1.0f + expf(-t))) * up;
     }
 }
 
+// Launch 2: token t, 16 rows of W2, 8 waves, wave j owns route j (then j+8,
+// ...); the routes' C2 rows meet in LDS.  The token's slots and the routing
+// weights of its active routes are fetched once into LDS.
 template <int NKB2>
-__global__ void __launch_bounds__(kWave * kFdWaves) decode_down_kernel(FusedDecodeArgs a) {
+__global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDecodeArgs a) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t t = blockIdx.x / a.tiles_c;
     const int ntile = blockIdx.x % a.tiles_c;
     const int64_t n0 = (int64_t)ntile * kFdTile;
     const int q16 = (lane / 16) * 16;
     __shared__ float part[64][kFdTile];
+    __shared__ int s_slot[64];
+    __shared__ float s_w[64];
     __shared__ __attribute__((aligned(16))) uint8_t hq[kFdWaves][NKB2][128];
+    if (threadIdx.x < a.topk) {
+        const int sl = a.slots[t * a.topk + threadIdx.x];
+        s_slot[threadIdx.x] = sl;
+        s_w[threadIdx.x] = sl >= 0 ? a.weights[t * a.topk + threadIdx.x] : 0.0f;
+    }
+    __syncthreads();
     for (int j = wave; j < a.topk; j += kFdWaves) {
         const int64_t r = t * a.topk + j;
-        const int slot = a.slots[r];
+        const int slot = s_slot[j];
         float val = 0.0f;
         if (slot >= 0) {
+            const float* hrow = a.h + r * a.I + 2 * lane;
+            float2 hv[NKB2];
+#pragma unroll
+            for (int kb = 0; kb < NKB2; kb++) hv[kb] = *reinterpret_cast<const float2*>(hrow + kb * 128);
             v4i blo[NKB2], bhi[NKB2];
             const uint8_t* wrow = a.w2 + (int64_t)slot * a.H * a.I + (n0 + (lane & 15)) * a.I + q16;
 #pragma unroll
@@ -174,22 +181,12 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down_kernel(FusedDeco
                 blo[kb] = *reinterpret_cast<const v4i*>(wrow + kb * 128);
                 bhi[kb] = *reinterpret_cast<const v4i*>(wrow + kb * 128 + 64);
             }
-            // the route's activation, one 128-column group per K block (2 columns per lane)
-            const float* c1row = a.c1 + r * 2 * a.I;
-            float2 gt[NKB2], up[NKB2];
-#pragma unroll
-            for (int kb = 0; kb < NKB2; kb++) {
-                gt[kb] = *reinterpret_cast<const float2*>(c1row + kb * 128 + 2 * lane);
-                up[kb] = *reinterpret_cast<const float2*>(c1row + a.I + kb * 128 + 2 * lane);
-            }
             float sa[NKB2];
 #pragma unroll
             for (int kb = 0; kb < NKB2; kb++) {
-                const float h0 = (gt[kb].x / (1.0f + expf(-gt[kb].x))) * up[kb].x;
-                const float h1 = (gt[kb].y / (1.0f + expf(-gt[kb].y))) * up[kb].y;
-                const float amax = group_max<6>(__builtin_fmaxf(__builtin_fabsf(h0), __builtin_fabsf(h1)));
+                const float amax = wave_max(__builtin_fmaxf(__builtin_fabsf(hv[kb].x), __builtin_fabsf(hv[kb].y)));
                 const float s = amax / 448.0f;
-                const uint16_t codes = (uint16_t)(s != 0.0f ? enc2_e4m3(h0 / s, h1 / s) : 0u);
+                const uint16_t codes = (uint16_t)(s != 0.0f ? enc2_e4m3(hv[kb].x / s, hv[kb].y / s) : 0u);
                 reinterpret_cast<uint16_t*>(hq[wave][kb])[lane] = codes;
                 sa[kb] = s;
                 if (ntile == 0) {
@@ -211,7 +208,6 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down_kernel(FusedDeco
             wave_lds_fence();
             val = acc[0];
         } else if (ntile == 0) {
-            // inactive route: its activation rows are zero
             for (int i = lane; i < a.I / 4; i += kWave) reinterpret_cast<uint32_t*>(a.aq + r * a.I)[i] = 0u;
             if (lane < NKB2) a.as[r * NKB2 + lane] = 0.0f;
         }
@@ -221,38 +217,29 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down_kernel(FusedDeco
         }
     }
     __syncthreads();
-    if (wave == 0 && lane < kFdTile) {
+    if (threadIdx.x < kFdTile) {
         float o = 0.0f;
-        for (int j = 0; j < a.topk; j++) {
-            if (a.slots[t * a.topk + j] < 0) continue;            // routing weight never read
-            o += a.weights[t * a.topk + j] * part[j][lane];
-        }
-        a.out[t * a.H + n0 + lane] = f32_to_bf16(o);
+        for (int j = 0; j < a.topk; j++)
+            if (s_slot[j] >= 0) o += s_w[j] * part[j][threadIdx.x];
+        a.out[t * a.H + n0 + threadIdx.x] = f32_to_bf16(o);
     }
 }
 
-template <int NT>
-static int launch_two_nt(hipStream_t st, FusedDecodeArgs a) {
-    a.tiles_a = 2 * a.I / (kFdTile * NT);
+int fused_decode_two_launch(hipStream_t st, FusedDecodeArgs a) {
+    if (a.I / 128 < 1 || a.I / 128 > kFdMaxNkb2) return MOE_ERR_SHAPE;
+    a.tiles_a = a.I / 8;
     a.n_a = a.T * a.topk * a.tiles_a;
-    dim3 block(kWave * kFdWaves);
-    hipLaunchKernelGGL((decode_gateup_kernel<NT>), dim3((unsigned)a.n_a), block, 0, st, a);
+    a.tiles_c = a.H / kFdTile;
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3((unsigned)a.n_a), dim3(kWave * kFdWaves), 0, st, a);
     const unsigned down = (unsigned)(a.T * a.tiles_c);
     switch (a.I / 128) {
-#define MOE_FD_CASE(n) case n: hipLaunchKernelGGL((decode_down_kernel<n>), dim3(down), block, 0, st, a); break;
+#define MOE_FD_CASE(n) case n: hipLaunchKernelGGL((decode_down16_kernel<n>), dim3(down), dim3(kWave * kFdWaves), 0, st, a); break;
         MOE_FD_CASE(1) MOE_FD_CASE(2) MOE_FD_CASE(3) MOE_FD_CASE(4)
         MOE_FD_CASE(5) MOE_FD_CASE(6) MOE_FD_CASE(7) MOE_FD_CASE(8)
 #undef MOE_FD_CASE
         default: return MOE_ERR_SHAPE;
     }
     return launch_status();
-}
-
-int fused_decode_two_launch(hipStream_t st, const FusedDecodeArgs& a, int nt) {
-    if (a.I / 128 < 1 || a.I / 128 > kFdMaxNkb2) return MOE_ERR_SHAPE;
-    if (nt == 4 && (2 * a.I) % 64 == 0) return launch_two_nt<4>(st, a);
-    if (nt >= 2 && (2 * a.I) % 32 == 0) return launch_two_nt<2>(st, a);
-    return launch_two_nt<1>(st, a);
 }
 
 }  // namespace moe

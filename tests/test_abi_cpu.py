@@ -108,7 +108,7 @@ def test_fused_decode_workspace_and_checks():
     L = m.lib()
     lay = m.fused_decode_workspace_layout(1, 2048, 768, 8)
     assert lay["c1"] == 0
-    assert lay["aq"] >= 8 * 1536 * 4 and lay["as"] >= lay["aq"] + 8 * 768
+    assert lay["h"] >= 8 * 1536 * 4 and lay["aq"] >= lay["h"] + 8 * 768 * 4 and lay["as"] >= lay["aq"] + 8 * 768
     assert lay["c2"] >= lay["as"] + 8 * 6 * 4 and lay["ctl"] >= lay["c2"] + 8 * 2048 * 4
     assert lay["total"] == m.fused_decode_workspace_size(1, 2048, 768, 8)
     assert all(v % 256 == 0 for v in lay.values())

@@ -53,11 +53,12 @@ def check_against_oracle(dd: DevDecode, ref, im, host_weights=None):
     got = u16(dd.out)
     assert_bf16_close(got, ref, what="fused decode out")
     c1 = dd.region("c1", torch.float32, (R, 2 * c.I)).cpu().numpy()
+    hh = dd.region("h", torch.float32, (R, c.I)).cpu().numpy()
     c2 = dd.region("c2", torch.float32, (R, c.H)).cpu().numpy()
     aq = dd.region("aq", torch.uint8, (R, c.I)).cpu().numpy()
     as_ = dd.region("as", torch.float32, (R, c.I // 128)).cpu().numpy()
     inactive = c.slot_ids.reshape(-1) < 0
-    for name, arr in (("c1", c1), ("c2", c2), ("as", as_)):
+    for name, arr in (("c1", c1), ("h", hh), ("c2", c2), ("as", as_)):
         assert np.all(arr[inactive].view(np.uint32) == 0), name + ": inactive rows must be +0.0"
     assert np.all(aq[inactive] == 0)
     ctl = dd.ws[dd.lay["ctl"]:dd.lay["total"]].cpu().numpy()
@@ -66,6 +67,8 @@ def check_against_oracle(dd: DevDecode, ref, im, host_weights=None):
         hw = host_weights or [t.cpu().numpy() for t in (c.w13_q, c.w13_s)]
         bound = gemm_abs_bound(im["xq"], im["xs"], hw[0], hw[1], c.slot_ids.reshape(-1), np.arange(R) // c.topk)
         assert_within_bound(c1, im["c1"], bound, what="c1")
+        g, u = im["c1"][:, :c.I].astype(np.float64), im["c1"][:, c.I:].astype(np.float64)
+        assert_close(hh[~inactive], (g / (1 + np.exp(-g)) * u)[~inactive], rel_l2=1e-4, max_abs=1e-4, what="h")
         assert_close(c2[~inactive], im["c2"][~inactive], what="c2")
 
 
