@@ -120,9 +120,11 @@ int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, in
 /*
  * moe_pick_block_m  [tile]
  *   The M tile of the grouped GEMM for `routes` routed rows over `experts`
- *   experts: next power of two of ceil(routes/experts), clamped to [16, 128]
- *   (about 6, 24, 96 rows per expert give 16, 32, 128).  Pure function.
- *   Returns 16 when routes or experts is <= 0.
+ *   experts.  As on the page, the tile grows with rows per expert; the
+ *   thresholds are MI355X's (a sweep of every tile at 6, 24 and 96 rows per
+ *   expert): the smallest power of two >= 2*ceil(routes/experts), clamped to
+ *   [32, 64], so 6 rows per expert give 32 and 24 or 96 give 64.  Pure
+ *   function of its two arguments; returns 32 when either is <= 0.
  */
 int moe_pick_block_m(int64_t routes, int64_t experts);
 

@@ -88,10 +88,13 @@ extern "C" const char* moe_status_string(int status) {
 extern "C" const char* moe_last_hip_error(void) { return g_last_hip_error; }
 
 extern "C" int moe_pick_block_m(int64_t routes, int64_t experts) {
-    if (routes <= 0 || experts <= 0) return 16;
-    const int64_t per = ceil_div(routes, experts);
-    int64_t bm = 16;
-    while (bm < per && bm < 128) bm <<= 1;
+    // Smallest power of two >= 2 * ceil(routes / experts), clamped to [32, 64]: the tile
+    // grows with rows per expert as on the pages, with thresholds from a sweep of all
+    // tiles on MI355X (6 rows per expert -> 32, 24 and 96 -> 64).
+    if (routes <= 0 || experts <= 0) return 32;
+    const int64_t per = 2 * ceil_div(routes, experts);
+    int64_t bm = 32;
+    while (bm < per && bm < 64) bm <<= 1;
     return (int)bm;
 }
 
