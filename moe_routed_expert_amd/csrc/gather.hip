@@ -4,10 +4,11 @@
 // moved as bytes; 64-bit row bases; masked tails).
 //
 // MI355X design: one wavefront per destination row.  The row bytes move as
-// 16-byte vectors, eight per lane in flight before the first store, so a
+// 16-byte vectors, up to eight per lane in flight before the first store, so a
 // 7168-byte row is 7 loads per lane; the row's scale words ride in the same
-// wave (lanes 0..g-1), so there is no second launch and no second walk of the
-// map.  Rows or strides that are not 16-byte aligned fall back to a byte loop.
+// wave (lanes 0..g-1) with its first chunk, so there is no second launch and
+// no second walk of the map.  Stores are non-temporal.  Rows or strides that
+// are not 16-byte aligned fall back to a byte loop.
 #include "device.h"
 #include "host.h"
 
@@ -15,67 +16,65 @@ namespace moe {
 namespace {
 
 constexpr int kRowsPerBlock = 4;   // 4 waves, one row each
-constexpr int kVecInFlight = 8;
+constexpr int kVecInFlight = 8;    // 16-byte loads per lane issued before the first store
+
+// Destination rows are written once and read by a later kernel, so they are
+// stored non-temporally (they stream past the caches instead of evicting the
+// source rows, which repeat across the map).
+__device__ __forceinline__ void nt_store(v4i* p, v4i v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void nt_store(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
 
 template <bool VEC>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64 * kRowsPerBlock)
 gather_rows_scales_kernel(const uint8_t* __restrict__ src_q, int64_t src_q_stride,
                           const uint32_t* __restrict__ src_s, int64_t src_s_stride,
                           int64_t k, int64_t g, const int32_t* __restrict__ dst2src, int64_t n_dst,
                           uint8_t* __restrict__ dst_q, int64_t dst_q_stride,
                           uint32_t* __restrict__ dst_s, int64_t dst_s_stride) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = threadIdx.x / kWave;
-    for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave; row < n_dst;
-         row += (int64_t)gridDim.x * kRowsPerBlock) {
-        const int64_t src = dst2src[row];
-        uint8_t* dq = dst_q + row * dst_q_stride;   // int64 row base
-        uint32_t* ds = dst_s + row * dst_s_stride;
-        if (src < 0) {
-            if constexpr (VEC) {
-                const uint4 z = make_uint4(0, 0, 0, 0);
-                for (int64_t c = lane; c < k / 16; c += kWave) reinterpret_cast<uint4*>(dq)[c] = z;
-            } else {
-                for (int64_t c = lane; c < k; c += kWave) dq[c] = 0;
-            }
-            for (int64_t c = lane; c < g; c += kWave) ds[c] = 0u;
-            continue;
-        }
-        const uint8_t* sq = src_q + src * src_q_stride;
-        const uint32_t* ss = src_s + src * src_s_stride;
-        // scales first: one word per lane, issued before the row stream
-        uint32_t sw[2];
-        bool sv[2];
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            int64_t c = lane + i * kWave;
-            sv[i] = c < g;
-            if (sv[i]) sw[i] = ss[c];
-        }
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+    if (row >= n_dst) return;
+    const int64_t src = dst2src[row];
+    uint8_t* dq = dst_q + row * dst_q_stride;   // int64 row base
+    uint32_t* ds = dst_s + row * dst_s_stride;
+    if (src < 0) {
         if constexpr (VEC) {
-            const int64_t nvec = k / 16;
-            const uint4* s4 = reinterpret_cast<const uint4*>(sq);
-            uint4* d4 = reinterpret_cast<uint4*>(dq);
-            for (int64_t base = 0; base < nvec; base += kWave * kVecInFlight) {
-                uint4 buf[kVecInFlight];
-#pragma unroll
-                for (int i = 0; i < kVecInFlight; i++) {
-                    int64_t c = base + i * kWave + lane;
-                    if (c < nvec) buf[i] = s4[c];
-                }
-#pragma unroll
-                for (int i = 0; i < kVecInFlight; i++) {
-                    int64_t c = base + i * kWave + lane;
-                    if (c < nvec) d4[c] = buf[i];
-                }
-            }
+            const v4i z = {0, 0, 0, 0};
+            for (int64_t c = lane; c < k / 16; c += kWave) nt_store(reinterpret_cast<v4i*>(dq) + c, z);
         } else {
-            for (int64_t c = lane; c < k; c += kWave) dq[c] = sq[c];
+            for (int64_t c = lane; c < k; c += kWave) dq[c] = 0;
         }
+        for (int64_t c = lane; c < g; c += kWave) nt_store(ds + c, 0u);
+        return;
+    }
+    const uint8_t* sq = src_q + src * src_q_stride;
+    const uint32_t* ss = src_s + src * src_s_stride;
+    if constexpr (VEC) {
+        const int64_t nvec = k / 16;
+        const v4i* s4 = reinterpret_cast<const v4i*>(sq);
+        v4i* d4 = reinterpret_cast<v4i*>(dq);
+        for (int64_t base = 0; base < nvec; base += kWave * kVecInFlight) {
+            v4i buf[kVecInFlight];
+            const bool sv = base == 0 && lane < g;      // the row's scales ride with its first chunk
+            const uint32_t sw = ss[sv ? lane : 0];
+            // unconditional loads (indices clamped to the row) so all of them issue back to back
 #pragma unroll
-        for (int i = 0; i < 2; i++)
-            if (sv[i]) ds[lane + i * kWave] = sw[i];
-        for (int64_t c = lane + 2 * kWave; c < g; c += kWave) ds[c] = ss[c];
+            for (int i = 0; i < kVecInFlight; i++) {
+                const int64_t c = base + i * kWave + lane;
+                buf[i] = s4[c < nvec ? c : nvec - 1];
+            }
+#pragma unroll
+            for (int i = 0; i < kVecInFlight; i++) {
+                const int64_t c = base + i * kWave + lane;
+                if (c < nvec) nt_store(d4 + c, buf[i]);
+            }
+            if (sv) nt_store(ds + lane, sw);
+        }
+        // scale words beyond the first 64 (and all of them for an empty row)
+        for (int64_t c = lane + (nvec > 0 ? kWave : 0); c < g; c += kWave) nt_store(ds + c, ss[c]);
+    } else {
+        for (int64_t c = lane; c < k; c += kWave) dq[c] = sq[c];
+        for (int64_t c = lane; c < g; c += kWave) nt_store(ds + c, ss[c]);
     }
 }
 
@@ -99,9 +98,9 @@ extern "C" int moe_gather_rows_scales(const void* src_q, int64_t src_q_stride,
     if (src_q_stride < k || dst_q_stride < k || src_s_stride < g || dst_s_stride < g) return MOE_ERR_SHAPE;
     const bool vec = k % 16 == 0 && src_q_stride % 16 == 0 && dst_q_stride % 16 == 0 &&
                      aligned16(src_q) && aligned16(dst_q);
-    int64_t blocks = ceil_div(n_dst, kRowsPerBlock);
-    if (blocks > 65536) blocks = 65536;
-    dim3 grid((unsigned)blocks), block(256);
+    const int64_t blocks = ceil_div(n_dst, kRowsPerBlock);
+    if (blocks > 0x7FFFFFFF) return MOE_ERR_SHAPE;
+    dim3 grid((unsigned)blocks), block(64 * kRowsPerBlock);
     auto s = as_stream(stream);
     if (vec)
         hipLaunchKernelGGL(gather_rows_scales_kernel<true>, grid, block, 0, s,

@@ -13,6 +13,9 @@
 namespace moe {
 namespace {
 
+constexpr int kRoutesPerPass = 8;
+__device__ const float kZeroWeight = 0.0f;
+
 template <int DT>
 __global__ void __launch_bounds__(256)
 topk_reduce_kernel(const void* __restrict__ y, int64_t y_stride, const int32_t* __restrict__ slot_ids,
@@ -23,15 +26,37 @@ topk_reduce_kernel(const void* __restrict__ y, int64_t y_stride, const int32_t* 
     const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= T || c >= chunks) return;
     const int64_t h0 = c * 4;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t j = 0; j < topk; j++) {
-        const int64_t rt = t * topk + j;
-        if (slot_ids[rt] < 0) continue;           // inactive: weight and rows untouched
-        const float w = weights[rt];
-        const int64_t row = route_rows ? (int64_t)route_rows[rt] : rt;
+    // columns of this thread, clamped into the row (the clamped tail values are never stored)
+    int64_t col[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            if (h0 + i < H) acc[i] += w * load_as_f32<DT>(y, row * y_stride + h0 + i);
+    for (int i = 0; i < 4; i++) col[i] = h0 + i < H ? h0 + i : H - 1;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t j0 = 0; j0 < topk; j0 += kRoutesPerPass) {
+        // one pass issues the loads of up to 8 routes back to back with no per-route branch; an
+        // inactive route reads its routing weight from a constant zero instead of the weights
+        // array, and its y values are dropped by a select
+        int32_t sl[kRoutesPerPass];
+        int64_t rt[kRoutesPerPass];
+#pragma unroll
+        for (int u = 0; u < kRoutesPerPass; u++) {
+            rt[u] = t * topk + (j0 + u < topk ? j0 + u : topk - 1);
+            sl[u] = slot_ids[rt[u]];
+        }
+        float w[kRoutesPerPass], v[kRoutesPerPass][4];
+        bool on[kRoutesPerPass];
+#pragma unroll
+        for (int u = 0; u < kRoutesPerPass; u++) {
+            on[u] = j0 + u < topk && sl[u] >= 0;
+            w[u] = *(on[u] ? weights + rt[u] : &kZeroWeight);
+            const int64_t rr = route_rows ? (int64_t)route_rows[rt[u]] : rt[u];
+            const int64_t row = on[u] ? rr : 0;
+#pragma unroll
+            for (int i = 0; i < 4; i++) v[u][i] = load_as_f32<DT>(y, row * y_stride + col[i]);
+        }
+#pragma unroll
+        for (int u = 0; u < kRoutesPerPass; u++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[i] = on[u] ? acc[i] + w[u] * v[u][i] : acc[i];
     }
     uint16_t* o = out + t * out_stride + h0;
     if (h0 + 4 <= H && (reinterpret_cast<uintptr_t>(o) & 7u) == 0) {
