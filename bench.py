@@ -22,9 +22,11 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-prefill]
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -63,6 +65,50 @@ class Timer:
 
 
 LAYERS = 16
+
+DECODE_SOURCES = ("moe_routed_expert_amd/csrc/fused_decode.hip", "moe_routed_expert_amd/csrc/device.h",
+                  "moe_routed_expert_amd/csrc/decode_args.h")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_h2048_i768_top8_pmc.md")
+
+
+def sources_sha256(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode step from the committed FETCH_SIZE/WRITE_SIZE summary, or None when the
+    summary is absent or was taken from other kernel sources."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"^TRAFFIC (\{.*\})$", text, flags=re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("sources_sha256") != sources_sha256(DECODE_SOURCES):
+        return None
+    return rec
+
+
+def copy_calibration(torch, m):
+    """One plain copy of known size: the gather entry point with an identity map moves 16384 rows of
+    4096 bytes plus 32 scale words each (64 MiB + 2 MiB read, the same written)."""
+    dev = torch.device("cuda")
+    n, k, g = 16384, 4096, 32
+    src_q = torch.randint(0, 256, (n, k), dtype=torch.uint8, device=dev)
+    src_s = torch.rand((n, g), dtype=torch.float32, device=dev)
+    dst_q, dst_s = torch.empty_like(src_q), torch.empty_like(src_s)
+    ident = torch.arange(n, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    m.gather_rows_scales(src_q, src_s, ident, dst_q, dst_s)
+    torch.cuda.synchronize()
+    assert torch.equal(dst_q, src_q)
+    return dict(rows=n, k=k, g=g, bytes_read=n * (k + 4 * g), bytes_written=n * (k + 4 * g))
 
 
 def decode_pools(torch, wl, H, I, S, seed):
@@ -230,6 +276,7 @@ def main():
     torch.cuda.init()
     reps = max(1, args.steps // LAYERS)
     steps = reps * LAYERS
+    calib = copy_calibration(torch, m)
 
     log("decode H=2048 I=768: building %d layer pools" % LAYERS)
     pools = decode_pools(torch, wl, 2048, 768, 64, seed=1)
@@ -254,9 +301,14 @@ def main():
         if not args.skip_prefill:
             log("prefill 24576 routes")
             extra["prefill"] = prefill_bench(torch, m, wl, 4096, 256, 6, 4096, 1024, 10)
-    roof = dict(bound="hbm", kernel="fused_decode_kernel (one launch per decode step, H=2048, I=768, 8/8 active)",
+    tr = measured_traffic()
+    roof = dict(bound="hbm",
+                kernel="moe_fused_decode step = decode_gateup_kernel + decode_down16_kernel (H=2048, I=768, "
+                       "8/8 active); one launch = one step",
                 bytes_per_launch=head["bytes_streamed"], us_per_launch=head["us_per_step_mean"],
-                achieved=head["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s", frac=head["hbm_frac"], traffic=None)
+                achieved=head["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s", frac=head["hbm_frac"],
+                traffic=tr["traffic_bytes_per_step"] if tr else None)
+    extra["copy_calibration"] = calib
     cpu = None
     if not args.skip_cpu:
         log("cpu baseline (oracle)")
