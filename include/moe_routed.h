@@ -180,14 +180,21 @@ int moe_topk_reduce(const void* y, int y_dt, int64_t y_stride,
  *   [2] aq   R x I            fp8 activation (1x128 requant of h)
  *   [3] as   R x ceil(I/128)  fp32 activation scales
  *   [4] c2   R x H            fp32 down output
- *   [5] ctl  reserved control words
+ *   [5] ctl  control block: the error word, per-route tile counters and
+ *            publish words, and the last-seen publish value of each down
+ *            tile (hand-off state of the one-launch step)
  *   [6] total size in bytes
  * Regions [0]..[4] may hold anything between calls: every call rewrites them
  * completely, and an inactive route's c1/h/aq/as/c2 rows become exact zeros
  * (h is only written when I <= 1024; wider I runs the step as four launches
  * that do not store h).  The control region must be cleared once with
- * moe_fused_decode_workspace_init before the first call.  Size 0 /
- * MOE_ERR_SHAPE for shapes moe_fused_decode rejects.
+ * moe_fused_decode_workspace_init before the first call and carries state
+ * from call to call: a workspace serves one shape (T, H, I, topk), and calls
+ * that share it must not overlap in time (e.g. on two streams without an
+ * event between them).  Its first 32-bit word is the error word: nonzero
+ * after a call means a hand-off wait gave up, the step's output is not valid,
+ * and the workspace must be initialized again.  Size 0 / MOE_ERR_SHAPE for
+ * shapes moe_fused_decode rejects.
  */
 size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk);
 int moe_fused_decode_workspace_layout(int64_t T, int64_t H, int64_t I, int64_t topk, int64_t offsets[7]);
@@ -205,8 +212,13 @@ int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes, int64_t T,
  *   w13_s [n_slots][ceil(2I/128)][ceil(H/128)] fp32;  w2_q [n_slots][H][I];
  *   w2_s [n_slots][ceil(H/128)][ceil(I/128)].
  *   Requirements: H % 128 == 0, I % 128 == 0, 1 <= topk <= 64,
- *   T * topk <= 65535; 16-byte aligned weights and workspace, 4-byte aligned x.  Launch shapes depend on (T, H, I, topk)
- *   only, so one captured graph serves any slot/weight/x contents.
+ *   T * topk <= 65535; 16-byte aligned weights and workspace, 4-byte aligned x.
+ *   Launch shapes depend on (T, H, I, topk) and the device only, so one
+ *   captured graph serves any slot/weight/x contents.  For small steps
+ *   (H <= 2048, I <= 1024, I/8 even or a multiple of 3) whose workgroups all
+ *   fit on the device at once, the step is a single launch in which gate/up
+ *   tiles hand h to the down tiles through the workspace's control block;
+ *   otherwise it is two launches (I <= 1024) or four (wider I).
  */
 int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk,
                      const int32_t* slot_ids, const float* weights, int64_t n_slots,

@@ -55,7 +55,7 @@ DecodeLayout decode_layout(int64_t T, int64_t H, int64_t I, int64_t topk) {
     L.off[2] = o; o = align256(o + R * I);                    // aq fp8
     L.off[3] = o; o = align256(o + R * ceil_div(I, 128) * 4); // as f32
     L.off[4] = o; o = align256(o + R * H * 4);                // c2 f32
-    L.off[5] = o; o = align256(o + 256);                      // ctl: reserved control words
+    L.off[5] = o; o = align256(o + decode_ctl_bytes(T, H, I, topk));  // ctl: hand-off words
     L.off[6] = o;
     return L;
 }
@@ -189,14 +189,16 @@ extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, in
     const int64_t gH = H / 128, gI = I / 128, g2I = 2 * I / 128;
     auto st = as_stream(stream);
     if (gI <= 8) {
-        // gate/up launch + down/reduce launch
+        // one launch when the step fits on the device at once, else gate/up launch + down/reduce launch
         FusedDecodeArgs a;
         a.x = x_bf16; a.slots = slot_ids; a.weights = weights;
         a.w13 = w13_q; a.w13s = w13_s; a.w2 = w2_q; a.w2s = w2_s;
         a.c1 = c1; a.h = hbuf; a.aq = aq; a.as = as; a.c2 = c2; a.out = out_bf16;
+        a.ctl = (uint32_t*)(ws + L.off[5]);
         a.T = (int)T; a.H = (int)H; a.I = (int)I; a.topk = (int)topk;
-        a.tiles_a = 0; a.tiles_c = (int)(H / 16); a.n_a = 0;
-        return fused_decode_two_launch(st, a);
+        a.tiles_a = 0; a.tiles_c = 0; a.n_a = 0;
+        const int rc = fused_decode_one_launch(st, a);
+        return rc == 1 ? fused_decode_two_launch(st, a) : rc;
     }
     // wider intermediate sizes: four launches
     // 1) gate/up per route, quantizing the bf16 token row on the fly

@@ -59,6 +59,19 @@ __device__ __forceinline__ v8i frag(v4i lo, v4i hi) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// 1x128 requant of an activation pair inside the fused step (the a3 step, held
+// to tolerance): s = amax/448 exactly, codes e4m3(v/s) with v/s formed as
+// v * (448 * rcp(amax)), within a few fp32 ulps of the quotient before the
+// e4m3 rounding.  Groups whose amax is tiny take exact divisions.
+__device__ __forceinline__ uint16_t requant_pair(float v0, float v1, float amax, float& s) {
+    s = amax / 448.0f;
+    if (amax >= 0x1p-100f) {
+        const float inv = 448.0f * __builtin_amdgcn_rcpf(amax);
+        return (uint16_t)enc2_e4m3(v0 * inv, v1 * inv);
+    }
+    return (uint16_t)(s != 0.0f ? enc2_e4m3(v0 / s, v1 / s) : 0u);
+}
+
 // Launch 1.  Tile = route r, act columns [8*j8, 8*j8+8): MFMA columns 0..7 are
 // gate rows 8*j8.., columns 8..15 the matching up rows I+8*j8.., so the tile
 // can form h = SiLU(gate)*up for its 8 columns after the split-K sum.
@@ -187,13 +200,17 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down8_kernel(FusedDec
                 blo[i] = *reinterpret_cast<const v4i*>(wrow + kb * 128);
                 bhi[i] = *reinterpret_cast<const v4i*>(wrow + kb * 128 + 64);
             }
+            // the tile's W2 block scales travel with its fragments
             const float* wsrow = a.w2s + (int64_t)slot * (a.H / 128) * NKB2 + (n0 / 128) * NKB2;
+            float sw[NKB2];
+#pragma unroll
+            for (int kb = 0; kb < NKB2; kb++) sw[kb] = wsrow[kb];
             float sa[NKB2];
 #pragma unroll
             for (int kb = 0; kb < NKB2; kb++) {
                 const float amax = wave_max(__builtin_fmaxf(__builtin_fabsf(hv[kb].x), __builtin_fabsf(hv[kb].y)));
-                const float s = amax / 448.0f;
-                const uint16_t codes = (uint16_t)(s != 0.0f ? enc2_e4m3(hv[kb].x / s, hv[kb].y / s) : 0u);
+                float s;
+                const uint16_t codes = requant_pair(hv[kb].x, hv[kb].y, amax, s);
                 reinterpret_cast<uint16_t*>(hq[wave][kb])[lane] = codes;
                 sa[kb] = s;
                 if (ntile == 0) {
@@ -218,8 +235,8 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down8_kernel(FusedDec
                 const v4i bl = b_on ? blo[i] : zero4, bh = b_on ? bhi[i] : zero4;
                 const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
                 const v4f p = mfma16x16x128_e4m3(frag(alo, ahi), frag(bl, bh), z);
-                const float f0 = sa[i] * wsrow[i];
-                const float f1 = has1 ? sa[(NS + i) % NKB2] * wsrow[(NS + i) % NKB2] : 0.0f;
+                const float f0 = sa[i] * sw[i];
+                const float f1 = has1 ? sa[(NS + i) % NKB2] * sw[(NS + i) % NKB2] : 0.0f;
                 acc += strm == 0 ? p[0] * f0 : p[1] * f1;
             }
             wave_lds_fence();
@@ -280,12 +297,17 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDe
                 blo[kb] = *reinterpret_cast<const v4i*>(wrow + kb * 128);
                 bhi[kb] = *reinterpret_cast<const v4i*>(wrow + kb * 128 + 64);
             }
+            // the tile's W2 block scales travel with its fragments
+            const float* wsrow = a.w2s + (int64_t)slot * (a.H / 128) * NKB2 + (n0 / 128) * NKB2;
+            float sw[NKB2];
+#pragma unroll
+            for (int kb = 0; kb < NKB2; kb++) sw[kb] = wsrow[kb];
             float sa[NKB2];
 #pragma unroll
             for (int kb = 0; kb < NKB2; kb++) {
                 const float amax = wave_max(__builtin_fmaxf(__builtin_fabsf(hv[kb].x), __builtin_fabsf(hv[kb].y)));
-                const float s = amax / 448.0f;
-                const uint16_t codes = (uint16_t)(s != 0.0f ? enc2_e4m3(hv[kb].x / s, hv[kb].y / s) : 0u);
+                float s;
+                const uint16_t codes = requant_pair(hv[kb].x, hv[kb].y, amax, s);
                 reinterpret_cast<uint16_t*>(hq[wave][kb])[lane] = codes;
                 sa[kb] = s;
                 if (ntile == 0) {
@@ -294,7 +316,6 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDe
                 }
             }
             wave_lds_fence();
-            const float* wsrow = a.w2s + (int64_t)slot * (a.H / 128) * NKB2 + (n0 / 128) * NKB2;
             v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kb = 0; kb < NKB2; kb++) {
@@ -302,7 +323,7 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDe
                 const v4i ahi = *reinterpret_cast<const v4i*>(&hq[wave][kb][64 + q16]);
                 const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
                 const v4f p = mfma16x16x128_e4m3(frag(alo, ahi), frag(blo[kb], bhi[kb]), z);
-                acc += p * (sa[kb] * wsrow[kb]);
+                acc += p * (sa[kb] * sw[kb]);
             }
             wave_lds_fence();
             val = acc[0];
@@ -346,6 +367,355 @@ int fused_decode_two_launch(hipStream_t st, FusedDecodeArgs a) {
         default: return MOE_ERR_SHAPE;
     }
     return launch_status();
+}
+
+
+// ---------------------------------------------------------------------------
+// One-launch step.  The grid holds both roles: gate/up tiles of 8*M act columns
+// (block ids [0, n_a)) and 8-row down tiles after them.  With tiles that wide
+// every block is resident at once on an idle GPU, so the W2 stream of the down
+// tiles runs beside the W13 stream instead of after a kernel boundary.
+//
+// Hand-off.  Each XCD has its own L2, so h must reach the device-coherent
+// level without a whole-L2 write-back per tile: h is written and read with
+// agent-scope atomic accesses (coherent across XCDs), and the writer waits for
+// its stores to complete before it counts its tile.  The tile that completes a
+// route's count resets the counter to zero and advances the route's publish
+// word (the only write to it in the call).  Every down tile keeps, per route,
+// the publish value it consumed last (a word no other tile touches), waits
+// until the publish word differs from it, then records the new value: no word
+// needs clearing between calls, and the polled words see no atomic traffic.
+// Down tiles have higher block ids than every gate/up tile they wait for, and
+// workgroups are dispatched in block order, so every awaited tile is already
+// running or done and the waits always end.  A wait is still bounded; if one
+// ever gave up, the error word of the control block is set.
+
+constexpr int kSpinLimit = 1 << 16;    // polls before a wait gives up (about 0.1 s)
+constexpr int kCtlLine = kDecodeCtlLineWords;
+
+// Control block (32-bit words): line 0 holds the error word, line 1 + r the
+// tile counter of route r, line 1 + R + r its publish word, and from line
+// 1 + 2R on, densely, the last-seen publish value of every (token, down tile,
+// route) triple.
+__device__ __forceinline__ uint32_t* route_counter(uint32_t* ctl, int64_t r) { return ctl + kCtlLine * (1 + r); }
+__device__ __forceinline__ uint32_t* route_publish(uint32_t* ctl, int64_t R, int64_t r) {
+    return ctl + kCtlLine * (1 + R + r);
+}
+
+__device__ __forceinline__ uint32_t load_coherent(uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    store_coherent(reinterpret_cast<uint32_t*>(p), __float_as_uint(v));
+}
+__device__ __forceinline__ float2 load_coherent2(const float* p) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Polls *p until it differs from `seen` and returns the new value in *now; false if the spin
+// limit ran out first.
+__device__ __forceinline__ bool wait_change(uint32_t* p, uint32_t seen, uint32_t* now) {
+    for (int it = 0; it < kSpinLimit; it++) {
+        const uint32_t v = (uint32_t)__builtin_amdgcn_readfirstlane((int)load_coherent(p));
+        if (v != seen) {
+            *now = v;
+            return true;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return false;
+}
+
+// Gate/up tile b of the one-launch step: route r, act columns [c0, c0 + 8M).
+// Column group g is one MFMA: columns 0..7 are gate rows c0+8g.., columns 8..15
+// the matching up rows I+c0+8g..  Each wave owns K blocks [kb0, kb1) of all M
+// groups and shares one quantized token-row operand between them.
+template <int M>
+__device__ __forceinline__ void gateup_tile_m(const FusedDecodeArgs& a, int b) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int64_t r = b / a.tiles_a;
+    const int64_t c0 = (int64_t)(b % a.tiles_a) * 8 * M;
+    const int64_t N = 2 * (int64_t)a.I;
+    const int slot = a.slots[r];
+    __shared__ float red[kFdWaves][M][kFdTile];
+    __shared__ __attribute__((aligned(16))) uint8_t xq[kFdWaves][kFdUnroll][128];
+    const int col = lane & 15;
+    if (slot < 0) {
+        if (threadIdx.x < kFdTile * M) {
+            const int g = threadIdx.x / kFdTile, c = threadIdx.x % kFdTile;
+            const int64_t rr = c < 8 ? c0 + 8 * g + c : a.I + c0 + 8 * g + (c - 8);
+            a.c1[r * N + rr] = 0.0f;
+            if (c < 8) a.h[r * a.I + c0 + 8 * g + c] = 0.0f;
+        }
+        return;
+    }
+    const int nkb = a.H / 128;
+    const int kb0 = wave * nkb / kFdWaves, kb1 = (wave + 1) * nkb / kFdWaves;
+    const int q16 = (lane / 16) * 16;
+    const uint8_t* wrow[M];
+    const float* wsrow[M];
+#pragma unroll
+    for (int g = 0; g < M; g++) {
+        const int64_t wr = col < 8 ? c0 + 8 * g + col : a.I + c0 + 8 * g + (col - 8);
+        wrow[g] = a.w13 + (int64_t)slot * N * a.H + wr * a.H + q16;
+        wsrow[g] = a.w13s + (int64_t)slot * (N / 128) * nkb + (wr / 128) * nkb;
+    }
+    const uint16_t* xrow = a.x + (r / a.topk) * a.H;
+    v4f acc[M];
+#pragma unroll
+    for (int g = 0; g < M; g++) acc[g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kb = kb0; kb < kb1; kb += kFdUnroll) {
+        v4i blo[M][kFdUnroll], bhi[M][kFdUnroll], alo[kFdUnroll], ahi[kFdUnroll];
+        float sa[kFdUnroll], sw[M][kFdUnroll];
+        uint32_t pair[kFdUnroll];
+        // token row first: its quantization then overlaps the weight stream (loads retire in order)
+#pragma unroll
+        for (int u = 0; u < kFdUnroll; u++)
+            if (kb + u < kb1) pair[u] = reinterpret_cast<const uint32_t*>(xrow + (int64_t)(kb + u) * 128)[lane];
+#pragma unroll
+        for (int g = 0; g < M; g++)
+#pragma unroll
+            for (int u = 0; u < kFdUnroll; u++) {
+                if (kb + u < kb1) {
+                    const uint8_t* wp = wrow[g] + (int64_t)(kb + u) * 128;
+                    blo[g][u] = *reinterpret_cast<const v4i*>(wp);
+                    bhi[g][u] = *reinterpret_cast<const v4i*>(wp + 64);
+                    sw[g][u] = wsrow[g][kb + u];
+                }
+            }
+#pragma unroll
+        for (int u = 0; u < kFdUnroll; u++) {
+            if (kb + u < kb1) {
+                const float v0 = bf16_to_f32((uint16_t)(pair[u] & 0xFFFF));
+                const float v1 = bf16_to_f32((uint16_t)(pair[u] >> 16));
+                const float amax = wave_max(__builtin_fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1)));
+                const float s = amax / 448.0f;
+                reinterpret_cast<uint16_t*>(xq[wave][u])[lane] = (uint16_t)(s != 0.0f ? enc2_e4m3(v0 / s, v1 / s) : 0u);
+                sa[u] = s;
+            }
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int u = 0; u < kFdUnroll; u++) {
+            if (kb + u < kb1) {
+                alo[u] = *reinterpret_cast<const v4i*>(&xq[wave][u][q16]);
+                ahi[u] = *reinterpret_cast<const v4i*>(&xq[wave][u][64 + q16]);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < M; g++)
+#pragma unroll
+            for (int u = 0; u < kFdUnroll; u++) {
+                if (kb + u < kb1) {
+                    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const v4f p = mfma16x16x128_e4m3(frag(alo[u], ahi[u]), frag(blo[g][u], bhi[g][u]), z);
+                    acc[g] += p * (sa[u] * sw[g][u]);
+                }
+            }
+        wave_lds_fence();
+    }
+#pragma unroll
+    for (int g = 0; g < M; g++)
+        if (lane < kFdTile) red[wave][g][lane] = acc[g][0];
+    __syncthreads();
+    if (threadIdx.x < kFdTile * M) {
+        const int g = threadIdx.x / kFdTile, c = threadIdx.x % kFdTile;
+        float t = red[0][g][c];
+#pragma unroll
+        for (int w = 1; w < kFdWaves; w++) t += red[w][g][c];
+        const float up = __shfl_down(t, 8, kFdTile);            // lanes c < 8 get their up value
+        if (c < 8) store_coherent(&a.h[r * a.I + c0 + 8 * g + c], (t / (1.0f + expf(-t))) * up);
+        // h of this tile is complete at the device-coherent level before the count moves
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (threadIdx.x == 0) {
+            uint32_t* cnt = route_counter(a.ctl, r);
+            const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (done == (uint32_t)a.tiles_a - 1) {
+                // last tile of the route: every other tile's h was complete before its count
+                store_coherent(cnt, 0u);
+                uint32_t* pub = route_publish(a.ctl, (int64_t)a.T * a.topk, r);
+                store_coherent(pub, load_coherent(pub) + 1u);
+            }
+        }
+        const int64_t rr = c < 8 ? c0 + 8 * g + c : a.I + c0 + 8 * g + (c - 8);
+        a.c1[r * N + rr] = t;
+    }
+}
+
+// Down tile b of the one-launch step: as decode_down8_kernel, but the W2
+// fragments are requested before the route's h is ready, and h is read
+// coherently once the route's publish word has moved.
+template <int NKB2>
+__device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
+    constexpr int NS = (NKB2 + 1) / 2;
+    constexpr bool kOdd = (NKB2 & 1) != 0;
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int64_t t = b / a.tiles_c;
+    const int ntile = b % a.tiles_c;
+    const int64_t n0 = (int64_t)ntile * kDnRows;
+    const int col = lane & 15, q16 = (lane / 16) * 16;
+    const int strm = col >> 3;
+    const int64_t R = (int64_t)a.T * a.topk;
+    uint32_t* last_seen = a.ctl + kCtlLine * (1 + 2 * R) + ((int64_t)t * a.tiles_c + ntile) * a.topk;
+    __shared__ float part[64][kDnRows];
+    __shared__ int on[64];
+    __shared__ __attribute__((aligned(16))) uint8_t hq[kFdWaves][NKB2][128];
+    bool timed_out = false;
+    for (int j = wave; j < a.topk; j += kFdWaves) {
+        const int64_t r = t * a.topk + j;
+        const int slot = a.slots[r];
+        float val = 0.0f, wgt = 0.0f;
+        if (slot >= 0) {
+            // the W2 fragments go out first, behind nothing but the slot id
+            const uint8_t* wrow = a.w2 + (int64_t)slot * a.H * a.I + (n0 + (col & 7)) * a.I + q16;
+            v4i blo[NS], bhi[NS];
+#pragma unroll
+            for (int i = 0; i < NS; i++) {
+                const int kb = strm * NS + i < NKB2 ? strm * NS + i : NKB2 - 1;
+                blo[i] = *reinterpret_cast<const v4i*>(wrow + kb * 128);
+                bhi[i] = *reinterpret_cast<const v4i*>(wrow + kb * 128 + 64);
+            }
+            const uint32_t seen = load_coherent(last_seen + j);
+            wgt = a.weights[r];
+            // the tile's W2 block scales travel with its fragments
+            const float* wsrow = a.w2s + (int64_t)slot * (a.H / 128) * NKB2 + (n0 / 128) * NKB2;
+            float sw[NKB2];
+#pragma unroll
+            for (int kb = 0; kb < NKB2; kb++) sw[kb] = wsrow[kb];
+            uint32_t now = seen;
+            if (!wait_change(route_publish(a.ctl, R, r), seen, &now)) timed_out = true;
+            asm volatile("" ::: "memory");
+            const float* hrow = a.h + r * a.I + 2 * lane;
+            float2 hv[NKB2];
+#pragma unroll
+            for (int kb = 0; kb < NKB2; kb++) hv[kb] = load_coherent2(hrow + kb * 128);
+            // stores wait until every load of the route is consumed: loads and stores retire in
+            // order, so an earlier store would hold up the waits below
+            float sa[NKB2];
+            uint16_t codes[NKB2];
+#pragma unroll
+            for (int kb = 0; kb < NKB2; kb++) {
+                const float amax = wave_max(__builtin_fmaxf(__builtin_fabsf(hv[kb].x), __builtin_fabsf(hv[kb].y)));
+                float s;
+                codes[kb] = requant_pair(hv[kb].x, hv[kb].y, amax, s);
+                reinterpret_cast<uint16_t*>(hq[wave][kb])[lane] = codes[kb];
+                sa[kb] = s;
+            }
+            wave_lds_fence();
+            const int m = lane & 15;
+            const v4i zero4 = {0, 0, 0, 0};
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NS; i++) {
+                const bool has1 = !(kOdd && i == NS - 1);
+                const int kbA = (m == 1 && has1) ? NS + i : i;
+                v4i alo = *reinterpret_cast<const v4i*>(&hq[wave][kbA][q16]);
+                v4i ahi = *reinterpret_cast<const v4i*>(&hq[wave][kbA][64 + q16]);
+                const bool a_on = m == 0 || (m == 1 && has1);
+                alo = a_on ? alo : zero4;
+                ahi = a_on ? ahi : zero4;
+                const bool b_on = strm == 0 || has1;
+                const v4i bl = b_on ? blo[i] : zero4, bh = b_on ? bhi[i] : zero4;
+                const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+                const v4f p = mfma16x16x128_e4m3(frag(alo, ahi), frag(bl, bh), z);
+                const float f0 = sa[i] * sw[i];
+                const float f1 = has1 ? sa[(NS + i) % NKB2] * sw[(NS + i) % NKB2] : 0.0f;
+                acc += strm == 0 ? p[0] * f0 : p[1] * f1;
+            }
+            wave_lds_fence();
+            val = acc + __shfl_down(acc, 8, 16);
+            // the next call's wait on this route starts from the value consumed here; a kernel
+            // boundary lies between, so a plain store is visible to it
+            if (lane == 0 && !timed_out) last_seen[j] = now;
+            if (ntile == 0) {
+#pragma unroll
+                for (int kb = 0; kb < NKB2; kb++) {
+                    reinterpret_cast<uint16_t*>(a.aq + r * a.I)[kb * 64 + lane] = codes[kb];
+                    if (lane == 0) a.as[r * NKB2 + kb] = sa[kb];
+                }
+            }
+        } else if (ntile == 0) {
+            for (int i = lane; i < a.I / 4; i += kWave) reinterpret_cast<uint32_t*>(a.aq + r * a.I)[i] = 0u;
+            if (lane < NKB2) a.as[r * NKB2 + lane] = 0.0f;
+        }
+        if (lane < kDnRows) {
+            part[j][lane] = wgt * val;
+            a.c2[r * a.H + n0 + lane] = val;
+        }
+        if (lane == 0) on[j] = slot >= 0;
+    }
+    if (timed_out && lane == 0) store_coherent(a.ctl, 1u);
+    __syncthreads();
+    if (threadIdx.x < kDnRows) {
+        float o = 0.0f;
+        for (int j = 0; j < a.topk; j++)
+            if (on[j]) o += part[j][threadIdx.x];
+        a.out[t * a.H + n0 + threadIdx.x] = f32_to_bf16(o);
+    }
+}
+
+template <int NKB2, int M>
+__global__ void __launch_bounds__(kWave * kFdWaves) decode_step_kernel(FusedDecodeArgs a) {
+    if ((int)blockIdx.x < a.n_a) gateup_tile_m<M>(a, (int)blockIdx.x);
+    else down8_tile<NKB2>(a, (int)blockIdx.x - a.n_a);
+}
+
+// Workgroups of decode_step_kernel<NKB2, M> that fit on the current device at once (0 if unknown).
+template <int NKB2, int M>
+int step_resident_blocks() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<NKB2, M>, kWave * kFdWaves, 0) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
+    }
+    return cached[dev] > 0 ? cached[dev] : 0;
+}
+
+// Launches the one-launch step if its blocks all fit on the device at once; returns 1 if it did not
+// launch (the caller then runs the two-launch step), else a status.
+template <int NKB2, int M>
+int try_step(hipStream_t st, FusedDecodeArgs a) {
+    a.tiles_a = a.I / (8 * M);
+    a.n_a = a.T * a.topk * a.tiles_a;
+    a.tiles_c = a.H / kDnRows;
+    const int64_t blocks = (int64_t)a.n_a + (int64_t)a.T * a.tiles_c;
+    if (blocks > step_resident_blocks<NKB2, M>()) return 1;
+    hipLaunchKernelGGL((decode_step_kernel<NKB2, M>), dim3((unsigned)blocks), dim3(kWave * kFdWaves), 0, st, a);
+    return launch_status();
+}
+
+template <int NKB2>
+int try_step_m(hipStream_t st, const FusedDecodeArgs& a) {
+    const int groups = a.I / 8;
+    if (groups % 3 == 0) return try_step<NKB2, 3>(st, a);
+    if (groups % 2 == 0) return try_step<NKB2, 2>(st, a);
+    return 1;
+}
+
+int fused_decode_one_launch(hipStream_t st, FusedDecodeArgs a) {
+    if (!a.ctl || !decode_one_launch_ok(a.T, a.H, a.I, a.topk)) return 1;
+    switch (a.I / 128) {
+        case 1: return try_step_m<1>(st, a);
+        case 2: return try_step_m<2>(st, a);
+        case 3: return try_step_m<3>(st, a);
+        case 4: return try_step_m<4>(st, a);
+        case 5: return try_step_m<5>(st, a);
+        case 6: return try_step_m<6>(st, a);
+        case 7: return try_step_m<7>(st, a);
+        case 8: return try_step_m<8>(st, a);
+        default: return 1;
+    }
 }
 
 }  // namespace moe

@@ -61,8 +61,9 @@ def check_against_oracle(dd: DevDecode, ref, im, host_weights=None):
     for name, arr in (("c1", c1), ("h", hh), ("c2", c2), ("as", as_)):
         assert np.all(arr[inactive].view(np.uint32) == 0), name + ": inactive rows must be +0.0"
     assert np.all(aq[inactive] == 0)
-    ctl = dd.ws[dd.lay["ctl"]:dd.lay["total"]].cpu().numpy()
-    assert np.all(ctl == 0), "control words must be clear after a call (and no wait timed out)"
+    ctl = dd.ws[dd.lay["ctl"]:dd.lay["total"]].view(torch.int32).cpu().numpy()
+    assert ctl[0] == 0, "a hand-off wait gave up"
+    assert np.all(ctl[32:32 * (1 + R):32] == 0), "route tile counters must be back at zero after a call"
     if (~inactive).any():
         hw = host_weights or [t.cpu().numpy() for t in (c.w13_q, c.w13_s)]
         bound = gemm_abs_bound(im["xq"], im["xs"], hw[0], hw[1], c.slot_ids.reshape(-1), np.arange(R) // c.topk)
