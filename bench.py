@@ -303,8 +303,8 @@ def main():
             extra["prefill"] = prefill_bench(torch, m, wl, 4096, 256, 6, 4096, 1024, 10)
     tr = measured_traffic()
     roof = dict(bound="hbm",
-                kernel="moe_fused_decode step = decode_gateup_kernel + decode_down16_kernel (H=2048, I=768, "
-                       "8/8 active); one launch = one step",
+                kernel="moe_fused_decode step = one decode_step_kernel launch (gate/up and down tiles in one "
+                       "grid; H=2048, I=768, 8/8 active)",
                 bytes_per_launch=head["bytes_streamed"], us_per_launch=head["us_per_step_mean"],
                 achieved=head["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s", frac=head["hbm_frac"],
                 traffic=tr["traffic_bytes_per_step"] if tr else None)
