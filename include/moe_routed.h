@@ -148,7 +148,9 @@ int moe_pick_block_m(int64_t routes, int64_t experts);
  *        writes a +0 output row and reads no A, W or scales of that row.
  *        Meant for decode-sized row counts (every row streams its expert).
  *   Requirements: K % 128 == 0, N % 16 == 0; w_q, a_q and their strides
- *   16-byte aligned (MOE_ERR_ALIGN otherwise).  n_experts == 0 with NULL
+ *   16-byte aligned (MOE_ERR_ALIGN otherwise).  Grouped mode also needs
+ *   N % 128 == 0, 1 <= n_experts <= 1024 and K <= 8192 (a tile keeps all its
+ *   K-block scales in LDS); MOE_ERR_SHAPE otherwise.  n_experts == 0 with NULL
  *   w_q/w_s is allowed in slot mode (an empty bank: every slot must be < 0).
  */
 int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,

@@ -93,6 +93,10 @@ def test_gemm_argument_checks():
     assert gemm(mode=0, N=144) == m.MOE_ERR_SHAPE  # grouped mode needs N % 128
     assert gemm(mode=0, block_m=48) == m.MOE_ERR_SHAPE
     assert gemm(mode=0, n_experts=0, w_q=None, w_s=None) == m.MOE_ERR_SHAPE
+    big_k = dict(K=8320, a_stride=8320, a_s_stride=65, w_stride_n=8320, w_stride_e=8320 * 256, w_s_stride_n=65,
+                 w_s_stride_e=2 * 65)
+    assert gemm(mode=0, **big_k) == m.MOE_ERR_SHAPE          # grouped mode keeps K/128 <= 64 scales per tile
+    assert gemm(mode=0, n_experts=1025, **big_k) == m.MOE_ERR_SHAPE
 
 
 def test_gather_act_reduce_argument_checks():
