@@ -381,7 +381,8 @@ int fused_decode_two_launch(hipStream_t st, FusedDecodeArgs a) {
 // agent-scope atomic accesses (coherent across XCDs), and the writer waits for
 // its stores to complete before it counts its tile.  The tile that completes a
 // route's count resets the counter to zero and advances the route's publish
-// word (the only write to it in the call).  Every down tile keeps, per route,
+// word (the only update of it in the call, so the poll on it sees no atomic
+// contention).  Every down tile keeps, per route,
 // the publish value it consumed last (a word no other tile touches), waits
 // until the publish word differs from it, then records the new value: no word
 // needs clearing between calls, and the polled words see no atomic traffic.
@@ -537,9 +538,10 @@ __device__ __forceinline__ void gateup_tile_m(const FusedDecodeArgs& a, int b) {
             const uint32_t done = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (done == (uint32_t)a.tiles_a - 1) {
                 // last tile of the route: every other tile's h was complete before its count
+                // (an add without return: advancing the publish word costs no round trip)
                 store_coherent(cnt, 0u);
-                uint32_t* pub = route_publish(a.ctl, (int64_t)a.T * a.topk, r);
-                store_coherent(pub, load_coherent(pub) + 1u);
+                __hip_atomic_fetch_add(route_publish(a.ctl, (int64_t)a.T * a.topk, r), 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         const int64_t rr = c < 8 ? c0 + 8 * g + c : a.I + c0 + 8 * g + (c - 8);
