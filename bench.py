@@ -11,9 +11,10 @@ the stream bracket each graph replay; a step is replay time / 16.  Inputs
 are resident in HBM before the timed region.
 
 Also reported: 4/2/0 active routes and H=4096, I=1024 (time vs active
-routes), the fused gather (k=7168; 8, 512, 8192 rows) timed the same way, the
-grouped prefill GEMMs at 24576 routes (E=256, top-6, H=4096, I=1024) in
-TFLOP/s against the fp8 dense peak and against the HBM roofline, the
+routes), the fused gather (k=7168 with 8, 64, 512 and 8192 rows; k=896 with
+512 rows) timed the same way, the grouped prefill GEMMs at 1536, 6144 and
+24576 routes (E=256, top-6, H=4096, I=1024) in TFLOP/s against the fp8 dense
+peak and against the HBM roofline, the
 roofline of the dominant kernel (the single fused decode kernel), and the
 CPU oracle timed on a bounded sample of the headline workload.
 
@@ -202,13 +203,19 @@ def gather_bench(torch, m, wl, k, tokens, topk, reps):
                 gbs=nbytes / (us * 1e-6) / 1e9, hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
 
-def prefill_bench(torch, m, wl, T, E, topk, H, I, steps):
+def prefill_weights(torch, wl, E, H, I):
+    dev = torch.device("cuda")
+    w13 = wl.block_fp8_weights(E, 2 * I, H, 21, device=dev, chunk_experts=32)
+    w2 = wl.block_fp8_weights(E, H, I, 22, device=dev, chunk_experts=32)
+    return w13, w2
+
+
+def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     dev = torch.device("cuda")
     rt = wl.prefill_routes(T, E, topk, seed=9)
     R = T * topk
     offs = torch.from_numpy(rt.expert_offsets).to(dev)
-    w13_q, w13_s = wl.block_fp8_weights(E, 2 * I, H, 21, device=dev, chunk_experts=32)
-    w2_q, w2_s = wl.block_fp8_weights(E, H, I, 22, device=dev, chunk_experts=32)
+    (w13_q, w13_s), (w2_q, w2_s) = weights
     a1_q, a1_s = wl.fp8_rows(R, H, seed=23, device=dev)
     a2_q, a2_s = wl.fp8_rows(R, I, seed=24, device=dev)
     c1 = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev)
@@ -235,7 +242,6 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps):
         out[name] = dict(us_median=us, tflops=tflops, fp8_peak_frac=tflops / FP8_PEAK_TFLOPS,
                          roofline_frac=tflops / attainable, arithmetic_intensity=ai, bytes=nbytes,
                          hbm_gbs=nbytes / (us * 1e-6) / 1e9)
-    del w13_q, w2_q
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
 
 
@@ -297,10 +303,18 @@ def main():
         del pools
         torch.cuda.empty_cache()
         log("gather")
-        extra["gather"] = [gather_bench(torch, m, wl, 7168, t, 8, 20) for t in (1, 64, 1024)]
+        extra["gather"] = [gather_bench(torch, m, wl, 7168, t, 8, 20) for t in (1, 8, 64, 1024)]
+        extra["gather"].append(gather_bench(torch, m, wl, 896, 64, 8, 20))
         if not args.skip_prefill:
-            log("prefill 24576 routes")
-            extra["prefill"] = prefill_bench(torch, m, wl, 4096, 256, 6, 4096, 1024, 10)
+            weights = prefill_weights(torch, wl, 256, 4096, 1024)
+            extra["prefill_densities"] = []
+            for T in (256, 1024, 4096):
+                log("prefill %d routes" % (T * 6))
+                r = prefill_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights)
+                extra["prefill_densities"].append(r)
+                if T == 4096:
+                    extra["prefill"] = r
+            del weights
     tr = measured_traffic()
     roof = dict(bound="hbm",
                 kernel="moe_fused_decode step = one decode_step_kernel launch (gate/up and down tiles in one "
