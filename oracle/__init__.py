@@ -59,6 +59,7 @@ def lib():
                                      I32, P, P, I64, I64, P, I32, I64]
         L.orc_silu_mul_quant.argtypes = [P, I32, I64, I64, I64, P, I64, P, I64]
         L.orc_topk_reduce.argtypes = [P, I32, I64, P, P, P, I64, I64, I64, P, I64]
+        L.orc_route_prep.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P]
         L.orc_fused_decode.argtypes = [P, I64, I64, I64, I64, P, P, I64, P, P, P, P, P,
                                        P, P, P, P, P, P]
         for name in ("orc_quant_groups", "orc_gather_rows_scales", "orc_block_gemm",
@@ -246,3 +247,20 @@ def fused_decode(x_bf16, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, intermedia
                                   _p(w13_q), _p(w13_s), _p(w2_q), _p(w2_s), _p(out),
                                   g("xq"), g("xs"), g("c1"), g("aq"), g("as_"), g("c2")))
     return (out, im) if intermediates else out
+
+
+def route_prep(logits: np.ndarray, topk: int):
+    """O7: top-k routing and the (expert, token)-ordered route maps.
+    Returns dict with expert_ids [T,topk] int32, weights [T,topk] f32, dst2src [T*topk], route_rows [T*topk],
+    expert_offsets [E+1] (all int32)."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.zeros((T, topk), np.int32)
+    w = np.zeros((T, topk), np.float32)
+    d2s = np.zeros(T * topk, np.int32)
+    rr = np.zeros(T * topk, np.int32)
+    offs = np.zeros(E + 1, np.int32)
+    rc = lib().orc_route_prep(_p(logits), E, T, E, topk, _p(ids), _p(w), _p(d2s), _p(rr), _p(offs))
+    if rc:
+        raise ValueError("orc_route_prep: bad arguments")
+    return dict(expert_ids=ids, weights=w, dst2src=d2s, route_rows=rr, expert_offsets=offs)

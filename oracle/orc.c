@@ -363,3 +363,56 @@ int orc_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, in
     if (own_c2) free(c2);
     return rc;
 }
+
+/* O7: routing prep.  Selection repeats "take the largest remaining logit" topk times (strictly larger
+ * wins, so equal logits go to the lower index); the weights follow the definition: softmax over all
+ * E experts in double, then division by the selected probabilities' sum.  The counting sort walks
+ * experts in ascending order and, for each, tokens in ascending order. */
+int orc_route_prep(const float* logits, int64_t logits_stride, int64_t T, int64_t E, int64_t topk,
+                   int32_t* expert_ids, float* weights, int32_t* dst2src, int32_t* route_rows,
+                   int32_t* expert_offsets) {
+    int64_t t, e, j, row;
+    double* p;
+    unsigned char* taken;
+    if (T < 0 || E <= 0 || topk < 1 || topk > E || logits_stride < E) return -2;
+    p = (double*)malloc((size_t)E * sizeof(double));
+    taken = (unsigned char*)malloc((size_t)E);
+    for (t = 0; t < T; t++) {
+        const float* l = logits + t * logits_stride;
+        double mx = l[0], sum = 0.0, sel = 0.0;
+        for (e = 1; e < E; e++)
+            if (l[e] > mx) mx = l[e];
+        for (e = 0; e < E; e++) {
+            p[e] = exp((double)l[e] - mx);
+            sum += p[e];
+        }
+        for (e = 0; e < E; e++) {
+            p[e] /= sum;
+            taken[e] = 0;
+        }
+        for (j = 0; j < topk; j++) {
+            int64_t best = -1;
+            for (e = 0; e < E; e++)
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+            taken[best] = 1;
+            expert_ids[t * topk + j] = (int32_t)best;
+            sel += p[best];
+        }
+        for (j = 0; j < topk; j++) weights[t * topk + j] = (float)(p[expert_ids[t * topk + j]] / sel);
+    }
+    row = 0;
+    for (e = 0; e < E; e++) {
+        expert_offsets[e] = (int32_t)row;
+        for (t = 0; t < T; t++)
+            for (j = 0; j < topk; j++)
+                if (expert_ids[t * topk + j] == e) {
+                    dst2src[row] = (int32_t)t;
+                    route_rows[t * topk + j] = (int32_t)row;
+                    row++;
+                }
+    }
+    expert_offsets[E] = (int32_t)row;
+    free(p);
+    free(taken);
+    return 0;
+}

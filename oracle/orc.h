@@ -108,6 +108,22 @@ int orc_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, in
                      uint16_t* out_bf16,
                      uint8_t* xq, float* xs, float* c1, uint8_t* aq, float* as, float* c2);
 
+/* ---- O7: routing prep of a prefill step ----
+ * Where the dst2src map of the gather comes from ("[MoE] Gather the cutlass MoE activation and its
+ * scales in one launch", Motivation: the activation is replicated once per routed expert through a
+ * map of m * topk entries) and the expert-grouped row order of the grouped GEMM ("perf(dsfp4): pick
+ * the grouped-prefill tile from route density on sm_89", Measurements: routes per expert).
+ * logits: T x E fp32 (row stride logits_stride).  For each token, the topk experts with the largest
+ * logits, in descending order (ties: lower expert index; logits must be finite); their weights are
+ * the softmax over all E experts renormalized over the top-k, computed here in double from the
+ * definition (softmax first, then renormalization) and rounded to fp32.
+ * Routes are then listed in (expert, token) order: row r of that list is route (dst2src[r], j) with
+ * ids[dst2src[r]][j] the row's expert; route_rows[t*topk + j] is the row of route (t, j), and
+ * expert_offsets[e] the first row of expert e (expert_offsets[E] = T*topk). */
+int orc_route_prep(const float* logits, int64_t logits_stride, int64_t T, int64_t E, int64_t topk,
+                   int32_t* expert_ids, float* weights, int32_t* dst2src, int32_t* route_rows,
+                   int32_t* expert_offsets);
+
 #ifdef __cplusplus
 }
 #endif

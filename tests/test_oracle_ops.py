@@ -347,3 +347,72 @@ def test_fused_decode_tiny_config(orc):
     out_only = orc.fused_decode(args[0], only, args[2], *args[3:])
     assert np.array_equal(out, out_only)
     assert np.all(im["c1"][1 - j] == 0) and np.abs(im["c1"][j]).max() > 0
+
+
+# ---- O7: routing prep -------------------------------------------------------------------------
+
+def _routing_logits(T, E, seed):
+    return np.random.default_rng(seed).standard_normal((T, E)).astype(np.float32)
+
+
+@pytest.mark.parametrize("T,E,topk", [(1, 8, 2), (37, 16, 4), (300, 256, 6), (64, 64, 64), (5, 1, 1)])
+def test_route_prep_selection_and_maps_vs_numpy_sort(orc, T, E, topk):
+    """Top-k equals numpy's stable argsort of -logits (ties to the lower index); the route maps equal a
+    stable numpy sort of the (expert, token) keys, and the offsets a bincount prefix sum."""
+    lg = _routing_logits(T, E, seed=T * 7 + E)
+    r = orc.route_prep(lg, topk)
+    want_ids = np.argsort(-lg, axis=1, kind="stable")[:, :topk].astype(np.int32)
+    assert np.array_equal(r["expert_ids"], want_ids)
+    keys = (want_ids.astype(np.int64) * T + np.arange(T)[:, None]).ravel()
+    order = np.argsort(keys, kind="stable")
+    assert np.array_equal(r["dst2src"], (order // topk).astype(np.int32))
+    inv = np.empty_like(order)
+    inv[order] = np.arange(order.size)
+    assert np.array_equal(r["route_rows"], inv.astype(np.int32))
+    offs = np.concatenate([[0], np.cumsum(np.bincount(want_ids.ravel(), minlength=E))]).astype(np.int32)
+    assert np.array_equal(r["expert_offsets"], offs)
+
+
+def test_route_prep_weights_vs_scipy_softmax_and_closed_form(orc):
+    from scipy.special import softmax
+    lg = _routing_logits(200, 64, seed=5)
+    r = orc.route_prep(lg, 6)
+    p = softmax(lg.astype(np.float64), axis=1)
+    sel = np.take_along_axis(p, r["expert_ids"].astype(np.int64), axis=1)
+    want = sel / sel.sum(axis=1, keepdims=True)
+    assert np.allclose(r["weights"], want, rtol=2e-7, atol=0)
+    # closed form: the ratio of two routes' weights is exp of their logit difference; weights sum to 1
+    l_sel = np.take_along_axis(lg.astype(np.float64), r["expert_ids"].astype(np.int64), axis=1)
+    ratio = r["weights"][:, 1:].astype(np.float64) / r["weights"][:, :1]
+    assert np.allclose(ratio, np.exp(l_sel[:, 1:] - l_sel[:, :1]), rtol=1e-6)
+    assert np.allclose(r["weights"].sum(axis=1, dtype=np.float64), 1.0, rtol=1e-6)
+
+
+def test_route_prep_ties_all_experts_and_empty(orc):
+    # all-equal logits: experts 0..topk-1, each weight exactly 1/topk
+    r = orc.route_prep(np.zeros((3, 10), np.float32), 4)
+    assert np.array_equal(r["expert_ids"], np.tile(np.arange(4, dtype=np.int32), (3, 1)))
+    assert np.all(r["weights"] == np.float32(0.25))
+    # +0 and -0 tie as well: the lower index wins
+    lg = np.array([[-0.0, 0.0, -1.0]], np.float32)
+    assert r is not None and orc.route_prep(lg, 2)["expert_ids"].tolist() == [[0, 1]]
+    # topk == E: every expert, weights = plain softmax
+    lg = _routing_logits(4, 5, seed=1)
+    r = orc.route_prep(lg, 5)
+    assert np.array_equal(np.sort(r["expert_ids"], axis=1), np.tile(np.arange(5), (4, 1)))
+    # no tokens: empty maps, all offsets zero
+    r = orc.route_prep(np.zeros((0, 8), np.float32), 2)
+    assert r["dst2src"].size == 0 and np.all(r["expert_offsets"] == 0)
+
+
+def test_route_prep_matches_the_workload_generator(orc):
+    """workloads.routing draws N(0,1) logits with torch in float64 and routes them in numpy (softmax,
+    stable top-k, renormalization); the oracle on the same logits in fp32 picks the same experts and
+    weights within fp32 rounding."""
+    import torch
+    T, E, topk, seed = 256, 64, 6, 11
+    ids, w = wl.routing(T, E, topk, seed)
+    lg = torch.randn((T, E), generator=wl._gen(seed), dtype=torch.float64).numpy()
+    r = orc.route_prep(lg.astype(np.float32), topk)
+    assert np.array_equal(r["expert_ids"], ids)
+    assert np.allclose(r["weights"], w, rtol=1e-6, atol=0)
