@@ -245,6 +245,46 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
 
 
+def route_prep_bench(torch, m, wl, T, E, topk, reps):
+    """Device routing prep (top-k, weights, route maps) on skewed router logits: 16 calls over 16
+    logit sets in one graph, so the time is the device's, not the host's launch latency."""
+    dev = torch.device("cuda")
+    size = m.lib().moe_route_prep_workspace_size(T, E)
+    sets = []
+    for i in range(LAYERS):
+        sets.append(dict(lg=torch.from_numpy(wl.router_logits(T, E, seed=41 + i, skew=1.0)).to(dev),
+                         ids=torch.empty((T, topk), dtype=torch.int32, device=dev),
+                         w=torch.empty((T, topk), dtype=torch.float32, device=dev),
+                         d2s=torch.empty(T * topk, dtype=torch.int32, device=dev),
+                         rr=torch.empty(T * topk, dtype=torch.int32, device=dev),
+                         offs=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                         ws=torch.empty(size, dtype=torch.uint8, device=dev)))
+
+    def run_all():
+        st = torch.cuda.current_stream().cuda_stream
+        for b in sets:
+            rc = m.lib().moe_route_prep(b["lg"].data_ptr(), E, T, E, topk, b["ids"].data_ptr(), b["w"].data_ptr(),
+                                        b["d2s"].data_ptr(), b["rr"].data_ptr(), b["offs"].data_ptr(),
+                                        b["ws"].data_ptr(), size, st)
+            assert rc == 0, rc
+
+    run_all()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=torch.cuda.Stream()):
+        run_all()
+    for _ in range(3):
+        gr.replay()
+    t = Timer(torch)
+    for _ in range(reps):
+        t.start()
+        gr.replay()
+        t.stop()
+    us = statistics.median(t.us()) / LAYERS
+    nbytes = T * E * 4 + T * topk * (4 + 4 + 4 + 4) + T * topk * 4
+    return dict(tokens=T, experts=E, topk=topk, us_per_call=us, bytes=nbytes, gbs=nbytes / (us * 1e-6) / 1e9)
+
+
 def cpu_baseline(wl, budget_s=12.0):
     """The CPU oracle on the headline workload, one thread, repeated for about budget_s seconds."""
     import numpy as np
@@ -305,6 +345,8 @@ def main():
         log("gather")
         extra["gather"] = [gather_bench(torch, m, wl, 7168, t, 8, 20) for t in (1, 8, 64, 1024)]
         extra["gather"].append(gather_bench(torch, m, wl, 896, 64, 8, 20))
+        log("route prep")
+        extra["route_prep"] = [route_prep_bench(torch, m, wl, T, 256, 6, 20) for T in (256, 4096)]
         if not args.skip_prefill:
             weights = prefill_weights(torch, wl, 256, 4096, 1024)
             extra["prefill_densities"] = []

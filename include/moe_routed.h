@@ -204,6 +204,36 @@ int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes, int64_t T,
                                     int64_t topk, void* stream);
 
 /*
+ * moe_route_prep  -- routing prep of a prefill step  [gather] [tile]
+ *   The step before the gather: the dst2src map that replicates each token's
+ *   activation once per routed expert, and the expert-grouped row order of the
+ *   grouped GEMM.
+ *   logits   DEVICE fp32 [T][logits_stride] (E used), finite.  A NaN logit
+ *   ranks as -inf so every selected id is a valid expert, but the weights of
+ *   such a token are then unspecified.
+ *   For each token: the topk experts with the largest logits in descending order
+ *   (ties: lower expert index), and weights w_j = exp(l_j - l_max) /
+ *   sum_{i in top-k} exp(l_i - l_max), i.e. the softmax over all E experts
+ *   renormalized over the top-k.
+ *   expert_ids [T][topk] int32, weights [T][topk] fp32.
+ *   Route maps in (expert, token) order: dst2src [T*topk] int32 (token of each
+ *   sorted row), route_rows [T*topk] int32 (row of route t*topk+j, the
+ *   route_rows argument of moe_topk_reduce), expert_offsets [E+1] int32 (rows
+ *   of expert e are [offsets[e], offsets[e+1]), the grouped GEMM's offsets).
+ *   workspace: moe_route_prep_workspace_size(T, E) bytes of DEVICE memory,
+ *   16-byte aligned; no initialization needed; scratch between the three
+ *   launches of one call, so overlapping calls need their own workspaces.
+ *   Deterministic (integer counting only).
+ *   Requirements: 1 <= E <= 1024, 1 <= topk <= min(E, 64), T * topk < 2^31.
+ *   T == 0 launches one small kernel that writes E + 1 zero offsets (the one
+ *   exception to "no work, no launch").
+ */
+size_t moe_route_prep_workspace_size(int64_t T, int64_t E);
+int moe_route_prep(const float* logits, int64_t logits_stride, int64_t T, int64_t E, int64_t topk,
+                   int32_t* expert_ids, float* weights, int32_t* dst2src, int32_t* route_rows,
+                   int32_t* expert_offsets, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * moe_fused_decode  -- one decode step of the routed experts  [inactive]
  *   x (T x H bf16) -> 1x128 fp8 quant -> gate/up GEMM per route (slot mode,
  *   A row = token) -> SiLU(gate)*up + 1x128 requant -> down GEMM per route

@@ -29,6 +29,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_gather_rows_scales", "moe_act_quant",
     "moe_pick_block_m", "moe_bf8_grouped_gemm", "moe_topk_reduce", "moe_fused_decode_workspace_size",
     "moe_fused_decode_workspace_layout", "moe_fused_decode_workspace_init", "moe_fused_decode",
+    "moe_route_prep_workspace_size", "moe_route_prep",
 )
 
 _lib = None
@@ -67,6 +68,8 @@ def lib():
             "moe_fused_decode_workspace_layout": ([I64, I64, I64, I64, P], I32),
             "moe_fused_decode_workspace_init": ([P, SZ, I64, I64, I64, I64, P], I32),
             "moe_fused_decode": ([P, I64, I64, I64, I64, P, P, I64, P, P, P, P, P, SZ, P, P], I32),
+            "moe_route_prep_workspace_size": ([I64, I64], SZ),
+            "moe_route_prep": ([P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -185,3 +188,25 @@ def fused_decode(x, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, workspace, out,
     _check("moe_fused_decode", lib().moe_fused_decode(
         _ptr(x), T, H, I, topk, _ptr(slot_ids), _ptr(weights), S, _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
         _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+
+
+def route_prep(logits, topk, stream=None):
+    """Top-k routing and the (expert, token)-ordered route maps of a prefill step.
+
+    logits: [T, E] float32 on the GPU.  Returns (expert_ids [T,topk] i32, weights [T,topk] f32,
+    dst2src [T*topk] i32, route_rows [T*topk] i32, expert_offsets [E+1] i32)."""
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    w = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    d2s = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    rr = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    size = lib().moe_route_prep_workspace_size(T, E)
+    if size == 0:
+        raise MoeError("moe_route_prep_workspace_size", MOE_ERR_SHAPE)
+    ws = torch.empty(size, dtype=torch.uint8, device=dev)
+    _check("moe_route_prep", lib().moe_route_prep(
+        _ptr(logits), _rowstride(logits), T, E, topk, _ptr(ids) if T else None, _ptr(w) if T else None,
+        _ptr(d2s) if T else None, _ptr(rr) if T else None, _ptr(offs), _ptr(ws), size, _stream(stream)))
+    return ids, w, d2s, rr, offs

@@ -146,3 +146,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(m, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         m.lib()
+
+
+def test_route_prep_workspace_and_checks():
+    L = m.lib()
+    size = L.moe_route_prep_workspace_size(4096, 256)
+    assert size >= (4096 // 16) * 256 * 4 and size % 256 == 0          # a count per (16-token chunk, expert)
+    assert L.moe_route_prep_workspace_size(4097, 256) > size
+    assert 0 < L.moe_route_prep_workspace_size(0, 256) < size
+    assert L.moe_route_prep_workspace_size(10, 0) == 0 and L.moe_route_prep_workspace_size(10, 1025) == 0
+    args = [FAKE, 256, 4096, 256, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, size, None]
+
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return L.moe_route_prep(*a)
+
+    assert call(a4=0) == m.MOE_ERR_SHAPE              # topk >= 1
+    assert call(a4=65) == m.MOE_ERR_SHAPE             # topk <= 64
+    assert call(a3=4, a4=5) == m.MOE_ERR_SHAPE        # topk <= E
+    assert call(a3=1025) == m.MOE_ERR_SHAPE           # E <= 1024
+    assert call(a1=255) == m.MOE_ERR_SHAPE            # logits stride >= E
+    assert call(a0=None) == m.MOE_ERR_NULL
+    assert call(a7=None) == m.MOE_ERR_NULL
+    assert call(a9=None) == m.MOE_ERR_NULL
+    assert call(a11=size - 1) == m.MOE_ERR_WORKSPACE
+    assert call(a10=P(0x1008)) == m.MOE_ERR_ALIGN

@@ -81,6 +81,16 @@ def routing(T: int, E: int, topk: int, seed: int):
     return ids, w
 
 
+def router_logits(T: int, E: int, seed: int, skew: float = 0.0) -> np.ndarray:
+    """fp32 router logits [T, E]: N(0,1) per (token, expert) plus a per-expert N(0, skew) offset, so
+    skew > 0 gives the uneven expert loads of a trained router (a few hot experts, some cold)."""
+    rng = np.random.default_rng(seed)
+    lg = rng.standard_normal((T, E))
+    if skew:
+        lg = lg + skew * rng.standard_normal(E)[None, :]
+    return lg.astype(np.float32)
+
+
 @dataclass
 class DecodeCase:
     T: int
