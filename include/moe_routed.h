@@ -121,10 +121,10 @@ int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, in
  * moe_pick_block_m  [tile]
  *   The M tile of the grouped GEMM for `routes` routed rows over `experts`
  *   experts.  As on the page, the tile grows with rows per expert; the
- *   thresholds are MI355X's (a sweep of every tile at 6, 24 and 96 rows per
- *   expert): the smallest power of two >= 2*ceil(routes/experts), clamped to
- *   [32, 64], so 6 rows per expert give 32 and 24 or 96 give 64.  Pure
- *   function of its two arguments; returns 32 when either is <= 0.
+ *   thresholds are MI355X's (a sweep of every tile at 6, 24, 48 and 96 rows
+ *   per expert): with r = ceil(routes/experts), r <= 8 gives 16, r <= 64
+ *   gives 64, larger r gives 128.  Pure function of its two arguments;
+ *   returns 16 when either is <= 0.
  */
 int moe_pick_block_m(int64_t routes, int64_t experts);
 
@@ -143,6 +143,8 @@ int moe_pick_block_m(int64_t routes, int64_t experts);
  *        expert_offsets[0] = 0 and expert_offsets[n_experts] <= m_rows (rows
  *        beyond it are left untouched).  block_m = 0 picks the M tile with
  *        moe_pick_block_m(m_rows, n_experts); 16, 32, 64 or 128 forces it.
+ *        The kernel is persistent (one workgroup per resident slot); tiles
+ *        come from the device offsets, clamped to [0, m_rows].
  *   mode MOE_MODE_SLOT (decode, [inactive]): row r uses slot slot_ids[r]
  *        (DEVICE int32 [m_rows]) and A row r / a_row_div; a negative slot
  *        writes a +0 output row and reads no A, W or scales of that row.

@@ -88,14 +88,12 @@ extern "C" const char* moe_status_string(int status) {
 extern "C" const char* moe_last_hip_error(void) { return g_last_hip_error; }
 
 extern "C" int moe_pick_block_m(int64_t routes, int64_t experts) {
-    // Smallest power of two >= 2 * ceil(routes / experts), clamped to [32, 64]: the tile
-    // grows with rows per expert as on the pages, with thresholds from a sweep of all
-    // tiles on MI355X (6 rows per expert -> 32, 24 and 96 -> 64).
-    if (routes <= 0 || experts <= 0) return 32;
-    const int64_t per = 2 * ceil_div(routes, experts);
-    int64_t bm = 32;
-    while (bm < per && bm < 64) bm <<= 1;
-    return (int)bm;
+    // The tile grows with rows per expert r as on the pages, with MI355X's own thresholds from a
+    // sweep of every tile: r <= 8 -> 16 (6 rows), r <= 64 -> 64 (24 and 48 rows), else 128 (96 rows:
+    // an expert's rows in one tile, so each weight byte is streamed once).
+    if (routes <= 0 || experts <= 0) return 16;
+    const int64_t r = ceil_div(routes, experts);
+    return r <= 8 ? 16 : (r <= 64 ? 64 : 128);
 }
 
 extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,

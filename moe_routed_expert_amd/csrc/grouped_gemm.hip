@@ -4,10 +4,9 @@
 // BLOCK_K is 128, one block-scale pair per K step).
 //
 // MI355X design.
-//  * Tile BM x 256 x 128 with 8 waves of 32 columns (BM <= 64) or 16 waves of
-//    16 columns (BM = 128); each wave owns its columns for all BM rows, so a
-//    wave's columns sit inside one 128x128 weight-scale block and the weight
-//    scale is one scalar per K step.  A last tile may hold only 128 columns
+//  * Tile BM x 256 x 128 with 8 waves of 32 columns; each wave owns its
+//    columns for all BM rows, so a wave's columns sit inside one 128x128
+//    weight-scale block and the weight scale is one scalar per K step.  A last tile may hold only 128 columns
 //    (N % 256 == 128); its upper half of the waves then idles.
 //  * Weights are the dominant HBM stream and each weight byte of a tile is used
 //    by one wave only, so they go global -> registers directly in MFMA operand
@@ -19,18 +18,24 @@
 //    (each lane's 32 bytes contiguous), so the MFMA operand reads are
 //    conflict-free.  Registers are kept low enough for two resident
 //    workgroups per CU at BM <= 64, which hides more latency than deeper
-//    per-wave prefetch (measured).
+//    per-wave prefetch (measured); BM = 128 runs one workgroup per CU.
 //  * Per K step: p = A*W with a fresh 16x16x128 e4m3 MFMA, then
 //    acc += p * (a_s[row][kb] * w_s[kb]) in fp32.  All scales of the tile are
 //    staged in LDS before the loop, and the loop issues no load behind a
 //    branch: vector loads retire in order, so a late small load or a load the
 //    compiler cannot count would make a step wait for every load in flight.
-//  * Work map: M tiles are (expert, 0..ceil(rows_e/BM)-1); the grid is an upper
-//    bound (ceil(m_rows/BM) + E tiles) fixed by scalars, and each workgroup finds
-//    its (expert, m0) from the device offsets with a block scan, so the launch
-//    can be captured.  Workgroup ids are remapped so that consecutive tiles of
-//    one M tile land on the same XCD (the dispatcher deals workgroups to the 8
-//    XCDs round-robin), keeping the A tile in that XCD's L2.
+//  * Work map: M tiles are (expert, 0..ceil(rows_e/BM)-1) and a tile is (M
+//    tile, 256-column N tile).  The kernel is persistent: the grid is the
+//    number of workgroups the device holds at once (fixed by scalars, so the
+//    launch can be captured); each workgroup scans the device offsets once into
+//    an LDS table of every expert's first M tile, then walks its share of the
+//    live tiles.  The live tiles are cut into 8 equal contiguous ranges, one per
+//    XCD (the dispatcher deals workgroups to the 8 XCDs round-robin), and an
+//    XCD's workgroups take its range in order, so the tiles in flight on an XCD
+//    are neighbouring N tiles of neighbouring M tiles: their A rows and weight
+//    tiles meet in that XCD's L2, and every XCD gets the same number of tiles.
+//  * A tile's expert is a binary search of the LDS table; its scales are
+//    loaded row-contiguous, all requests in flight before the LDS stores.
 #include "device.h"
 #include "host.h"
 
@@ -40,18 +45,19 @@ constexpr int kXcds = 8;
 constexpr int kMaxExpertsScan = 1024;            // experts handled by the in-kernel scan
 constexpr int kGgMaxKb = 64;                     // K/128 blocks whose scales a tile keeps in LDS (K <= 8192)
 
-// Tile configuration per M tile, always 256 columns (which halves how often the A
-// tile is re-read compared with a 128-column tile).  Up to 64 rows: 8 waves of
-// two 16-column MFMA tiles each, with a weight ring that shrinks as the M tile
-// grows.  128 rows (an expert's whole row range at high route density, so each
-// weight byte enters the CUs once): 16 waves of one 16-column tile each, which
-// keeps the accumulators and a 4-step weight ring under 128 registers.
+// Tile configuration per M tile: always 8 waves of two 16-column MFMA tiles, 256 columns (which
+// halves how often the A tile is re-read compared with a 128-column tile).  Up to 64 rows the
+// registers stay under 128, so two workgroups share a CU (4 waves per SIMD) and hide each other's
+// latency; the weight ring shrinks as the M tile grows.  128 rows (an expert's whole row range at
+// high route density, so each weight byte enters the CU once) need about 200 registers: one
+// workgroup per CU (2 waves per SIMD) with a deeper weight ring instead.
 template <int BM> struct GgCfg {
-    static constexpr int WAVES = BM >= 128 ? 16 : 8;
-    static constexpr int TPW = BM >= 128 ? 1 : 2;                   // 16-column MFMA tiles per wave
+    static constexpr int WAVES = 8;
+    static constexpr int TPW = 2;                                   // 16-column MFMA tiles per wave
     static constexpr int BN = 16 * TPW * WAVES;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int S = BM >= 128 ? 4 : (BM >= 64 ? 3 : 4);   // weight ring depth (K steps)
+    static constexpr int WAVES_PER_EU = BM >= 128 ? 2 : 4;          // occupancy the registers are sized for
 };
 
 // Exclusive scan of one int per thread over a block of WAVES waves.
@@ -71,13 +77,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* ldsw) {
     return base + x - v;
 }
 
+// One BM x 256 tile: rows [row0, min(row0 + BM, row_end)) of expert `expert`, N tile n_tile.  The
+// caller's workgroup runs it with all threads; it leaves LDS free for the next tile (its last LDS
+// read is before its last barrier).
 template <int BM, int OUT_DT>
-__global__ void __launch_bounds__(GgCfg<BM>::THREADS, BM >= 128 ? 1 : 2)
-grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const float* __restrict__ a_s,
-                    int64_t a_s_stride, const uint8_t* __restrict__ w_q, int64_t w_stride_e, int64_t w_stride_n,
-                    const float* __restrict__ w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int n_experts,
-                    int64_t N, int64_t K, const int32_t* __restrict__ offsets, int n_tiles_n, int grid_per_xcd,
-                    void* __restrict__ out, int64_t out_stride) {
+__device__ __forceinline__ void grouped_gemm_tile(const uint8_t* __restrict__ a_q, int64_t a_stride,
+                                                  const float* __restrict__ a_s, int64_t a_s_stride,
+                                                  const uint8_t* __restrict__ w_q, int64_t w_stride_e,
+                                                  int64_t w_stride_n, const float* __restrict__ w_s,
+                                                  int64_t w_s_stride_e, int64_t w_s_stride_n, int64_t N, int64_t K,
+                                                  int expert, int row0, int row_end, int n_tile,
+                                                  void* __restrict__ out, int64_t out_stride) {
     using C = GgCfg<BM>;
     constexpr int TPW = C::TPW;
     constexpr int CPW = 16 * TPW;               // columns per wave
@@ -86,50 +96,16 @@ grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const flo
     constexpr int NT = C::THREADS;
     constexpr int A_CHUNKS = BM * 8;            // 16-byte chunks of one A K-step
     constexpr int A_PER_THREAD = (A_CHUNKS + NT - 1) / NT;
-    constexpr int E_PER_THREAD = kMaxExpertsScan / NT;
+    constexpr int SA_ROW = BM + 4;              // padded [kb] row of the A-scale table (16-byte aligned)
     __shared__ __attribute__((aligned(32))) uint8_t a_lds[2][BM * 128];
-    __shared__ __attribute__((aligned(16))) float sa_lds[kGgMaxKb][BM];   // A scales of the tile, [kb][row]
-    __shared__ float ws_lds[2][kGgMaxKb];                                  // weight scales, [block][kb]
-    __shared__ int scan_lds[C::WAVES];
-    __shared__ int tile_info[3];                // expert, row begin, row end
+    __shared__ __attribute__((aligned(16))) float sa_lds[kGgMaxKb * SA_ROW];   // A scales, [kb][row]
+    __shared__ float ws_lds[2][kGgMaxKb];                                       // weight scales, [block][kb]
 
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    // XCD-aware remap of the linear workgroup id
-    const int bid = blockIdx.x;
-    const int logical = (bid % kXcds) * grid_per_xcd + bid / kXcds;
-    const int m_tile = logical / n_tiles_n, n_tile = logical % n_tiles_n;
-
-    // ---- find (expert, m0) for this M tile from the device offsets ----
-    int local = 0, my_tiles[E_PER_THREAD];
-#pragma unroll
-    for (int i = 0; i < E_PER_THREAD; i++) {
-        const int e = threadIdx.x * E_PER_THREAD + i;
-        int t = 0;
-        if (e < n_experts) t = (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-        my_tiles[i] = t;
-        local += t;
-    }
-    int before = block_exclusive_scan<C::WAVES>(local, scan_lds);
-    if (threadIdx.x == 0) tile_info[0] = -1;
-    __syncthreads();
-    if (m_tile >= before && m_tile < before + local) {
-        int acc_t = before;
-#pragma unroll
-        for (int i = 0; i < E_PER_THREAD; i++) {
-            if (m_tile >= acc_t && m_tile < acc_t + my_tiles[i]) {
-                const int e = threadIdx.x * E_PER_THREAD + i;
-                tile_info[0] = e;
-                tile_info[1] = offsets[e] + (m_tile - acc_t) * BM;
-                tile_info[2] = offsets[e + 1];
-            }
-            acc_t += my_tiles[i];
-        }
-    }
-    __syncthreads();
-    const int expert = tile_info[0];
-    if (expert < 0) return;                     // beyond the live tiles: nothing to do
-    const int row0 = tile_info[1], row_end = tile_info[2];
-
+    // A fresh copy of the thread index per tile: without it the compiler hoists every thread-index
+    // expression of the tile out of the caller's tile loop and keeps them all live across it.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int nkb = (int)(K / 128);
     const int64_t n0 = (int64_t)n_tile * C::BN;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -143,17 +119,29 @@ grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const flo
     const uint8_t* wp1 = wp0 + 16 * w_stride_n;
     const int wsb = (int)((wcol - n0) / 128);   // this wave's 128-column scale block within the tile
 
-    // All scales of the tile go to LDS once: A scales [kb][row], weight scales [block][kb].
-    for (int i = threadIdx.x; i < nkb * BM; i += NT) {
-        const int kb = i / BM, rr = i % BM;
+    // All scales of the tile go to LDS once: A scales [kb][row] (wave w reads rows w, w + WAVES, ...,
+    // lane = K block, so each request is one contiguous row of scales), weight scales [block][kb]
+    // (waves 0 and 1, one 128-column block each).  Every load is requested before the first LDS
+    // store, and no index needs a division by the block count.
+    constexpr int SA_ROWS = BM / C::WAVES;      // A-scale rows per wave
+    const int kbl = lane < nkb ? lane : nkb - 1;
+    float sa_v[SA_ROWS];
+#pragma unroll
+    for (int j = 0; j < SA_ROWS; j++) {
+        const int rr = wave + j * C::WAVES;
         const int row = row0 + rr < row_end ? row0 + rr : row_end - 1;
-        sa_lds[kb][rr] = a_s[(int64_t)row * a_s_stride + kb];
+        sa_v[j] = a_s[(int64_t)row * a_s_stride + kbl];
     }
     const int64_t nblk = (N - n0) >= 256 ? 2 : 1;
-    for (int i = threadIdx.x; i < 2 * nkb; i += NT) {
-        const int blk = i / nkb, kb = i % nkb;
-        const int64_t b = n0 / 128 + (blk < nblk ? blk : 0);
-        ws_lds[blk][kb] = w_s[(int64_t)expert * w_s_stride_e + b * w_s_stride_n + kb];
+    float ws_v = 0.0f;
+    if (wave < 2) {
+        const int64_t b = n0 / 128 + (wave < nblk ? wave : 0);
+        ws_v = w_s[(int64_t)expert * w_s_stride_e + b * w_s_stride_n + kbl];
+    }
+    if (lane < nkb) {
+#pragma unroll
+        for (int j = 0; j < SA_ROWS; j++) sa_lds[lane * SA_ROW + wave + j * C::WAVES] = sa_v[j];
+        if (wave < 2) ws_lds[wave][lane] = ws_v;
     }
 
     // A staging: chunk c of the BM x 128 K-step -> row c/8, byte 16*(c%8); stored in fragment order.
@@ -162,7 +150,7 @@ grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const flo
     int a_dst[A_PER_THREAD];
 #pragma unroll
     for (int j = 0; j < A_PER_THREAD; j++) {
-        const int c0 = threadIdx.x + j * NT;
+        const int c0 = tid + j * NT;
         const int c = c0 < A_CHUNKS ? c0 : c0 % A_CHUNKS;
         const int rr = c / 8, ch = c % 8;
         int row = row0 + rr;
@@ -187,7 +175,7 @@ grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const flo
     auto store_a = [&](int stage, int buf) {
 #pragma unroll
         for (int j = 0; j < A_PER_THREAD; j++)
-            if (A_CHUNKS % NT == 0 || threadIdx.x + j * NT < A_CHUNKS)
+            if (A_CHUNKS % NT == 0 || tid + j * NT < A_CHUNKS)
                 *reinterpret_cast<v4i*>(&a_lds[buf][a_dst[j]]) = a_reg[stage][j];
     };
     v4i w_ring[S][2 * TPW];
@@ -234,7 +222,7 @@ grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const flo
                 for (int m = 0; m < MS; m++) {
                     const v8i a = *reinterpret_cast<const v8i*>(&a_lds[buf][m * 2048 + lane * 32]);
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f sa = *reinterpret_cast<const v4f*>(&sa_lds[kb][m * 16 + 4 * (lane / 16)]);
+                    const v4f sa = *reinterpret_cast<const v4f*>(&sa_lds[kb * SA_ROW + m * 16 + 4 * (lane / 16)]);
                     const v4f sc = sa * sw;
 #pragma unroll
                     for (int c = 0; c < TPW; c++) acc[m][c] += mfma16x16x128_e4m3(a, b[c], zero) * sc;
@@ -259,6 +247,103 @@ grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const flo
     }
 }
 
+// Workgroups of one configuration the device holds at once (cached per device and output type).
+template <int BM, int OUT_DT>
+__global__ void __launch_bounds__(GgCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(GgCfg<BM>::WAVES_PER_EU, 8)))
+grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const float* __restrict__ a_s,
+                    int64_t a_s_stride, const uint8_t* __restrict__ w_q, int64_t w_stride_e, int64_t w_stride_n,
+                    const float* __restrict__ w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int n_experts,
+                    int64_t N, int64_t K, const int32_t* __restrict__ offsets, int m_rows, int n_tiles_n, int per_xcd,
+                    int step_m, int step_n, void* __restrict__ out, int64_t out_stride) {
+    using C = GgCfg<BM>;
+    constexpr int NT = C::THREADS;
+    constexpr int E_PER_THREAD = kMaxExpertsScan / NT;
+    __shared__ int cum_lds[kMaxExpertsScan + 1];    // first M tile of each expert; [E] = live M tiles
+    __shared__ int off_lds[kMaxExpertsScan + 1];    // expert row offsets
+    __shared__ int scan_lds[C::WAVES];
+
+    // ---- tile table, once per workgroup ----
+    int local = 0, my_tiles[E_PER_THREAD];
+#pragma unroll
+    for (int i = 0; i < E_PER_THREAD; i++) {
+        const int e = threadIdx.x * E_PER_THREAD + i;
+        int t = 0;
+        if (e < n_experts) {
+            // offsets clamped to [0, m_rows] so that malformed offsets never reach past the rows
+            const int o0 = min(max(offsets[e], 0), m_rows), o1 = min(max(offsets[e + 1], o0), m_rows);
+            off_lds[e] = o0;
+            if (e == n_experts - 1) off_lds[e + 1] = o1;
+            t = (o1 - o0 + BM - 1) / BM;
+        }
+        my_tiles[i] = t;
+        local += t;
+    }
+    int run = block_exclusive_scan<C::WAVES>(local, scan_lds);
+#pragma unroll
+    for (int i = 0; i < E_PER_THREAD; i++) {
+        const int e = threadIdx.x * E_PER_THREAD + i;
+        if (e < n_experts) cum_lds[e] = run;
+        run += my_tiles[i];
+    }
+    if (threadIdx.x == NT - 1) cum_lds[n_experts] = run;     // threads past the experts hold no tiles
+    __syncthreads();
+
+    // ---- this workgroup's share: XCD range [lo, hi), every per_xcd-th tile from its slot ----
+    const int64_t live = (int64_t)__builtin_amdgcn_readfirstlane(cum_lds[n_experts]) * n_tiles_n;
+    const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+    const int lo = (int)(live * xcd / kXcds), hi = (int)(live * (xcd + 1) / kXcds);
+    int t = lo + slot;
+    // (M tile, N tile) of t, advanced by (step_m, step_n) = divmod(per_xcd, n_tiles_n) per tile
+    int m_tile = t / n_tiles_n, n_tile = t - m_tile * n_tiles_n;
+    for (; t < hi; t += per_xcd) {
+        // last expert whose first tile <= m_tile; the table values are made wave-uniform so the tile's
+        // addresses stay scalar
+        int e_lo = 0, e_hi = n_experts - 1;
+        while (e_lo < e_hi) {
+            const int mid = (e_lo + e_hi + 1) / 2;
+            if (__builtin_amdgcn_readfirstlane(cum_lds[mid]) <= m_tile)
+                e_lo = mid;
+            else
+                e_hi = mid - 1;
+        }
+        const int expert = e_lo;
+        const int row0 = __builtin_amdgcn_readfirstlane(off_lds[expert]) +
+                         (m_tile - __builtin_amdgcn_readfirstlane(cum_lds[expert])) * BM;
+        const int row_end = __builtin_amdgcn_readfirstlane(off_lds[expert + 1]);
+        grouped_gemm_tile<BM, OUT_DT>(a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, w_s, w_s_stride_e,
+                                      w_s_stride_n, N, K, expert, row0, row_end, n_tile, out, out_stride);
+        m_tile += step_m;
+        n_tile += step_n;
+        if (n_tile >= n_tiles_n) {
+            n_tile -= n_tiles_n;
+            m_tile++;
+        }
+    }
+}
+
+template <int BM>
+static int gg_resident_blocks(int out_dt) {
+    using C = GgCfg<BM>;
+    static int cached[64][3];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || out_dt < 0 || out_dt > 2) return 0;
+    int& c = cached[dev][out_dt];
+    if (c == 0) {
+        int per_cu = 0, cus = 0;
+        hipError_t e;
+        if (out_dt == MOE_F32)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, kF32>, C::THREADS, 0);
+        else if (out_dt == MOE_BF16)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, kBF16>, C::THREADS, 0);
+        else
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, kF16>, C::THREADS, 0);
+        if (e != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        c = per_cu * cus > 0 ? per_cu * cus : -1;
+    }
+    return c > 0 ? c : 0;
+}
+
 template <int BM>
 static int launch_grouped_bm(hipStream_t st, int out_dt, const uint8_t* a_q, int64_t a_stride, const float* a_s,
                              int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
@@ -267,13 +352,14 @@ static int launch_grouped_bm(hipStream_t st, int out_dt, const uint8_t* a_q, int
     using C = GgCfg<BM>;
     if (N % 128 != 0) return MOE_ERR_SHAPE;
     const int64_t n_tiles_n = ceil_div(N, C::BN);
-    const int64_t m_tiles = ceil_div(m_rows, BM) + E;   // upper bound over any split of the rows
-    int64_t total = ceil_div(n_tiles_n * m_tiles, kXcds) * kXcds;
-    if (total > 0x7FFFFFFF) return MOE_ERR_SHAPE;
-    const int per_xcd = (int)(total / kXcds);
-    dim3 grid((unsigned)total), block(C::THREADS);
+    if (m_rows > 0x7FFFFFFF || n_tiles_n * (ceil_div(m_rows, BM) + E) > 0x7FFFFFFF - (1 << 20)) return MOE_ERR_SHAPE;
+    const int wgs = gg_resident_blocks<BM>(out_dt);
+    if (wgs < kXcds) return MOE_ERR_HIP;
+    const int per_xcd = wgs / kXcds;
+    const int step_m = per_xcd / (int)n_tiles_n, step_n = per_xcd % (int)n_tiles_n;
+    dim3 grid((unsigned)(per_xcd * kXcds)), block(C::THREADS);
 #define MOE_GG_ARGS a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, w_s, w_s_stride_e, w_s_stride_n, \
-                    (int)E, N, K, offsets, (int)n_tiles_n, per_xcd, out, out_stride
+                    (int)E, N, K, offsets, (int)m_rows, (int)n_tiles_n, per_xcd, step_m, step_n, out, out_stride
     if (out_dt == MOE_F32)
         hipLaunchKernelGGL((grouped_gemm_kernel<BM, kF32>), grid, block, 0, st, MOE_GG_ARGS);
     else if (out_dt == MOE_BF16)

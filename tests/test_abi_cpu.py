@@ -44,23 +44,26 @@ def test_abi_version_and_status_strings():
 def test_pick_block_m_follows_density_like_the_page():
     """The page (sm_89) found the best M tile tracks rows per expert (16, 32, 128 at 6, 24, 96 rows,
     tests/golden/tile_picker_density.json).  The picker keeps that rule -- a pure, non-decreasing
-    function of rows per expert -- with MI355X's own thresholds from a sweep of every tile at the same
-    three densities: 32 at 6 rows per expert, 64 at 24 and at 96."""
+    function of rows per expert -- with MI355X's own thresholds from a sweep of every tile: 16 at 6
+    rows per expert, 64 at 24 (and 48), 128 at 96, so the ends agree with the page and the middle
+    tile is 64 rather than 32."""
     spec = json.load(open(os.path.join(ROOT, "tests", "golden", "tile_picker_density.json")))
-    mi355x = {6: 32, 24: 64, 96: 64}
+    mi355x = {6: 16, 24: 64, 96: 128}
     prev = 0
     for c in spec["cases"]:
         bm = m.pick_block_m(c["routes"], spec["experts"])
         assert bm == mi355x[c["rows_per_expert"]], c
         assert bm >= prev
         prev = bm
+    assert [m.pick_block_m(c["routes"], spec["experts"]) for c in spec["cases"]][::2] == \
+        [c["block_m"] for c in spec["cases"]][::2]          # the page's two ends
     last = 0
     for r in range(0, 100000, 97):
         bm = m.pick_block_m(r, 256)
         assert bm in (16, 32, 64, 128) and bm >= last
         last = bm
-    assert m.pick_block_m(0, 256) == 32 and m.pick_block_m(10, 0) == 32
-    assert m.pick_block_m(256 * 1000, 256) == 64
+    assert m.pick_block_m(0, 256) == 16 and m.pick_block_m(10, 0) == 16
+    assert m.pick_block_m(256 * 48, 256) == 64 and m.pick_block_m(256 * 1000, 256) == 128
 
 
 P = ctypes.c_void_p
