@@ -245,6 +245,18 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
 
 
+def prefill_all(torch, m, wl):
+    """The grouped GEMMs at 1536, 6144 and 24576 routes (E=256, top-6, H=4096, I=1024)."""
+    weights = prefill_weights(torch, wl, 256, 4096, 1024)
+    res = []
+    for T in (256, 1024, 4096):
+        log("prefill %d routes" % (T * 6))
+        res.append(prefill_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights))
+    del weights
+    torch.cuda.empty_cache()
+    return res
+
+
 def route_prep_bench(torch, m, wl, T, E, topk, reps):
     """Device routing prep (top-k, weights, route maps) on skewed router logits: 16 calls over 16
     logit sets in one graph, so the time is the device's, not the host's launch latency."""
@@ -311,6 +323,7 @@ def main():
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--only-prefill", action="store_true", help="copy calibration and the prefill GEMMs only")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -323,6 +336,10 @@ def main():
     reps = max(1, args.steps // LAYERS)
     steps = reps * LAYERS
     calib = copy_calibration(torch, m)
+    if args.only_prefill:
+        print(json.dumps({"metric": "prefill fp8 TFLOP/s (grouped GEMMs only)", "copy_calibration": calib,
+                          "prefill_densities": prefill_all(torch, m, wl)}))
+        return
 
     log("decode H=2048 I=768: building %d layer pools" % LAYERS)
     pools = decode_pools(torch, wl, 2048, 768, 64, seed=1)
@@ -348,15 +365,8 @@ def main():
         log("route prep")
         extra["route_prep"] = [route_prep_bench(torch, m, wl, T, 256, 6, 20) for T in (256, 4096)]
         if not args.skip_prefill:
-            weights = prefill_weights(torch, wl, 256, 4096, 1024)
-            extra["prefill_densities"] = []
-            for T in (256, 1024, 4096):
-                log("prefill %d routes" % (T * 6))
-                r = prefill_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights)
-                extra["prefill_densities"].append(r)
-                if T == 4096:
-                    extra["prefill"] = r
-            del weights
+            extra["prefill_densities"] = prefill_all(torch, m, wl)
+            extra["prefill"] = extra["prefill_densities"][-1]
     tr = measured_traffic()
     roof = dict(bound="hbm",
                 kernel="moe_fused_decode step = one decode_step_kernel launch (gate/up and down tiles in one "
