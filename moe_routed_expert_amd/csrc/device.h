@@ -71,6 +71,22 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, float v) {
     else ((uint16_t*)p)[i] = f32_to_f16(v);
 }
 
+// Four consecutive elements i..i+3 from fp32 in one store; p + i must be aligned to 4 elements.
+template <int DT>
+__device__ __forceinline__ void store4_from_f32(void* p, int64_t i, v4f v) {
+    if constexpr (DT == kF32) {
+        *reinterpret_cast<v4f*>((float*)p + i) = v;
+    } else {
+        uint16_t h[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) h[k] = DT == kBF16 ? f32_to_bf16(v[k]) : f32_to_f16(v[k]);
+        uint2 w;
+        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        *reinterpret_cast<uint2*>((uint16_t*)p + i) = w;
+    }
+}
+
 // Max over aligned groups of 2^LOG lanes (butterfly; every lane gets the group max).
 template <int LOG>
 __device__ __forceinline__ float group_max(float v) {

@@ -19,8 +19,10 @@
 //    conflict-free.  Registers are kept low enough for two resident
 //    workgroups per CU at BM <= 64, which hides more latency than deeper
 //    per-wave prefetch (measured); BM = 128 runs one workgroup per CU.
-//  * Per K step: p = A*W with a fresh 16x16x128 e4m3 MFMA, then
-//    acc += p * (a_s[row][kb] * w_s[kb]) in fp32.  All scales of the tile are
+//  * Per K step: p = W*A^T with a fresh 16x16x128 e4m3 MFMA (weights as the
+//    row operand, so a lane's four results are four columns of one A row),
+//    then acc += p * (a_s[row][kb] * w_s[kb]) in fp32 with one scale per lane;
+//    the epilogue stores the four columns as one vector.  All scales of the tile are
 //    staged in LDS before the loop, and the loop issues no load behind a
 //    branch: vector loads retire in order, so a late small load or a load the
 //    compiler cannot count would make a step wait for every load in flight.
@@ -220,28 +222,36 @@ __device__ __forceinline__ void grouped_gemm_tile(const uint8_t* __restrict__ a_
                     b[c] = __builtin_shufflevector(w_ring[s][2 * c], w_ring[s][2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                 for (int m = 0; m < MS; m++) {
+                    // W is the MFMA's row operand and A its column operand, so a lane's four results
+                    // share one A row (lane % 16) and take a single scale
                     const v8i a = *reinterpret_cast<const v8i*>(&a_lds[buf][m * 2048 + lane * 32]);
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f sa = *reinterpret_cast<const v4f*>(&sa_lds[kb * SA_ROW + m * 16 + 4 * (lane / 16)]);
-                    const v4f sc = sa * sw;
+                    const float sc = sa_lds[kb * SA_ROW + m * 16 + (lane & 15)] * sw;
 #pragma unroll
-                    for (int c = 0; c < TPW; c++) acc[m][c] += mfma16x16x128_e4m3(a, b[c], zero) * sc;
+                    for (int c = 0; c < TPW; c++) acc[m][c] += mfma16x16x128_e4m3(b[c], a, zero) * sc;
                 }
             }
             store_a((s + 1) % S, buf ^ 1);            // A step kb+1 (requested a step ago)
             __syncthreads();
         }
     }
-    // ---- epilogue: lane holds rows m*16 + 4*(lane/16) + i, column lane%16 of each sub-tile ----
+    // ---- epilogue: lane holds row m*16 + lane%16, columns 4*(lane/16) + i of each 16-column sub-tile,
+    // stored as one 4-element vector where the output allows it ----
+    const bool vec4 = (out_stride % 4 == 0) &&
+                      (reinterpret_cast<uintptr_t>(out) % (OUT_DT == kF32 ? 16 : 8) == 0);
 #pragma unroll
     for (int m = 0; m < MS; m++) {
+        const int row = row0 + m * 16 + (lane & 15);
+        if (cols && row < row_end) {
+            const int64_t o = (int64_t)row * out_stride + n0 + wave * CPW + 4 * (lane / 16);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int row = row0 + m * 16 + 4 * (lane / 16) + i;
-            if (cols && row < row_end) {
-                const int64_t o = (int64_t)row * out_stride + n0 + wave * CPW + (lane & 15);
+            for (int c = 0; c < TPW; c++) {
+                if (vec4) {
+                    store4_from_f32<OUT_DT>(out, o + 16 * c, acc[m][c]);
+                } else {
 #pragma unroll
-                for (int c = 0; c < TPW; c++) store_from_f32<OUT_DT>(out, o + 16 * c, acc[m][c][i]);
+                    for (int i = 0; i < 4; i++) store_from_f32<OUT_DT>(out, o + 16 * c + i, acc[m][c][i]);
+                }
             }
         }
     }
