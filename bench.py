@@ -242,6 +242,27 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
         out[name] = dict(us_median=us, tflops=tflops, fp8_peak_frac=tflops / FP8_PEAK_TFLOPS,
                          roofline_frac=tflops / attainable, arithmetic_intensity=ai, bytes=nbytes,
                          hbm_gbs=nbytes / (us * 1e-6) / 1e9)
+    # gate/up with the SiLU-mul requant fused into its epilogue, against the unfused pair (gate/up above
+    # writing bf16 c1, then act_quant reading it)
+    aq = torch.empty((R, I), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
+    for _ in range(3):
+        m.bf8_grouped_gemm_silu_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_)
+    t = Timer(torch)
+    for _ in range(steps):
+        t.start()
+        m.bf8_grouped_gemm_silu_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_)
+        t.stop()
+    us_f = statistics.median(t.us())
+    t = Timer(torch)
+    for _ in range(steps):
+        t.start()
+        m.act_quant(c1, aq, as_, act=m.MOE_ACT_SILU_MUL)
+        t.stop()
+    us_a = statistics.median(t.us())
+    flops = 2.0 * R * 2 * I * H
+    out["gate_up_silu_quant"] = dict(us_median=us_f, tflops=flops / (us_f * 1e-6) / 1e12,
+                                     unfused_us=out["gate_up"]["us_median"] + us_a, act_quant_us=us_a)
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
 
 

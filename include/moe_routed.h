@@ -164,6 +164,30 @@ int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s,
                          void* out, int out_dt, int64_t out_stride, void* stream);
 
 /*
+ * moe_bf8_grouped_gemm_silu_quant  -- the prefill gate/up GEMM with the
+ *   activation and its requant in the epilogue  [tile] [inactive]
+ *   The gate/up GEMM of grouped (prefill) mode followed by moe_act_quant
+ *   SILU_MUL, in one launch: with c1 the fp32 GEMM result of
+ *   moe_bf8_grouped_gemm (N = 2I, W13 rows 0..I-1 gate, I..2I-1 up), never
+ *   stored, h[r, c] = (g / (1 + exp(-g))) * u with g = c1[r, c], u = c1[r, I + c]
+ *   (fp32), then per 1x128 group s = amax/448 and q = e4m3(h/s) as in
+ *   moe_act_quant (q = 0x00, s = +0 when amax = 0).
+ *   a_q, a_s, w_q, w_s, expert_offsets, m_rows, block_m: as moe_bf8_grouped_gemm
+ *   in MOE_MODE_GROUPED with N = 2I.
+ *   out_q [m_rows][q_stride] fp8 (I used), out_s [m_rows][s_stride] fp32 (I/128
+ *   used).  The results equal moe_bf8_grouped_gemm with MOE_F32 output followed
+ *   by moe_act_quant SILU_MUL on it, bit for bit.
+ *   Requirements: I % 128 == 0, K % 128 == 0, K <= 8192, 1 <= n_experts <=
+ *   1024, alignment as moe_bf8_grouped_gemm; m_rows == 0 launches nothing.
+ */
+int moe_bf8_grouped_gemm_silu_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                                    const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
+                                    const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n,
+                                    int64_t n_experts, int64_t I, int64_t K, const int32_t* expert_offsets,
+                                    int64_t m_rows, int32_t block_m, uint8_t* out_q, int64_t q_stride,
+                                    float* out_s, int64_t s_stride, void* stream);
+
+/*
  * moe_topk_reduce  -- routing-weighted sum over each token's top-k routes
  *   out[t, h] = bf16_rne( sum_{j = 0..topk-1, slot_ids[t,j] >= 0} weights[t,j] * y[row(t,j), h] )
  *   summed in fp32 in ascending j from +0; row(t,j) = route_rows[t*topk + j]

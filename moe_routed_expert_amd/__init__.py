@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_gather_rows_scales", "moe_act_quant",
     "moe_pick_block_m", "moe_bf8_grouped_gemm", "moe_topk_reduce", "moe_fused_decode_workspace_size",
     "moe_fused_decode_workspace_layout", "moe_fused_decode_workspace_init", "moe_fused_decode",
-    "moe_route_prep_workspace_size", "moe_route_prep",
+    "moe_route_prep_workspace_size", "moe_route_prep", "moe_bf8_grouped_gemm_silu_quant",
 )
 
 _lib = None
@@ -70,6 +70,8 @@ def lib():
             "moe_fused_decode": ([P, I64, I64, I64, I64, P, P, I64, P, P, P, P, P, SZ, P, P], I32),
             "moe_route_prep_workspace_size": ([I64, I64], SZ),
             "moe_route_prep": ([P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
+            "moe_bf8_grouped_gemm_silu_quant": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, P, I64,
+                                                 I32, P, I64, P, I64, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -145,6 +147,21 @@ def bf8_grouped_gemm(a_q, a_s, w_q, w_s, out, *, mode, expert_offsets=None, slot
         _ptr(w_q), w_q.stride(0), w_q.stride(1), _ptr(w_s), w_s.stride(0), w_s.stride(1),
         E, N, K, mode, _ptr(expert_offsets), _ptr(slot_ids), m_rows, a_row_div, block_m,
         _ptr(out), _dt(out), _rowstride(out), _stream(stream)))
+
+
+def bf8_grouped_gemm_silu_quant(a_q, a_s, w13_q, w13_s, expert_offsets, out_q, out_s, m_rows=None, block_m=0,
+                                stream=None):
+    """Prefill gate/up GEMM with SiLU(gate)*up and the 1x128 fp8 requant in its epilogue.
+    w13_q [E, 2I, K] (gate rows, then up rows), w13_s [E, 2I/128, K/128]; out_q [rows, I] u8, out_s [rows, I/128]."""
+    E, N, K = w13_q.shape
+    if m_rows is None:
+        m_rows = out_q.shape[0]
+    assert w13_q.stride(2) == 1 and w13_s.stride(2) == 1
+    _check("moe_bf8_grouped_gemm_silu_quant", lib().moe_bf8_grouped_gemm_silu_quant(
+        _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
+        _ptr(w13_q), w13_q.stride(0), w13_q.stride(1), _ptr(w13_s), w13_s.stride(0), w13_s.stride(1),
+        E, N // 2, K, _ptr(expert_offsets), m_rows, block_m, _ptr(out_q), _rowstride(out_q),
+        _ptr(out_s), _rowstride(out_s), _stream(stream)))
 
 
 def topk_reduce(y, slot_ids, weights, out, route_rows=None, stream=None):

@@ -19,6 +19,11 @@ int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t
                         const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int64_t E, int64_t N,
                         int64_t K, const int32_t* offsets, int64_t m_rows, void* out, int out_dt,
                         int64_t out_stride);
+int grouped_gemm_silu_quant_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t a_stride,
+                                   const float* a_s, int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
+                                   int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
+                                   int64_t w_s_stride_n, int64_t E, int64_t I, int64_t K, const int32_t* offsets,
+                                   int64_t m_rows, uint8_t* q, int64_t q_stride, float* s, int64_t s_stride);
 int topk_reduce_launch(hipStream_t st, const void* y, int y_dt, int64_t y_stride, const int32_t* slot_ids,
                        const int32_t* route_rows, const float* weights, int64_t T, int64_t topk, int64_t H,
                        uint16_t* out, int64_t out_stride);
@@ -135,6 +140,29 @@ extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const 
     return grouped_gemm_launch(st, bm, a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, w_s,
                                w_s_stride_e, w_s_stride_n, n_experts, N, K, expert_offsets, m_rows, out, out_dt,
                                out_stride);
+}
+
+extern "C" int moe_bf8_grouped_gemm_silu_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s,
+                                               int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
+                                               int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
+                                               int64_t w_s_stride_n, int64_t n_experts, int64_t I, int64_t K,
+                                               const int32_t* expert_offsets, int64_t m_rows, int32_t block_m,
+                                               uint8_t* out_q, int64_t q_stride, float* out_s, int64_t s_stride,
+                                               void* stream) {
+    if (m_rows < 0 || n_experts < 1 || n_experts > 1024 || I < 128 || I % 128 || K < 128 || K % 128 || K > 8192)
+        return MOE_ERR_SHAPE;
+    if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_SHAPE;
+    if (m_rows == 0) return MOE_OK;
+    if (!a_q || !a_s || !w_q || !w_s || !expert_offsets || !out_q || !out_s) return MOE_ERR_NULL;
+    const int64_t kb = K / 128, nb = 2 * I / 128;
+    if (a_stride < K || a_s_stride < kb || w_stride_n < K || w_s_stride_n < kb || q_stride < I || s_stride < I / 128)
+        return MOE_ERR_SHAPE;
+    if (n_experts > 1 && (w_stride_e < 2 * I * w_stride_n || w_s_stride_e < nb * w_s_stride_n)) return MOE_ERR_SHAPE;
+    if (!aligned16(w_q) || !aligned16(a_q) || w_stride_n % 16 || w_stride_e % 16 || a_stride % 16) return MOE_ERR_ALIGN;
+    const int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
+    return grouped_gemm_silu_quant_launch(as_stream(stream), bm, a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e,
+                                          w_stride_n, w_s, w_s_stride_e, w_s_stride_n, n_experts, I, K,
+                                          expert_offsets, m_rows, out_q, q_stride, out_s, s_stride);
 }
 
 extern "C" size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk) {

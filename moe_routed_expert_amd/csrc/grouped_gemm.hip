@@ -38,6 +38,14 @@
 //    tiles meet in that XCD's L2, and every XCD gets the same number of tiles.
 //  * A tile's expert is a binary search of the LDS table; its scales are
 //    loaded row-contiguous, all requests in flight before the LDS stores.
+//  * Fused SiLU-mul requant (the gate/up GEMM of a prefill step with the
+//    activation in its epilogue): a tile covers one 128-column act group; each
+//    wave's two 16-column sub-tiles are gate rows and the matching up rows of
+//    W13, so a lane holds gate and up of the same four columns of one row and
+//    forms h = SiLU(gate)*up from the fp32 accumulators.  The group amax is a
+//    lane shuffle plus an 8-wave LDS max, then s = amax/448 and the codes
+//    e4m3(h/s) leave as one 4-byte store per lane; the [rows][2I] GEMM output
+//    is never written.
 #include "device.h"
 #include "host.h"
 
@@ -62,6 +70,30 @@ template <int BM> struct GgCfg {
     static constexpr int WAVES_PER_EU = BM >= 128 ? 2 : 4;          // occupancy the registers are sized for
 };
 
+// Arguments of one grouped GEMM launch (pointers and strides as in moe_bf8_grouped_gemm).  The fused
+// SiLU-mul requant variant (N = 2I) writes codes q and scales s instead of out.
+struct GgArgs {
+    const uint8_t* a_q;
+    int64_t a_stride;
+    const float* a_s;
+    int64_t a_s_stride;
+    const uint8_t* w_q;
+    int64_t w_stride_e, w_stride_n;
+    const float* w_s;
+    int64_t w_s_stride_e, w_s_stride_n;
+    int n_experts;
+    int64_t N, K;
+    const int32_t* offsets;
+    int m_rows;
+    int n_tiles_n, per_xcd, step_m, step_n;   // tile walk (see the kernel)
+    void* out;
+    int64_t out_stride;
+    uint8_t* q;                               // fused: codes [rows][q_stride], I used
+    int64_t q_stride;
+    float* s;                                 // fused: scales [rows][s_stride], I/128 used
+    int64_t s_stride;
+};
+
 // Exclusive scan of one int per thread over a block of WAVES waves.
 template <int WAVES>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* ldsw) {
@@ -79,17 +111,66 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* ldsw) {
     return base + x - v;
 }
 
-// One BM x 256 tile: rows [row0, min(row0 + BM, row_end)) of expert `expert`, N tile n_tile.  The
-// caller's workgroup runs it with all threads; it leaves LDS free for the next tile (its last LDS
-// read is before its last barrier).
-template <int BM, int OUT_DT>
-__device__ __forceinline__ void grouped_gemm_tile(const uint8_t* __restrict__ a_q, int64_t a_stride,
-                                                  const float* __restrict__ a_s, int64_t a_s_stride,
-                                                  const uint8_t* __restrict__ w_q, int64_t w_stride_e,
-                                                  int64_t w_stride_n, const float* __restrict__ w_s,
-                                                  int64_t w_s_stride_e, int64_t w_s_stride_n, int64_t N, int64_t K,
-                                                  int expert, int row0, int row_end, int n_tile,
-                                                  void* __restrict__ out, int64_t out_stride) {
+// Fused epilogue: acc[m][0] holds gate and acc[m][1] up for row m*16 + lane%16, act columns
+// 128*n_tile + 16*wave + 4*(lane/16) + i.  h = SiLU(gate)*up in fp32; per row, the amax of the 128
+// columns (4 lanes by shuffle, then the 8 waves through LDS), s = amax/448 (correctly rounded), codes
+// e4m3(h/s) (zero codes when s == 0).
+template <int BM>
+__device__ __forceinline__ void act_quant_epilogue(const GgArgs& g, v4f (&acc)[BM / 16][2], int row0, int row_end,
+                                                   int n_tile, int lane, int wave) {
+    using C = GgCfg<BM>;
+    constexpr int MS = BM / 16;
+    __shared__ float amax_lds[C::WAVES][BM];
+#pragma unroll
+    for (int m = 0; m < MS; m++) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float gt = acc[m][0][i], up = acc[m][1][i];
+            acc[m][0][i] = (gt / (1.0f + expf(-gt))) * up;      // h replaces gate
+            a = __builtin_fmaxf(a, __builtin_fabsf(acc[m][0][i]));
+        }
+        a = __builtin_fmaxf(a, __shfl_xor(a, 16, kWave));
+        a = __builtin_fmaxf(a, __shfl_xor(a, 32, kWave));
+        if (lane < 16) amax_lds[wave][m * 16 + lane] = a;
+    }
+    __syncthreads();
+    const bool vec = (g.q_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(g.q) % 4 == 0);
+#pragma unroll
+    for (int m = 0; m < MS; m++) {
+        const int rl = m * 16 + (lane & 15);
+        float amax = amax_lds[0][rl];
+#pragma unroll
+        for (int w = 1; w < C::WAVES; w++) amax = __builtin_fmaxf(amax, amax_lds[w][rl]);
+        const float s = amax / 448.0f;
+        const v4f h = acc[m][0];
+        const uint32_t code = s != 0.0f ? enc4_e4m3(h[0] / s, h[1] / s, h[2] / s, h[3] / s) : 0u;
+        const int row = row0 + rl;
+        if (row < row_end) {
+            uint8_t* q = g.q + (int64_t)row * g.q_stride + (int64_t)n_tile * 128 + 16 * wave + 4 * (lane / 16);
+            if (vec) {
+                *reinterpret_cast<uint32_t*>(q) = code;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; i++) q[i] = (uint8_t)(code >> (8 * i));
+            }
+            if (wave == 0 && lane < 16) g.s[(int64_t)row * g.s_stride + n_tile] = s;
+        }
+    }
+}
+
+// One tile: rows [row0, min(row0 + BM, row_end)) of expert `expert`, N tile n_tile (256 output
+// columns, or act group n_tile when FUSED).  The caller's workgroup runs it with all threads; it
+// leaves LDS free for the next tile (its last LDS read is before its last barrier).
+template <int BM, int OUT_DT, bool FUSED>
+__device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, int row0, int row_end, int n_tile) {
+    const uint8_t* __restrict__ a_q = g.a_q;
+    const float* __restrict__ a_s = g.a_s;
+    const uint8_t* __restrict__ w_q = g.w_q;
+    const float* __restrict__ w_s = g.w_s;
+    const int64_t a_stride = g.a_stride, a_s_stride = g.a_s_stride, w_stride_e = g.w_stride_e;
+    const int64_t w_stride_n = g.w_stride_n, w_s_stride_e = g.w_s_stride_e, w_s_stride_n = g.w_s_stride_n;
+    const int64_t N = g.N, K = g.K;
     using C = GgCfg<BM>;
     constexpr int TPW = C::TPW;
     constexpr int CPW = 16 * TPW;               // columns per wave
@@ -111,15 +192,17 @@ __device__ __forceinline__ void grouped_gemm_tile(const uint8_t* __restrict__ a_
     const int nkb = (int)(K / 128);
     const int64_t n0 = (int64_t)n_tile * C::BN;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const bool cols = n0 + wv * CPW < N;        // a last 256-column tile may hold only 128 columns
+    const bool cols = FUSED || n0 + wv * CPW < N;   // a last 256-column tile may hold only 128 columns
     const int q16 = (lane / 16) * 16;
     // weight fragment pointers: wave owns columns n0 + CPW*wave + [0, CPW), TPW 16-column sub-tiles.
     // The idle waves of a 128-column last tile read valid columns (their results are dropped), so
-    // the loop has no branch around its loads.
-    const int64_t wcol = cols ? n0 + wv * CPW : n0;
+    // the loop has no branch around its loads.  Fused: sub-tile 0 is gate rows 128*n_tile + 16*wave +
+    // [0, 16), sub-tile 1 the matching up rows I + ..., with scale blocks n_tile and I/128 + n_tile.
+    const int64_t I = N / 2;
+    const int64_t wcol = FUSED ? (int64_t)n_tile * 128 + 16 * wv : (cols ? n0 + wv * CPW : n0);
     const uint8_t* wp0 = w_q + (int64_t)expert * w_stride_e + (wcol + (lane & 15)) * w_stride_n + q16;
-    const uint8_t* wp1 = wp0 + 16 * w_stride_n;
-    const int wsb = (int)((wcol - n0) / 128);   // this wave's 128-column scale block within the tile
+    const uint8_t* wp1 = wp0 + (FUSED ? I : 16) * w_stride_n;
+    const int wsb = FUSED ? 0 : (int)((wcol - n0) / 128);   // this wave's 128-column scale block
 
     // All scales of the tile go to LDS once: A scales [kb][row] (wave w reads rows w, w + WAVES, ...,
     // lane = K block, so each request is one contiguous row of scales), weight scales [block][kb]
@@ -137,7 +220,7 @@ __device__ __forceinline__ void grouped_gemm_tile(const uint8_t* __restrict__ a_
     const int64_t nblk = (N - n0) >= 256 ? 2 : 1;
     float ws_v = 0.0f;
     if (wave < 2) {
-        const int64_t b = n0 / 128 + (wave < nblk ? wave : 0);
+        const int64_t b = FUSED ? (wave == 0 ? n_tile : I / 128 + n_tile) : n0 / 128 + (wave < nblk ? wave : 0);
         ws_v = w_s[(int64_t)expert * w_s_stride_e + b * w_s_stride_n + kbl];
     }
     if (lane < nkb) {
@@ -215,7 +298,9 @@ __device__ __forceinline__ void grouped_gemm_tile(const uint8_t* __restrict__ a_
             load_w(kb + S - 1 < last ? kb + S - 1 : last, w_ring[(s + S - 1) % S]);
             const int buf = kb & 1;
             if (kb < nkb) {
-                const float sw = ws_lds[wsb][kb];
+                float sw[TPW];                            // sub-tile c's weight scale (fused: gate, up)
+#pragma unroll
+                for (int c = 0; c < TPW; c++) sw[c] = ws_lds[FUSED ? c : wsb][kb];
                 v8i b[TPW];
 #pragma unroll
                 for (int c = 0; c < TPW; c++)
@@ -226,17 +311,23 @@ __device__ __forceinline__ void grouped_gemm_tile(const uint8_t* __restrict__ a_
                     // share one A row (lane % 16) and take a single scale
                     const v8i a = *reinterpret_cast<const v8i*>(&a_lds[buf][m * 2048 + lane * 32]);
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const float sc = sa_lds[kb * SA_ROW + m * 16 + (lane & 15)] * sw;
+                    const float sa = sa_lds[kb * SA_ROW + m * 16 + (lane & 15)];
 #pragma unroll
-                    for (int c = 0; c < TPW; c++) acc[m][c] += mfma16x16x128_e4m3(b[c], a, zero) * sc;
+                    for (int c = 0; c < TPW; c++) acc[m][c] += mfma16x16x128_e4m3(b[c], a, zero) * (sa * sw[c]);
                 }
             }
             store_a((s + 1) % S, buf ^ 1);            // A step kb+1 (requested a step ago)
             __syncthreads();
         }
     }
+    if constexpr (FUSED) {
+        act_quant_epilogue<BM>(g, acc, row0, row_end, n_tile, lane, wave);
+        return;
+    }
     // ---- epilogue: lane holds row m*16 + lane%16, columns 4*(lane/16) + i of each 16-column sub-tile,
     // stored as one 4-element vector where the output allows it ----
+    void* __restrict__ out = g.out;
+    const int64_t out_stride = g.out_stride;
     const bool vec4 = (out_stride % 4 == 0) &&
                       (reinterpret_cast<uintptr_t>(out) % (OUT_DT == kF32 ? 16 : 8) == 0);
 #pragma unroll
@@ -257,14 +348,12 @@ __device__ __forceinline__ void grouped_gemm_tile(const uint8_t* __restrict__ a_
     }
 }
 
-// Workgroups of one configuration the device holds at once (cached per device and output type).
-template <int BM, int OUT_DT>
+template <int BM, int OUT_DT, bool FUSED>
 __global__ void __launch_bounds__(GgCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(GgCfg<BM>::WAVES_PER_EU, 8)))
-grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const float* __restrict__ a_s,
-                    int64_t a_s_stride, const uint8_t* __restrict__ w_q, int64_t w_stride_e, int64_t w_stride_n,
-                    const float* __restrict__ w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int n_experts,
-                    int64_t N, int64_t K, const int32_t* __restrict__ offsets, int m_rows, int n_tiles_n, int per_xcd,
-                    int step_m, int step_n, void* __restrict__ out, int64_t out_stride) {
+grouped_gemm_kernel(GgArgs g) {
+    const int32_t* __restrict__ offsets = g.offsets;
+    const int n_experts = g.n_experts, m_rows = g.m_rows, n_tiles_n = g.n_tiles_n, per_xcd = g.per_xcd;
+    const int step_m = g.step_m, step_n = g.step_n;
     using C = GgCfg<BM>;
     constexpr int NT = C::THREADS;
     constexpr int E_PER_THREAD = kMaxExpertsScan / NT;
@@ -320,8 +409,7 @@ grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const flo
         const int row0 = __builtin_amdgcn_readfirstlane(off_lds[expert]) +
                          (m_tile - __builtin_amdgcn_readfirstlane(cum_lds[expert])) * BM;
         const int row_end = __builtin_amdgcn_readfirstlane(off_lds[expert + 1]);
-        grouped_gemm_tile<BM, OUT_DT>(a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, w_s, w_s_stride_e,
-                                      w_s_stride_n, N, K, expert, row0, row_end, n_tile, out, out_stride);
+        grouped_gemm_tile<BM, OUT_DT, FUSED>(g, expert, row0, row_end, n_tile);
         m_tile += step_m;
         n_tile += step_n;
         if (n_tile >= n_tiles_n) {
@@ -331,53 +419,61 @@ grouped_gemm_kernel(const uint8_t* __restrict__ a_q, int64_t a_stride, const flo
     }
 }
 
-template <int BM>
-static int gg_resident_blocks(int out_dt) {
+// Workgroups of one configuration the device holds at once (cached per device and variant).
+template <int BM, int OUT_DT, bool FUSED>
+static int gg_resident_blocks() {
     using C = GgCfg<BM>;
-    static int cached[64][3];
+    static int cached[64];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64 || out_dt < 0 || out_dt > 2) return 0;
-    int& c = cached[dev][out_dt];
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int& c = cached[dev];
     if (c == 0) {
         int per_cu = 0, cus = 0;
-        hipError_t e;
-        if (out_dt == MOE_F32)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, kF32>, C::THREADS, 0);
-        else if (out_dt == MOE_BF16)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, kBF16>, C::THREADS, 0);
-        else
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, kF16>, C::THREADS, 0);
-        if (e != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, OUT_DT, FUSED>, C::THREADS,
+                                                         0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
         c = per_cu * cus > 0 ? per_cu * cus : -1;
     }
     return c > 0 ? c : 0;
 }
 
-template <int BM>
-static int launch_grouped_bm(hipStream_t st, int out_dt, const uint8_t* a_q, int64_t a_stride, const float* a_s,
-                             int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
-                             const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int64_t E, int64_t N,
-                             int64_t K, const int32_t* offsets, int64_t m_rows, void* out, int64_t out_stride) {
+// Fills the tile walk of g (N tiles of BN columns, or I/128 act groups when fused) and launches.
+template <int BM, int OUT_DT, bool FUSED>
+static int launch_grouped(hipStream_t st, GgArgs g) {
     using C = GgCfg<BM>;
-    if (N % 128 != 0) return MOE_ERR_SHAPE;
-    const int64_t n_tiles_n = ceil_div(N, C::BN);
-    if (m_rows > 0x7FFFFFFF || n_tiles_n * (ceil_div(m_rows, BM) + E) > 0x7FFFFFFF - (1 << 20)) return MOE_ERR_SHAPE;
-    const int wgs = gg_resident_blocks<BM>(out_dt);
+    if (g.N % 128 != 0 || (FUSED && g.N % 256 != 0)) return MOE_ERR_SHAPE;
+    const int64_t n_tiles_n = FUSED ? g.N / 256 : ceil_div(g.N, C::BN);
+    if (g.m_rows > 0x7FFFFFFF || n_tiles_n * (ceil_div(g.m_rows, BM) + g.n_experts) > 0x7FFFFFFF - (1 << 20))
+        return MOE_ERR_SHAPE;
+    const int wgs = gg_resident_blocks<BM, OUT_DT, FUSED>();
     if (wgs < kXcds) return MOE_ERR_HIP;
-    const int per_xcd = wgs / kXcds;
-    const int step_m = per_xcd / (int)n_tiles_n, step_n = per_xcd % (int)n_tiles_n;
-    dim3 grid((unsigned)(per_xcd * kXcds)), block(C::THREADS);
-#define MOE_GG_ARGS a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, w_s, w_s_stride_e, w_s_stride_n, \
-                    (int)E, N, K, offsets, (int)m_rows, (int)n_tiles_n, per_xcd, step_m, step_n, out, out_stride
-    if (out_dt == MOE_F32)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, kF32>), grid, block, 0, st, MOE_GG_ARGS);
-    else if (out_dt == MOE_BF16)
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, kBF16>), grid, block, 0, st, MOE_GG_ARGS);
-    else
-        hipLaunchKernelGGL((grouped_gemm_kernel<BM, kF16>), grid, block, 0, st, MOE_GG_ARGS);
-#undef MOE_GG_ARGS
+    g.n_tiles_n = (int)n_tiles_n;
+    g.per_xcd = wgs / kXcds;
+    g.step_m = g.per_xcd / g.n_tiles_n;
+    g.step_n = g.per_xcd % g.n_tiles_n;
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, OUT_DT, FUSED>), dim3((unsigned)(g.per_xcd * kXcds)),
+                       dim3(C::THREADS), 0, st, g);
     return launch_status();
+}
+
+template <int BM>
+static int launch_grouped_dt(hipStream_t st, int out_dt, bool fused, const GgArgs& g) {
+    if (fused) return launch_grouped<BM, kF32, true>(st, g);
+    if (out_dt == MOE_F32) return launch_grouped<BM, kF32, false>(st, g);
+    if (out_dt == MOE_BF16) return launch_grouped<BM, kBF16, false>(st, g);
+    return launch_grouped<BM, kF16, false>(st, g);
+}
+
+static int grouped_launch_bm(hipStream_t st, int block_m, int out_dt, bool fused, const GgArgs& g) {
+    if (g.n_experts > kMaxExpertsScan || g.K / 128 > kGgMaxKb) return MOE_ERR_SHAPE;
+    switch (block_m) {
+        case 16: return launch_grouped_dt<16>(st, out_dt, fused, g);
+        case 32: return launch_grouped_dt<32>(st, out_dt, fused, g);
+        case 64: return launch_grouped_dt<64>(st, out_dt, fused, g);
+        case 128: return launch_grouped_dt<128>(st, out_dt, fused, g);
+        default: return MOE_ERR_SHAPE;
+    }
 }
 
 int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t a_stride, const float* a_s,
@@ -385,17 +481,27 @@ int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t
                         const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int64_t E, int64_t N,
                         int64_t K, const int32_t* offsets, int64_t m_rows, void* out, int out_dt,
                         int64_t out_stride) {
-    if (E > kMaxExpertsScan || K / 128 > kGgMaxKb) return MOE_ERR_SHAPE;
-#define MOE_GG_CALL(bm) launch_grouped_bm<bm>(st, out_dt, a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, \
-                                             w_s, w_s_stride_e, w_s_stride_n, E, N, K, offsets, m_rows, out, out_stride)
-    switch (block_m) {
-        case 16: return MOE_GG_CALL(16);
-        case 32: return MOE_GG_CALL(32);
-        case 64: return MOE_GG_CALL(64);
-        case 128: return MOE_GG_CALL(128);
-        default: return MOE_ERR_SHAPE;
-    }
-#undef MOE_GG_CALL
+    GgArgs g{};
+    g.a_q = a_q; g.a_stride = a_stride; g.a_s = a_s; g.a_s_stride = a_s_stride;
+    g.w_q = w_q; g.w_stride_e = w_stride_e; g.w_stride_n = w_stride_n;
+    g.w_s = w_s; g.w_s_stride_e = w_s_stride_e; g.w_s_stride_n = w_s_stride_n;
+    g.n_experts = (int)E; g.N = N; g.K = K; g.offsets = offsets; g.m_rows = (int)m_rows;
+    g.out = out; g.out_stride = out_stride;
+    return grouped_launch_bm(st, block_m, out_dt, false, g);
+}
+
+int grouped_gemm_silu_quant_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t a_stride,
+                                   const float* a_s, int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
+                                   int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
+                                   int64_t w_s_stride_n, int64_t E, int64_t I, int64_t K, const int32_t* offsets,
+                                   int64_t m_rows, uint8_t* q, int64_t q_stride, float* s, int64_t s_stride) {
+    GgArgs g{};
+    g.a_q = a_q; g.a_stride = a_stride; g.a_s = a_s; g.a_s_stride = a_s_stride;
+    g.w_q = w_q; g.w_stride_e = w_stride_e; g.w_stride_n = w_stride_n;
+    g.w_s = w_s; g.w_s_stride_e = w_s_stride_e; g.w_s_stride_n = w_s_stride_n;
+    g.n_experts = (int)E; g.N = 2 * I; g.K = K; g.offsets = offsets; g.m_rows = (int)m_rows;
+    g.q = q; g.q_stride = q_stride; g.s = s; g.s_stride = s_stride;
+    return grouped_launch_bm(st, block_m, MOE_F32, true, g);
 }
 
 }  // namespace moe

@@ -176,3 +176,29 @@ def test_route_prep_workspace_and_checks():
     assert call(a9=None) == m.MOE_ERR_NULL
     assert call(a11=size - 1) == m.MOE_ERR_WORKSPACE
     assert call(a10=P(0x1008)) == m.MOE_ERR_ALIGN
+
+
+def test_fused_gate_up_silu_quant_checks():
+    L = m.lib()
+    args = dict(a_q=FAKE, a_stride=256, a_s=FAKE, a_s_stride=2, w_q=FAKE, w_stride_e=256 * 256, w_stride_n=256,
+                w_s=FAKE, w_s_stride_e=4, w_s_stride_n=2, n_experts=4, I=128, K=256, offsets=FAKE, m_rows=8,
+                block_m=0, q=FAKE, q_stride=128, s=FAKE, s_stride=1, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.moe_bf8_grouped_gemm_silu_quant(*a.values())
+
+    assert call(I=200) == m.MOE_ERR_SHAPE                 # I % 128
+    assert call(K=200) == m.MOE_ERR_SHAPE                 # K % 128
+    assert call(K=8320, a_stride=8320, w_stride_n=8320, w_stride_e=8320 * 256, a_s_stride=65,
+                w_s_stride_n=65, w_s_stride_e=2 * 65) == m.MOE_ERR_SHAPE   # K <= 8192
+    assert call(n_experts=0) == m.MOE_ERR_SHAPE
+    assert call(n_experts=1025) == m.MOE_ERR_SHAPE
+    assert call(block_m=48) == m.MOE_ERR_SHAPE
+    assert call(m_rows=0, q=None, s=None) == m.MOE_OK   # no work, no launch
+    assert call(q=None) == m.MOE_ERR_NULL
+    assert call(offsets=None) == m.MOE_ERR_NULL
+    assert call(q_stride=100) == m.MOE_ERR_SHAPE
+    assert call(w_stride_e=128 * 256) == m.MOE_ERR_SHAPE  # experts overlap: 2I rows of 256 each
+    assert call(w_q=P(0x1008)) == m.MOE_ERR_ALIGN

@@ -172,3 +172,113 @@ def test_grouped_prefill_routes_chain(orc):
     assert np.array_equal(gq_d.cpu().numpy(), gq)
     assert_bf16_close(u16(c1_d), c1, what="prefill c1")
     assert_bf16_close(u16(out), ref, what="prefill out")
+
+
+# ------------------------------------------------- fused SiLU-mul requant ---
+
+def silu_h_bound(c1_ref, c1_bound, I):
+    """|h_gpu - h_oracle| bound from the two sides' fp32 c1 bound: SiLU' lies in [-0.1, 1.1], so
+    |dh| <= 1.1 |dg| (|u| + |du|) + |silu(g)| |du|, plus a few fp32 roundings of h itself."""
+    g, u = c1_ref[:, :I].astype(np.float64), c1_ref[:, I:].astype(np.float64)
+    dg, du = c1_bound[:, :I], c1_bound[:, I:]
+    sg = g / (1 + np.exp(-g))
+    return 1.1 * dg * (np.abs(u) + du) + np.abs(sg) * du + 8 * 2.0 ** -24 * np.abs(sg * u)
+
+
+def check_codes_and_scales(orc, q, s, ref_q, ref_s, h_bound):
+    """Scales within the h bound / 448 of the oracle's.  Each side's dequantized value is within half an
+    e4m3 step of its own h (a step is at most 1/8 of the value, or 2^-9 scale units below the normal
+    range), and the two h are within h_bound of each other, so the dequantized values may differ by
+    h_bound plus both half steps.  Codes rarely differ at all."""
+    groups = ref_s.shape[1]
+    hb = h_bound.reshape(h_bound.shape[0], groups, 128).max(axis=2)
+    assert np.all(np.abs(s.astype(np.float64) - ref_s) <= hb / 448 * 1.01 + 2.0 ** -24 * np.abs(ref_s)), "scales"
+    diff = q != ref_q
+    assert diff.mean() < 1e-2, "codes differ at %.3g of positions" % diff.mean()
+    dec = lambda c: orc.e4m3_decode(c).astype(np.float64)
+    sg = np.repeat(s.astype(np.float64), 128, axis=1)
+    sr = np.repeat(ref_s.astype(np.float64), 128, axis=1)
+    dq, dr = dec(q) * sg, dec(ref_q) * sr
+    allowed = 1.01 * h_bound + 0.0625 * (np.abs(dq) + np.abs(dr)) + 2.0 ** -10 * (sg + sr)
+    bad = np.abs(dq - dr) > allowed
+    assert not bad.any(), "%d dequantized values beyond the bound" % bad.sum()
+
+
+@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128])
+def test_grouped_silu_quant_vs_oracle_and_unfused(orc, bm):
+    """The fused gate/up + SiLU-mul requant equals the oracle's fp32 GEMM followed by its requant (within
+    the derived bound), and the device's own unfused pair (fp32 GEMM, then act_quant) bit for bit."""
+    E, I, K = 5, 256, 640
+    counts = [3, 0, 40, 129, 17]        # empty expert, ragged tails, several M tiles
+    print("fused gate/up silu-quant BM=%d" % bm, flush=True)
+    w_q, w_s, a_q, a_s, offs = grouped_case(E, 2 * I, K, counts, seed=100 + bm)
+    R = int(offs[-1])
+    c1 = orc.block_gemm(a_q.numpy(), a_s.numpy(), w_q.numpy(), w_s.numpy(), mode=orc.MODE_GROUPED,
+                        expert_offsets=offs, out_dtype=np.float32)
+    ref_q, ref_s = orc.silu_mul_quant(c1)
+    d = dev()
+    q = torch.full((R + 2, I), 0xAB, dtype=torch.uint8, device=d)          # 2 spare rows stay untouched
+    s = torch.full((R + 2, I // 128), float("nan"), dtype=torch.float32, device=d)
+    wq, ws, aq, as_, od = w_q.to(d), w_s.to(d), a_q.to(d), a_s.to(d), to_dev(offs)
+    m.bf8_grouped_gemm_silu_quant(aq, as_, wq, ws, od, q, s, m_rows=R + 2, block_m=bm)
+    # the unfused device pair
+    c1_d = torch.empty((R, 2 * I), dtype=torch.float32, device=d)
+    m.bf8_grouped_gemm(aq, as_, wq, ws, c1_d, mode=m.MOE_MODE_GROUPED, expert_offsets=od, block_m=bm)
+    q2 = torch.empty((R, I), dtype=torch.uint8, device=d)
+    s2 = torch.empty((R, I // 128), dtype=torch.float32, device=d)
+    m.act_quant(c1_d, q2, s2, act=m.MOE_ACT_SILU_MUL)
+    torch.cuda.synchronize()
+    hq, hs = q.cpu().numpy(), s.cpu().numpy()
+    assert np.all(hq[R:] == 0xAB) and np.all(np.isnan(hs[R:]))
+    assert np.array_equal(hq[:R], q2.cpu().numpy()) and np.array_equal(hs[:R].view(np.uint32),
+                                                                      s2.cpu().numpy().view(np.uint32))
+    experts = np.repeat(np.arange(E), np.diff(offs))
+    c1_bound = gemm_abs_bound(a_q.numpy(), a_s.numpy(), w_q.numpy(), w_s.numpy(), experts, np.arange(R))
+    check_codes_and_scales(orc, hq[:R], hs[:R], ref_q, ref_s, silu_h_bound(c1, c1_bound, I))
+
+
+def test_grouped_silu_quant_zero_rows():
+    """Rows whose activation is all zero (an inactive route's tile) give zero codes and +0 scales."""
+    E, I, K = 2, 128, 256
+    w_q, w_s, a_q, a_s, offs = grouped_case(E, 2 * I, K, [5, 7], seed=9)
+    a_q[3] = 0
+    a_s[3] = 0
+    d = dev()
+    q = torch.full((12, I), 0xAB, dtype=torch.uint8, device=d)
+    s = torch.full((12, 1), float("nan"), dtype=torch.float32, device=d)
+    m.bf8_grouped_gemm_silu_quant(a_q.to(d), a_s.to(d), w_q.to(d), w_s.to(d), to_dev(offs), q, s)
+    torch.cuda.synchronize()
+    assert np.all(q.cpu().numpy()[3] == 0) and s.cpu().numpy()[3, 0] == 0.0 and not np.signbit(s.cpu().numpy()[3, 0])
+
+
+def test_grouped_silu_quant_full_prefill_size(orc):
+    """At the 24576-route prefill size (E=256, top-6, H=4096, I=1024) in the picker's launch: fused equals the
+    unfused device pair bit for bit, and one sampled expert's rows match the oracle."""
+    E, topk, H, I, T = 256, 6, 4096, 1024, 4096
+    print("fused gate/up silu-quant at 24576 routes", flush=True)
+    d = dev()
+    w_q, w_s = wl.block_fp8_weights(E, 2 * I, H, 21, device=d, chunk_experts=32)
+    rt = wl.prefill_routes(T, E, topk, seed=9)
+    R = T * topk
+    od = to_dev(rt.expert_offsets)
+    a_q, a_s = wl.fp8_rows(R, H, seed=23, device=d)
+    q = torch.empty((R, I), dtype=torch.uint8, device=d)
+    s = torch.empty((R, I // 128), dtype=torch.float32, device=d)
+    m.bf8_grouped_gemm_silu_quant(a_q, a_s, w_q, w_s, od, q, s)
+    c1_d = torch.empty((R, 2 * I), dtype=torch.float32, device=d)
+    m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c1_d, mode=m.MOE_MODE_GROUPED, expert_offsets=od)
+    q2 = torch.empty_like(q)
+    s2 = torch.empty_like(s)
+    m.act_quant(c1_d, q2, s2, act=m.MOE_ACT_SILU_MUL)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(s.view(torch.int32), s2.view(torch.int32))
+    e = 77
+    r0, r1 = int(rt.expert_offsets[e]), int(rt.expert_offsets[e + 1])
+    wq_e, ws_e = w_q[e:e + 1].cpu().numpy(), w_s[e:e + 1].cpu().numpy()
+    aq_e, as_e = a_q[r0:r1].cpu().numpy(), a_s[r0:r1].cpu().numpy()
+    offs_e = np.array([0, r1 - r0], np.int32)
+    c1 = orc.block_gemm(aq_e, as_e, wq_e, ws_e, mode=orc.MODE_GROUPED, expert_offsets=offs_e, out_dtype=np.float32)
+    ref_q, ref_s = orc.silu_mul_quant(c1)
+    bound = gemm_abs_bound(aq_e, as_e, wq_e, ws_e, np.zeros(r1 - r0, np.int64), np.arange(r1 - r0))
+    check_codes_and_scales(orc, q[r0:r1].cpu().numpy(), s[r0:r1].cpu().numpy(), ref_q, ref_s,
+                           silu_h_bound(c1, bound, I))
