@@ -266,6 +266,56 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
 
 
+def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
+    """One whole prefill layer on the device from router logits: routing prep, input quant, gather,
+    fused gate/up + SiLU-mul requant, down GEMM, top-k reduce (timed per layer with events)."""
+    dev = torch.device("cuda")
+    (w13_q, w13_s), (w2_q, w2_s) = weights
+    R = T * topk
+    # iid N(0,1) logits: each token's top-k is a uniform draw of distinct experts, as in the GEMM lines
+    lg = torch.from_numpy(wl.router_logits(T, E, seed=41, skew=0.0)).to(dev)
+    x = wl.bf16_normal((T, H), seed=42, device=dev)
+    ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    w = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    d2s = torch.empty(R, dtype=torch.int32, device=dev)
+    rr = torch.empty(R, dtype=torch.int32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ws_size = m.lib().moe_route_prep_workspace_size(T, E)
+    ws = torch.empty(ws_size, dtype=torch.uint8, device=dev)
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+    gq = torch.empty((R, H), dtype=torch.uint8, device=dev)
+    gs = torch.empty((R, H // 128), dtype=torch.float32, device=dev)
+    aq = torch.empty((R, I), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
+    c2 = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def layer():
+        st = torch.cuda.current_stream().cuda_stream
+        rc = m.lib().moe_route_prep(lg.data_ptr(), E, T, E, topk, ids.data_ptr(), w.data_ptr(), d2s.data_ptr(),
+                                    rr.data_ptr(), offs.data_ptr(), ws.data_ptr(), ws_size, st)
+        assert rc == 0, rc
+        m.act_quant(x, xq, xs)
+        m.gather_rows_scales(xq, xs, d2s, gq, gs)
+        m.bf8_grouped_gemm_silu_quant(gq, gs, w13_q, w13_s, offs, aq, as_, block_m=m.pick_block_m(R, E))
+        m.bf8_grouped_gemm(aq, as_, w2_q, w2_s, c2, mode=m.MOE_MODE_GROUPED, expert_offsets=offs,
+                           block_m=m.pick_block_m(R, E))
+        m.topk_reduce(c2, ids, w, out, route_rows=rr)
+
+    for _ in range(2):
+        layer()
+    t = Timer(torch)
+    for _ in range(steps):
+        t.start()
+        layer()
+        t.stop()
+    us = statistics.median(t.us())
+    flops = 2.0 * R * (2 * I * H + H * I)
+    return dict(tokens=T, routes=R, experts=E, topk=topk, H=H, I=I, us_per_layer=us,
+                gemm_tflops=flops / (us * 1e-6) / 1e12, routing="uniform (iid N(0,1) logits)")
+
+
 def prefill_all(torch, m, wl):
     """The grouped GEMMs at 1536, 6144 and 24576 routes (E=256, top-6, H=4096, I=1024)."""
     weights = prefill_weights(torch, wl, 256, 4096, 1024)
@@ -273,6 +323,7 @@ def prefill_all(torch, m, wl):
     for T in (256, 1024, 4096):
         log("prefill %d routes" % (T * 6))
         res.append(prefill_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights))
+        res[-1]["layer"] = prefill_layer_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights)
     del weights
     torch.cuda.empty_cache()
     return res

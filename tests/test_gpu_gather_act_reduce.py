@@ -135,18 +135,41 @@ def test_act_quant_silu_mul_within_one_step(orc, dtype, rows, n):
 
 # ------------------------------------------------------------------ reduce ---
 
-@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16])
-def test_topk_reduce(orc, ydt):
-    rng = np.random.default_rng(5)
-    T, topk, H = 6, 8, 2048
+def assert_reduce_bound(got, ref, y, slots, w, rr):
+    """Both sides sum the active routes in ascending order in fp32 (the device may fuse each multiply-add),
+    so each fp32 sum is within (topk + 1) * 2^-24 * sum|w*y| of the exact one; one bf16 rounding each adds
+    half a bf16 ulp of the result."""
+    from gpu_util import bf16_bits_to_f64
+    T, topk = slots.shape
+    rows = np.arange(T * topk).reshape(T, topk) if rr is None else rr
+    act = (slots >= 0).astype(np.float64)
+    wa = np.where(slots >= 0, np.nan_to_num(w.astype(np.float64)), 0.0)
+    S = np.einsum("tj,tjh->th", np.abs(wa) * act, np.abs(y.astype(np.float64)[rows]))
+    g, r = bf16_bits_to_f64(got), bf16_bits_to_f64(ref)
+    mag = np.maximum(np.abs(g), np.abs(r))
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 2.0 ** -133)
+    bound = 2 * (topk + 1) * 2.0 ** -24 * S + ulp
+    assert np.all(np.abs(g - r) <= bound), "reduce beyond its fp32 + bf16 rounding bound"
+
+
+@pytest.mark.parametrize("ydt", [torch.float32, torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("H,topk", [(2048, 8), (100, 6), (4096, 6), (24, 11)])
+def test_topk_reduce(orc, ydt, H, topk):
+    """8-column vector path (H % 8 == 0) and the 4-column path (H = 100); topk above one 8-route pass."""
+    print("topk_reduce %s H=%d topk=%d" % (ydt, H, topk), flush=True)
+    rng = np.random.default_rng(5 + H + topk)
+    T = 6
     y = torch.from_numpy(rng.standard_normal((T * topk, H)).astype(np.float32)).to(ydt)
     slots = rng.integers(0, 64, size=(T, topk)).astype(np.int32)
     slots[1, [0, 3, 5]] = -1
     slots[2, :] = -1
+    slots[3, topk - 1] = -1
     w = rng.random((T, topk)).astype(np.float32)
     w[slots < 0] = np.nan                                     # never read
     perm = rng.permutation(T * topk).astype(np.int32).reshape(T, topk)
     host_y = y.view(torch.int16).numpy().view(np.uint16) if ydt == torch.bfloat16 else y.numpy()
+    if ydt == torch.float16:
+        host_y = y.numpy()
     for rr in (None, perm):
         ref = orc.topk_reduce(host_y, slots, w, route_rows=rr)
         out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=dev())
@@ -155,5 +178,20 @@ def test_topk_reduce(orc, ydt):
         got = u16(out)
         assert np.all(got[2] == 0)
         assert_bf16_close(got, ref, what="topk_reduce")
-        # fp32 sums in the same order: at most one bf16 ulp apart
-        assert np.abs(got.astype(np.int64) - ref.astype(np.int64)).max() <= 1
+        assert_reduce_bound(got, ref, y.float().numpy(), slots, w, rr)
+
+
+def test_topk_reduce_strided_rows_take_the_4_column_path(orc):
+    """y rows with a stride that breaks 16-byte alignment of every row: the 4-column path, same results."""
+    rng = np.random.default_rng(11)
+    T, topk, H = 5, 6, 64
+    ypad = torch.from_numpy(rng.standard_normal((T * topk, H + 4)).astype(np.float32)).to(torch.bfloat16)
+    y = ypad[:, :H]
+    slots = rng.integers(0, 8, size=(T, topk)).astype(np.int32)
+    w = rng.random((T, topk)).astype(np.float32)
+    ref = orc.topk_reduce(np.ascontiguousarray(y.view(torch.int16).numpy()).view(np.uint16), slots, w)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev())
+    m.topk_reduce(ypad.to(dev())[:, :H], to_dev(slots), to_dev(w), out)
+    torch.cuda.synchronize()
+    got = u16(out)
+    assert_reduce_bound(got, ref, y.float().numpy(), slots, w, None)

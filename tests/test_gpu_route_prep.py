@@ -99,3 +99,45 @@ def test_route_prep_feeds_the_gather_and_reduce_maps(orc):
         seg = slice(offs[e], offs[e + 1])
         assert np.all(row_e[seg] == e)
         assert np.all(np.diff(got["dst2src"][seg]) > 0)
+
+
+def test_prefill_layer_on_device_from_logits(orc):
+    """Routing prep -> input quant -> gather -> fused gate/up + SiLU-mul requant -> down -> top-k reduce,
+    every step on the device, against the oracle's chain on the same logits, activations and weights."""
+    from gpu_util import assert_bf16_close, u16
+    T, E, topk, H, I = 200, 16, 4, 512, 256
+    lg = wl.router_logits(T, E, seed=3, skew=1.0)
+    x = wl.bf16_normal((T, H), seed=4)
+    w13_q, w13_s = wl.block_fp8_weights(E, 2 * I, H, seed=5)
+    w2_q, w2_s = wl.block_fp8_weights(E, H, I, seed=6)
+    # oracle chain (c1 in fp32, as the fused step keeps it)
+    r = orc.route_prep(lg, topk)
+    xq, xs = orc.quant_groups(x.view(torch.int16).numpy().view(np.uint16))
+    gq, gs = orc.gather_rows_scales(xq, xs, r["dst2src"])
+    c1 = orc.block_gemm(gq, gs, w13_q.numpy(), w13_s.numpy(), mode=orc.MODE_GROUPED,
+                        expert_offsets=r["expert_offsets"], out_dtype=np.float32)
+    aq, as_ = orc.silu_mul_quant(c1)
+    c2 = orc.block_gemm(aq, as_, w2_q.numpy(), w2_s.numpy(), mode=orc.MODE_GROUPED,
+                        expert_offsets=r["expert_offsets"], out_dtype=np.uint16)
+    ref = orc.topk_reduce(c2, r["expert_ids"], r["weights"], route_rows=r["route_rows"])
+    # device chain
+    d = dev()
+    R = T * topk
+    ids, w, d2s, rr, offs = m.route_prep(to_dev(lg), topk)
+    xq_d = torch.empty((T, H), dtype=torch.uint8, device=d)
+    xs_d = torch.empty((T, H // 128), dtype=torch.float32, device=d)
+    m.act_quant(x.to(d), xq_d, xs_d)
+    gq_d = torch.empty((R, H), dtype=torch.uint8, device=d)
+    gs_d = torch.empty((R, H // 128), dtype=torch.float32, device=d)
+    m.gather_rows_scales(xq_d, xs_d, d2s, gq_d, gs_d)
+    aq_d = torch.empty((R, I), dtype=torch.uint8, device=d)
+    as_d = torch.empty((R, I // 128), dtype=torch.float32, device=d)
+    m.bf8_grouped_gemm_silu_quant(gq_d, gs_d, w13_q.to(d), w13_s.to(d), offs, aq_d, as_d)
+    c2_d = torch.empty((R, H), dtype=torch.bfloat16, device=d)
+    m.bf8_grouped_gemm(aq_d, as_d, w2_q.to(d), w2_s.to(d), c2_d, mode=m.MOE_MODE_GROUPED, expert_offsets=offs)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
+    m.topk_reduce(c2_d, ids, w, out, route_rows=rr)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), r["expert_ids"]) and np.array_equal(d2s.cpu().numpy(), r["dst2src"])
+    assert np.array_equal(gq_d.cpu().numpy(), gq)
+    assert_bf16_close(u16(out), ref, what="prefill layer out")
