@@ -58,12 +58,13 @@ def lib():
         L.orc_block_gemm.argtypes = [P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64,
                                      I32, P, P, I64, I64, P, I32, I64]
         L.orc_silu_mul_quant.argtypes = [P, I32, I64, I64, I64, P, I64, P, I64]
+        L.orc_gated_act_quant.argtypes = [P, I32, I64, I64, I64, I32, P, I64, P, I64]
         L.orc_topk_reduce.argtypes = [P, I32, I64, P, P, P, I64, I64, I64, P, I64]
         L.orc_route_prep.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P]
-        L.orc_fused_decode.argtypes = [P, I64, I64, I64, I64, P, P, I64, P, P, P, P, P,
+        L.orc_fused_decode.argtypes = [P, I64, I64, I64, I64, I32, P, P, I64, P, P, P, P, P,
                                        P, P, P, P, P, P]
         for name in ("orc_quant_groups", "orc_gather_rows_scales", "orc_block_gemm",
-                     "orc_silu_mul_quant", "orc_topk_reduce", "orc_fused_decode"):
+                     "orc_silu_mul_quant", "orc_gated_act_quant", "orc_topk_reduce", "orc_fused_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,6 +190,22 @@ def block_gemm(a_q, a_s, w_q, w_s, *, mode, out_dtype=np.float32, expert_offsets
 
 # ---- O4 ---------------------------------------------------------------------
 
+# gated activations of O4 (the five GLU variants; values as in the C header)
+ACT_SILU_MUL, ACT_GELU_MUL, ACT_RELU_MUL, ACT_SIGMOID_MUL, ACT_MUL = 1, 2, 3, 4, 5
+
+
+def gated_act_quant(c1: np.ndarray, act: int):
+    """c1: [rows, 2n] (float32, float16 or bf16 bits), gate then up -> (q [rows, n], s [rows, ceil(n/128)])."""
+    c1 = np.ascontiguousarray(c1)
+    rows, n2 = c1.shape
+    n = n2 // 2
+    g = (n + 127) // 128
+    q = np.empty((rows, n), np.uint8)
+    s = np.empty((rows, g), np.float32)
+    _check(lib().orc_gated_act_quant(_p(c1), _dt_code(c1.dtype), n2, rows, n, act, _p(q), n, _p(s), g))
+    return q, s
+
+
 def silu_mul_quant(c1: np.ndarray):
     """c1: [rows, 2n] (float32, float16 or bf16 bits) -> (q [rows, n], s [rows, ceil(n/128)])."""
     c1 = np.ascontiguousarray(c1)
@@ -219,7 +236,7 @@ def topk_reduce(y: np.ndarray, slot_ids: np.ndarray, weights: np.ndarray, route_
 
 # ---- O6 ---------------------------------------------------------------------
 
-def fused_decode(x_bf16, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, intermediates=False):
+def fused_decode(x_bf16, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, intermediates=False, act=ACT_SILU_MUL):
     """x_bf16: [T, H] uint16 bits; slot_ids/weights: [T, topk]; W13 [S, 2I, H], W2 [S, H, I].
 
     Returns out bf16 bits [T, H] (and a dict of intermediates if asked)."""
@@ -243,7 +260,7 @@ def fused_decode(x_bf16, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, intermedia
                   c1=np.empty((R, 2 * I), np.float32), aq=np.empty((R, I), np.uint8),
                   as_=np.empty((R, (I + 127) // 128), np.float32), c2=np.empty((R, H), np.float32))
     g = (lambda k: _p(im[k])) if im else (lambda k: None)
-    _check(lib().orc_fused_decode(_p(x_bf16), T, H, I, topk, _p(slot_ids), _p(weights), S,
+    _check(lib().orc_fused_decode(_p(x_bf16), T, H, I, topk, act, _p(slot_ids), _p(weights), S,
                                   _p(w13_q), _p(w13_s), _p(w2_q), _p(w2_s), _p(out),
                                   g("xq"), g("xs"), g("c1"), g("aq"), g("as_"), g("c2")))
     return (out, im) if intermediates else out

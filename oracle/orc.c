@@ -277,24 +277,50 @@ int orc_block_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64
 /* O4                                                                 */
 /* ------------------------------------------------------------------ */
 
-int orc_silu_mul_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, int64_t n,
-                       uint8_t* q, int64_t q_stride, float* s, int64_t s_stride) {
+/* The gated activations, each one fp32 expression in this order of operations: the five GLU variants
+ * (GLU, bilinear, ReGLU, GEGLU, SwiGLU of "GLU Variants Improve Transformer"), gate g and up u. */
+static float gated_act(int act, float g, float u) {
+    switch (act) {
+        case ORC_ACT_SILU_MUL: {        /* Swish_1(g) * u = g * sigmoid(g) * u */
+            float den = 1.0f + expf(-g);
+            return (g / den) * u;
+        }
+        case ORC_ACT_GELU_MUL: {        /* GELU(g) * u = g * Phi(g) * u, Phi via erf */
+            float phi = 0.5f * (1.0f + erff(g * 0.70710678118654752f));
+            return (g * phi) * u;
+        }
+        case ORC_ACT_RELU_MUL:          /* max(g, 0) * u, with +0 for g <= 0 */
+            return (g > 0.0f ? g : 0.0f) * u;
+        case ORC_ACT_SIGMOID_MUL: {     /* sigmoid(g) * u */
+            float den = 1.0f + expf(-g);
+            return (1.0f / den) * u;
+        }
+        default:                        /* ORC_ACT_MUL: g * u */
+            return g * u;
+    }
+}
+
+int orc_gated_act_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, int64_t n, int act,
+                        uint8_t* q, int64_t q_stride, float* s, int64_t s_stride) {
     float* h;
-    if (rows < 0 || n < 0 || !dt_ok(in_dt)) return -2;
+    if (rows < 0 || n < 0 || !dt_ok(in_dt) || act < ORC_ACT_SILU_MUL || act > ORC_ACT_MUL) return -2;
     if (rows == 0 || n == 0) return 0;
     h = (float*)malloc((size_t)n * sizeof(float));
     for (int64_t r = 0; r < rows; r++) {
         for (int64_t c = 0; c < n; c++) {
             float g = load_elem(in, in_dt, r * in_stride + c);
             float u = load_elem(in, in_dt, r * in_stride + n + c);
-            float sig_den = 1.0f + expf(-g);
-            float silu = g / sig_den;
-            h[c] = silu * u;
+            h[c] = gated_act(act, g, u);
         }
         quant_row(h, n, q + r * q_stride, s + r * s_stride);
     }
     free(h);
     return 0;
+}
+
+int orc_silu_mul_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, int64_t n,
+                       uint8_t* q, int64_t q_stride, float* s, int64_t s_stride) {
+    return orc_gated_act_quant(in, in_dt, in_stride, rows, n, ORC_ACT_SILU_MUL, q, q_stride, s, s_stride);
 }
 
 /* ------------------------------------------------------------------ */
@@ -327,7 +353,7 @@ int orc_topk_reduce(const void* y, int y_dt, int64_t y_stride,
 /* O6                                                                 */
 /* ------------------------------------------------------------------ */
 
-int orc_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk,
+int orc_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk, int act,
                      const int32_t* slot_ids, const float* weights, int64_t n_slots,
                      const uint8_t* w13_q, const float* w13_s,
                      const uint8_t* w2_q, const float* w2_s,
@@ -349,7 +375,7 @@ int orc_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, in
     if (!rc) rc = orc_block_gemm(xq, H, xs, gH, w13_q, 2 * I * H, H, w13_s, g2I * gH, gH,
                                  n_slots, 2 * I, H, ORC_MODE_SLOT, NULL, slot_ids, R, topk,
                                  c1, ORC_F32, 2 * I);
-    if (!rc) rc = orc_silu_mul_quant(c1, ORC_F32, 2 * I, R, I, aq, I, as, gI);
+    if (!rc) rc = orc_gated_act_quant(c1, ORC_F32, 2 * I, R, I, act, aq, I, as, gI);
     if (!rc) rc = orc_block_gemm(aq, I, as, gI, w2_q, H * I, I, w2_s, gH * gI, gI,
                                  n_slots, H, I, ORC_MODE_SLOT, NULL, slot_ids, R, 1,
                                  c2, ORC_F32, H);

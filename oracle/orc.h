@@ -82,8 +82,18 @@ int orc_block_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64
                    void* out, int out_dt, int64_t out_stride);
 
 /* ---- O4: gated activation + requant ----
- * in: rows x 2n (gate = columns [0,n), up = columns [n,2n)) of type in_dt.
- * h = (g / (1 + expf(-g))) * u in fp32, then O1 on h. */
+ * in: rows x 2n (gate g = columns [0,n), up u = columns [n,2n)) of type in_dt.  h in fp32, then O1
+ * on h.  The activations are the five GLU variants ("GLU Variants Improve Transformer", the gated
+ * linear units with sigmoid, identity, ReLU, GELU and Swish_1 gates); the pages name "five
+ * activations" without listing them:
+ *   SILU_MUL    h = (g / (1 + expf(-g))) * u          (SwiGLU)
+ *   GELU_MUL    h = (g * (0.5 * (1 + erff(g * 1/sqrt2)))) * u   (GEGLU, exact GELU)
+ *   RELU_MUL    h = (g > 0 ? g : +0) * u              (ReGLU)
+ *   SIGMOID_MUL h = (1 / (1 + expf(-g))) * u          (GLU)
+ *   MUL         h = g * u                             (bilinear) */
+enum { ORC_ACT_SILU_MUL = 1, ORC_ACT_GELU_MUL = 2, ORC_ACT_RELU_MUL = 3, ORC_ACT_SIGMOID_MUL = 4, ORC_ACT_MUL = 5 };
+int orc_gated_act_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, int64_t n, int act,
+                        uint8_t* q, int64_t q_stride, float* s, int64_t s_stride);
 int orc_silu_mul_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, int64_t n,
                        uint8_t* q, int64_t q_stride, float* s, int64_t s_stride);
 
@@ -95,13 +105,13 @@ int orc_topk_reduce(const void* y, int y_dt, int64_t y_stride,
                     const int32_t* slot_ids, const int32_t* route_rows, const float* weights,
                     int64_t T, int64_t topk, int64_t H, uint16_t* out_bf16, int64_t out_stride);
 
-/* ---- O6: fused decode = O1(x) -> O3 slot(W13, fp32) -> O4 -> O3 slot(W2, fp32) -> O5 ----
+/* ---- O6: fused decode = O1(x) -> O3 slot(W13, fp32) -> O4 (act) -> O3 slot(W2, fp32) -> O5 ----
  * x: T x H bf16; slots/weights: T x topk; W13 [n_slots][2I][H], W2 [n_slots][H][I] (contiguous),
  * scales [n_slots][2I/128][H/128] and [n_slots][H/128][I/128] (contiguous).
  * Optional outputs of the intermediates (NULL to skip):
  *   xq [T][H], xs [T][ceil(H/128)], c1 [T*topk][2I] f32, aq [T*topk][I], as [T*topk][ceil(I/128)],
  *   c2 [T*topk][H] f32. */
-int orc_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk,
+int orc_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk, int act,
                      const int32_t* slot_ids, const float* weights, int64_t n_slots,
                      const uint8_t* w13_q, const float* w13_s,
                      const uint8_t* w2_q, const float* w2_s,

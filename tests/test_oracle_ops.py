@@ -233,6 +233,84 @@ def test_silu_mul_quant_of_zero_tile_is_zero(orc):
     assert np.all(q == 0) and np.all(s.view(np.uint32) == 0)
 
 
+def _act64(act, g, u):
+    """The five GLU variants in float64 from independent library routines."""
+    from scipy.special import erf, expit
+    if act == 1:
+        return g * expit(g) * u                          # Swish_1(g) * u
+    if act == 2:
+        return g * 0.5 * (1.0 + erf(g / np.sqrt(2.0))) * u   # GELU(g) * u, GELU = x Phi(x)
+    if act == 3:
+        return np.maximum(g, 0.0) * u
+    if act == 4:
+        return expit(g) * u
+    return g * u
+
+
+@pytest.mark.parametrize("act", [1, 2, 3, 4, 5])
+def test_gated_act_quant_vs_float64(orc, act):
+    """Each gated activation against its float64 definition: every dequantized value within half an e4m3
+    step of the float64 h, codes equal to torch's cast of the float64 h except near rounding midpoints,
+    and gate/up not swapped."""
+    rng = np.random.default_rng(70 + act)
+    rows, n = 12, 512
+    c1 = (rng.standard_normal((rows, 2 * n)) * 3).astype(np.float32)
+    q, s = orc.gated_act_quant(c1, act)
+    g64, u64 = c1[:, :n].astype(np.float64), c1[:, n:].astype(np.float64)
+    h64 = _act64(act, g64, u64)
+    sc = np.repeat(s, 128, axis=1).astype(np.float64)
+    deq = t_dec(q).astype(np.float64) * sc
+    bound = np.maximum(np.abs(h64) * 2.0 ** -4, 2.0 ** -10 * sc) * (1 + 1e-4) + 1e-6 * sc
+    assert np.all(np.abs(deq - h64) <= bound)
+    s64 = (np.abs(h64).reshape(rows, -1, 128).max(axis=2) / 448.0).astype(np.float32)
+    want = t_enc((h64 / np.repeat(s64, 128, axis=1)).astype(np.float32))
+    assert np.mean(want != q) < 1e-3
+    if act != 5:                                 # g * u is symmetric in gate and up
+        h_sw = _act64(act, u64, g64)
+        assert np.abs(deq - h_sw).max() > 10 * np.abs(deq - h64).max()
+    z = orc.gated_act_quant(np.zeros((2, 256), np.float32), act)
+    assert np.all(z[0] == 0) and np.all(z[1].view(np.uint32) == 0)
+
+
+@pytest.mark.parametrize("act", [3, 5])
+def test_relu_and_bilinear_are_exact_products(orc, act):
+    """ReGLU and bilinear form h with one exact-rounded fp32 product, so the codes and scales equal O1's
+    definition applied to numpy's fp32 product bit for bit (a non-positive gate gives +0, and +0 times a
+    negative up is -0, code 0x80)."""
+    rng = np.random.default_rng(80 + act)
+    rows, n = 6, 384
+    c1 = (rng.standard_normal((rows, 2 * n)) * 2).astype(np.float32)
+    c1[0, :n] = -np.abs(c1[0, :n])              # row 0: every gate <= 0 ...
+    c1[0, 5] = 1.5                               # ... but one
+    q, s = orc.gated_act_quant(c1, act)
+    g, u = c1[:, :n], c1[:, n:]
+    h = (np.where(g > 0, g, np.float32(0)) * u if act == 3 else g * u).astype(np.float32)
+    s_want = (np.abs(h).reshape(rows, -1, 128).max(axis=2) / np.float32(448)).astype(np.float32)
+    assert np.array_equal(s.view(np.uint32), s_want.view(np.uint32))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        v = h / np.repeat(s_want, 128, axis=1)
+    v = np.where(np.repeat(s_want, 128, axis=1) == 0, 0, v).astype(np.float32)
+    assert np.array_equal(q, t_enc(v))
+    if act == 3:
+        # group 0 of row 0 holds the one positive gate, so its scale is nonzero and the zeros keep their
+        # sign; groups 1 and 2 are all zero (s = 0) and give 0x00 codes whatever the sign
+        c = np.arange(128)
+        neg_u = (u[0, :128] < 0) & (c != 5)
+        assert np.all(q[0, :128][neg_u] == 0x80) and np.all(q[0, :128][~neg_u & (c != 5)] == 0x00)
+        assert np.all(q[0, 128:] == 0) and np.all(s[0, 1:] == 0)
+
+
+def test_gelu_gate_closed_form(orc):
+    """GELU(x) - GELU(-x) = x: with up = 1, the GEGLU rows of x and -x dequantize to values whose
+    difference is x within the two rows' half steps."""
+    x = np.linspace(-6, 6, 256).astype(np.float32)
+    c1 = np.stack([np.concatenate([x, np.ones_like(x)]), np.concatenate([-x, np.ones_like(x)])])
+    q, s = orc.gated_act_quant(c1, 2)
+    d = t_dec(q).astype(np.float64) * np.repeat(s, 128, axis=1)
+    step = np.maximum(np.abs(d) * 2.0 ** -4, 2.0 ** -10 * np.repeat(s, 128, axis=1))
+    assert np.all(np.abs((d[0] - d[1]) - x) <= step[0] + step[1] + 1e-6)
+
+
 # ---------------------------------------------------------------- O5 -------
 
 def test_topk_reduce_one_hot_all_inactive_and_float64(orc):
@@ -277,11 +355,13 @@ def _case(H=256, I=128, topk=2, n_slots=8, active=1, seed=0, T=1, tail=False):
                c.w2_q.numpy(), c.w2_s.numpy())
 
 
-def test_fused_decode_vs_float64_layer(orc):
-    """Whole layer in float64 from dequantized operands; only the two quantization points
-    (x and the activation) are kept, done with numpy division and torch's fp8 cast."""
+@pytest.mark.parametrize("act", [1, 2, 3, 4, 5])
+def test_fused_decode_vs_float64_layer(orc, act):
+    """Whole layer in float64 from dequantized operands, for each gated activation; only the two
+    quantization points (x and the activation) are kept, done with numpy division and torch's fp8
+    cast."""
     c, args = _case(H=512, I=256, topk=4, n_slots=6, active=3, seed=3, T=2)
-    out = orc.fused_decode(*args)
+    out = orc.fused_decode(*args, act=act)
     x = c.x.to(torch.float32).numpy()
     xs = (np.abs(x).reshape(c.T, -1, 128).max(2) / np.float32(448)).astype(np.float32)
     xq = t_enc(x / np.repeat(xs, 128, axis=1))
@@ -296,7 +376,7 @@ def test_fused_decode_vs_float64_layer(orc):
                 continue
             h = W13[sl] @ X[t]
             g, u = h[:c.I], h[c.I:]
-            a = g / (1 + np.exp(-g)) * u
+            a = _act64(act, g, u)
             a_s = (np.abs(a).reshape(-1, 128).max(1) / 448.0).astype(np.float32)
             aq = t_enc((a / np.repeat(a_s, 128)).astype(np.float32))
             A = t_dec(aq).astype(np.float64) * np.repeat(a_s, 128)
