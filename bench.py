@@ -247,11 +247,11 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     aq = torch.empty((R, I), dtype=torch.uint8, device=dev)
     as_ = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
     for _ in range(3):
-        m.bf8_grouped_gemm_silu_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_)
+        m.bf8_grouped_gemm_act_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_)
     t = Timer(torch)
     for _ in range(steps):
         t.start()
-        m.bf8_grouped_gemm_silu_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_)
+        m.bf8_grouped_gemm_act_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_)
         t.stop()
     us_f = statistics.median(t.us())
     t = Timer(torch)
@@ -261,7 +261,7 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
         t.stop()
     us_a = statistics.median(t.us())
     flops = 2.0 * R * 2 * I * H
-    out["gate_up_silu_quant"] = dict(us_median=us_f, tflops=flops / (us_f * 1e-6) / 1e12,
+    out["gate_up_act_quant"] = dict(us_median=us_f, tflops=flops / (us_f * 1e-6) / 1e12,
                                      unfused_us=out["gate_up"]["us_median"] + us_a, act_quant_us=us_a)
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
 
@@ -298,7 +298,7 @@ def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
         assert rc == 0, rc
         m.act_quant(x, xq, xs)
         m.gather_rows_scales(xq, xs, d2s, gq, gs)
-        m.bf8_grouped_gemm_silu_quant(gq, gs, w13_q, w13_s, offs, aq, as_, block_m=m.pick_block_m(R, E))
+        m.bf8_grouped_gemm_act_quant(gq, gs, w13_q, w13_s, offs, aq, as_, block_m=m.pick_block_m(R, E))
         m.bf8_grouped_gemm(aq, as_, w2_q, w2_s, c2, mode=m.MOE_MODE_GROUPED, expert_offsets=offs,
                            block_m=m.pick_block_m(R, E))
         m.topk_reduce(c2, ids, w, out, route_rows=rr)

@@ -68,7 +68,16 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_F16 = 2 } moe_dtype;
-typedef enum { MOE_ACT_IDENTITY = 0, MOE_ACT_SILU_MUL = 1 } moe_act;
+/* Gated activations h = act(gate) * up: the five GLU variants (SwiGLU, GEGLU with the exact GELU,
+ * ReGLU, GLU, bilinear); IDENTITY quantizes its input as is. */
+typedef enum {
+    MOE_ACT_IDENTITY = 0,
+    MOE_ACT_SILU_MUL = 1,     /* (g / (1 + exp(-g))) * u */
+    MOE_ACT_GELU_MUL = 2,     /* (g * (0.5 * (1 + erf(g / sqrt 2)))) * u */
+    MOE_ACT_RELU_MUL = 3,     /* (g > 0 ? g : +0) * u */
+    MOE_ACT_SIGMOID_MUL = 4,  /* (1 / (1 + exp(-g))) * u */
+    MOE_ACT_MUL = 5           /* g * u */
+} moe_act;
 typedef enum { MOE_MODE_GROUPED = 0, MOE_MODE_SLOT = 1 } moe_gemm_mode;
 
 /* Version of this header the library was built from (MOE_ABI_VERSION). */
@@ -101,17 +110,20 @@ int moe_gather_rows_scales(const void* src_q, int64_t src_q_stride,
                            void* stream);
 
 /*
- * moe_act_quant  -- per-row 1x128 fp8 quantization, optionally of SiLU(gate)*up
+ * moe_act_quant  -- per-row 1x128 fp8 quantization, optionally of a gated activation
  *   act = MOE_ACT_IDENTITY: v = in[r, c] for c in [0, n)
- *   act = MOE_ACT_SILU_MUL: in row is [gate(0:n) | up(n:2n)], v = gate/(1+exp(-gate)) * up, fp32
+ *   gated acts (moe_act 1..5): in row is [gate(0:n) | up(n:2n)], v = act(gate) * up in fp32, with the
+ *   expressions of moe_act ([inactive] Validation lists five activations; the five GLU variants are
+ *   taken as them)
  *   per group of 128 columns of v (last group may be shorter):
  *     s = max|v| / 448 (fp32, correctly rounded);  q = (s == 0) ? 0x00 : e4m3_rne(v / s)
  *   in    [rows][in_stride] of in_dt (MOE_BF16, MOE_F16 or MOE_F32)
  *   out_q [rows][q_stride] bytes, out_s [rows][s_stride] fp32 (ceil(n/128) used)
  *   Inputs must be finite.  IDENTITY mode is bit-exact with a correctly
- *   rounded division and round-to-nearest-even e4m3 encoding; SILU_MUL uses
- *   the device expf, so its codes may differ by one e4m3 step from a host
- *   evaluation.  An all-zero group gives s = +0 and q = 0x00 (a zeroed
+ *   rounded division and round-to-nearest-even e4m3 encoding, and so are
+ *   RELU_MUL and MUL (exact fp32 products); SILU, GELU and SIGMOID use the
+ *   device expf / erff, so their codes may differ by one e4m3 step from a
+ *   host evaluation.  An all-zero group gives s = +0 and q = 0x00 (a zeroed
  *   inactive-route tile stays zero, [inactive] opening section).
  */
 int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, int64_t n, int act,
@@ -164,28 +176,28 @@ int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s,
                          void* out, int out_dt, int64_t out_stride, void* stream);
 
 /*
- * moe_bf8_grouped_gemm_silu_quant  -- the prefill gate/up GEMM with the
+ * moe_bf8_grouped_gemm_act_quant  -- the prefill gate/up GEMM with the gated
  *   activation and its requant in the epilogue  [tile] [inactive]
- *   The gate/up GEMM of grouped (prefill) mode followed by moe_act_quant
- *   SILU_MUL, in one launch: with c1 the fp32 GEMM result of
+ *   The gate/up GEMM of grouped (prefill) mode followed by moe_act_quant with
+ *   a gated act (moe_act 1..5), in one launch: with c1 the fp32 GEMM result of
  *   moe_bf8_grouped_gemm (N = 2I, W13 rows 0..I-1 gate, I..2I-1 up), never
- *   stored, h[r, c] = (g / (1 + exp(-g))) * u with g = c1[r, c], u = c1[r, I + c]
- *   (fp32), then per 1x128 group s = amax/448 and q = e4m3(h/s) as in
- *   moe_act_quant (q = 0x00, s = +0 when amax = 0).
+ *   stored, h[r, c] = act(g) * u with g = c1[r, c], u = c1[r, I + c] (fp32,
+ *   the moe_act expressions), then per 1x128 group s = amax/448 and
+ *   q = e4m3(h/s) as in moe_act_quant (q = 0x00, s = +0 when amax = 0).
  *   a_q, a_s, w_q, w_s, expert_offsets, m_rows, block_m: as moe_bf8_grouped_gemm
  *   in MOE_MODE_GROUPED with N = 2I.
  *   out_q [m_rows][q_stride] fp8 (I used), out_s [m_rows][s_stride] fp32 (I/128
  *   used).  The results equal moe_bf8_grouped_gemm with MOE_F32 output followed
- *   by moe_act_quant SILU_MUL on it, bit for bit.
+ *   by moe_act_quant with the same act on it, bit for bit.
  *   Requirements: I % 128 == 0, K % 128 == 0, K <= 8192, 1 <= n_experts <=
  *   1024, alignment as moe_bf8_grouped_gemm; m_rows == 0 launches nothing.
  */
-int moe_bf8_grouped_gemm_silu_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
-                                    const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
-                                    const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n,
-                                    int64_t n_experts, int64_t I, int64_t K, const int32_t* expert_offsets,
-                                    int64_t m_rows, int32_t block_m, uint8_t* out_q, int64_t q_stride,
-                                    float* out_s, int64_t s_stride, void* stream);
+int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                                   const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
+                                   const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n,
+                                   int64_t n_experts, int64_t I, int64_t K, const int32_t* expert_offsets,
+                                   int64_t m_rows, int32_t block_m, int act, uint8_t* out_q, int64_t q_stride,
+                                   float* out_s, int64_t s_stride, void* stream);
 
 /*
  * moe_topk_reduce  -- routing-weighted sum over each token's top-k routes
@@ -262,8 +274,10 @@ int moe_route_prep(const float* logits, int64_t logits_stride, int64_t T, int64_
 /*
  * moe_fused_decode  -- one decode step of the routed experts  [inactive]
  *   x (T x H bf16) -> 1x128 fp8 quant -> gate/up GEMM per route (slot mode,
- *   A row = token) -> SiLU(gate)*up + 1x128 requant -> down GEMM per route
- *   -> routing-weighted top-k reduce -> out (T x H bf16).
+ *   A row = token) -> act(gate)*up + 1x128 requant -> down GEMM per route
+ *   -> routing-weighted top-k reduce -> out (T x H bf16).  act: a gated
+ *   moe_act (1..5), as in moe_act_quant ([inactive] Validation: five
+ *   activations).
  *   slot_ids, weights: DEVICE [T][topk]; slot < 0 = inactive route (zero
  *   c1/act/c2 tiles, no reads of its weights, scales or routing weight).
  *   w13_q [n_slots][2I][H] fp8 (gate rows 0..I-1, up rows I..2I-1), contiguous;
@@ -278,7 +292,7 @@ int moe_route_prep(const float* logits, int64_t logits_stride, int64_t T, int64_
  *   tiles hand h to the down tiles through the workspace's control block;
  *   otherwise it is two launches (I <= 1024) or four (wider I).
  */
-int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk,
+int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk, int act,
                      const int32_t* slot_ids, const float* weights, int64_t n_slots,
                      const uint8_t* w13_q, const float* w13_s,
                      const uint8_t* w2_q, const float* w2_s,

@@ -22,14 +22,14 @@ LIB_PATH = os.path.join(HERE, "libmoe_routed.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 MOE_BF16, MOE_F32, MOE_F16 = 0, 1, 2
-MOE_ACT_IDENTITY, MOE_ACT_SILU_MUL = 0, 1
+MOE_ACT_IDENTITY, MOE_ACT_SILU_MUL, MOE_ACT_GELU_MUL, MOE_ACT_RELU_MUL, MOE_ACT_SIGMOID_MUL, MOE_ACT_MUL = 0, 1, 2, 3, 4, 5
 MOE_MODE_GROUPED, MOE_MODE_SLOT = 0, 1
 
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_gather_rows_scales", "moe_act_quant",
     "moe_pick_block_m", "moe_bf8_grouped_gemm", "moe_topk_reduce", "moe_fused_decode_workspace_size",
     "moe_fused_decode_workspace_layout", "moe_fused_decode_workspace_init", "moe_fused_decode",
-    "moe_route_prep_workspace_size", "moe_route_prep", "moe_bf8_grouped_gemm_silu_quant",
+    "moe_route_prep_workspace_size", "moe_route_prep", "moe_bf8_grouped_gemm_act_quant",
 )
 
 _lib = None
@@ -67,11 +67,11 @@ def lib():
             "moe_fused_decode_workspace_size": ([I64, I64, I64, I64], SZ),
             "moe_fused_decode_workspace_layout": ([I64, I64, I64, I64, P], I32),
             "moe_fused_decode_workspace_init": ([P, SZ, I64, I64, I64, I64, P], I32),
-            "moe_fused_decode": ([P, I64, I64, I64, I64, P, P, I64, P, P, P, P, P, SZ, P, P], I32),
+            "moe_fused_decode": ([P, I64, I64, I64, I64, I32, P, P, I64, P, P, P, P, P, SZ, P, P], I32),
             "moe_route_prep_workspace_size": ([I64, I64], SZ),
             "moe_route_prep": ([P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
-            "moe_bf8_grouped_gemm_silu_quant": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, P, I64,
-                                                 I32, P, I64, P, I64, P], I32),
+            "moe_bf8_grouped_gemm_act_quant": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, P, I64,
+                                                I32, I32, P, I64, P, I64, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -149,18 +149,19 @@ def bf8_grouped_gemm(a_q, a_s, w_q, w_s, out, *, mode, expert_offsets=None, slot
         _ptr(out), _dt(out), _rowstride(out), _stream(stream)))
 
 
-def bf8_grouped_gemm_silu_quant(a_q, a_s, w13_q, w13_s, expert_offsets, out_q, out_s, m_rows=None, block_m=0,
-                                stream=None):
-    """Prefill gate/up GEMM with SiLU(gate)*up and the 1x128 fp8 requant in its epilogue.
+def bf8_grouped_gemm_act_quant(a_q, a_s, w13_q, w13_s, expert_offsets, out_q, out_s, m_rows=None, block_m=0,
+                               act=1, stream=None):
+    """Prefill gate/up GEMM with act(gate)*up (moe_act 1..5, default SwiGLU) and the 1x128 fp8 requant in
+    its epilogue.
     w13_q [E, 2I, K] (gate rows, then up rows), w13_s [E, 2I/128, K/128]; out_q [rows, I] u8, out_s [rows, I/128]."""
     E, N, K = w13_q.shape
     if m_rows is None:
         m_rows = out_q.shape[0]
     assert w13_q.stride(2) == 1 and w13_s.stride(2) == 1
-    _check("moe_bf8_grouped_gemm_silu_quant", lib().moe_bf8_grouped_gemm_silu_quant(
+    _check("moe_bf8_grouped_gemm_act_quant", lib().moe_bf8_grouped_gemm_act_quant(
         _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
         _ptr(w13_q), w13_q.stride(0), w13_q.stride(1), _ptr(w13_s), w13_s.stride(0), w13_s.stride(1),
-        E, N // 2, K, _ptr(expert_offsets), m_rows, block_m, _ptr(out_q), _rowstride(out_q),
+        E, N // 2, K, _ptr(expert_offsets), m_rows, block_m, act, _ptr(out_q), _rowstride(out_q),
         _ptr(out_s), _rowstride(out_s), _stream(stream)))
 
 
@@ -194,7 +195,7 @@ def fused_decode_workspace(T, H, I, topk, device="cuda", stream=None) -> torch.T
     return ws
 
 
-def fused_decode(x, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, workspace, out, stream=None):
+def fused_decode(x, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, workspace, out, act=1, stream=None):
     """One routed-expert decode step: x [T, H] bf16 -> out [T, H] bf16."""
     T, H = x.shape
     topk = slot_ids.shape[1]
@@ -203,7 +204,7 @@ def fused_decode(x, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, workspace, out,
     for t in (x, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, out):
         assert t.is_contiguous()
     _check("moe_fused_decode", lib().moe_fused_decode(
-        _ptr(x), T, H, I, topk, _ptr(slot_ids), _ptr(weights), S, _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
+        _ptr(x), T, H, I, topk, act, _ptr(slot_ids), _ptr(weights), S, _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
         _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
 
 

@@ -19,11 +19,11 @@ int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t
                         const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n, int64_t E, int64_t N,
                         int64_t K, const int32_t* offsets, int64_t m_rows, void* out, int out_dt,
                         int64_t out_stride);
-int grouped_gemm_silu_quant_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t a_stride,
-                                   const float* a_s, int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
-                                   int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
-                                   int64_t w_s_stride_n, int64_t E, int64_t I, int64_t K, const int32_t* offsets,
-                                   int64_t m_rows, uint8_t* q, int64_t q_stride, float* s, int64_t s_stride);
+int grouped_gemm_act_quant_launch(hipStream_t st, int block_m, int act, const uint8_t* a_q, int64_t a_stride,
+                                  const float* a_s, int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
+                                  int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
+                                  int64_t w_s_stride_n, int64_t E, int64_t I, int64_t K, const int32_t* offsets,
+                                  int64_t m_rows, uint8_t* q, int64_t q_stride, float* s, int64_t s_stride);
 int topk_reduce_launch(hipStream_t st, const void* y, int y_dt, int64_t y_stride, const int32_t* slot_ids,
                        const int32_t* route_rows, const float* weights, int64_t T, int64_t topk, int64_t H,
                        uint16_t* out, int64_t out_stride);
@@ -142,15 +142,16 @@ extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const 
                                out_stride);
 }
 
-extern "C" int moe_bf8_grouped_gemm_silu_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s,
-                                               int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
-                                               int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
-                                               int64_t w_s_stride_n, int64_t n_experts, int64_t I, int64_t K,
-                                               const int32_t* expert_offsets, int64_t m_rows, int32_t block_m,
-                                               uint8_t* out_q, int64_t q_stride, float* out_s, int64_t s_stride,
-                                               void* stream) {
+extern "C" int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s,
+                                              int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
+                                              int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
+                                              int64_t w_s_stride_n, int64_t n_experts, int64_t I, int64_t K,
+                                              const int32_t* expert_offsets, int64_t m_rows, int32_t block_m,
+                                              int act, uint8_t* out_q, int64_t q_stride, float* out_s,
+                                              int64_t s_stride, void* stream) {
     if (m_rows < 0 || n_experts < 1 || n_experts > 1024 || I < 128 || I % 128 || K < 128 || K % 128 || K > 8192)
         return MOE_ERR_SHAPE;
+    if (act < MOE_ACT_SILU_MUL || act > MOE_ACT_MUL) return MOE_ERR_SHAPE;
     if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_SHAPE;
     if (m_rows == 0) return MOE_OK;
     if (!a_q || !a_s || !w_q || !w_s || !expert_offsets || !out_q || !out_s) return MOE_ERR_NULL;
@@ -160,9 +161,9 @@ extern "C" int moe_bf8_grouped_gemm_silu_quant(const uint8_t* a_q, int64_t a_str
     if (n_experts > 1 && (w_stride_e < 2 * I * w_stride_n || w_s_stride_e < nb * w_s_stride_n)) return MOE_ERR_SHAPE;
     if (!aligned16(w_q) || !aligned16(a_q) || w_stride_n % 16 || w_stride_e % 16 || a_stride % 16) return MOE_ERR_ALIGN;
     const int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
-    return grouped_gemm_silu_quant_launch(as_stream(stream), bm, a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e,
-                                          w_stride_n, w_s, w_s_stride_e, w_s_stride_n, n_experts, I, K,
-                                          expert_offsets, m_rows, out_q, q_stride, out_s, s_stride);
+    return grouped_gemm_act_quant_launch(as_stream(stream), bm, act, a_q, a_stride, a_s, a_s_stride, w_q,
+                                         w_stride_e, w_stride_n, w_s, w_s_stride_e, w_s_stride_n, n_experts, I, K,
+                                         expert_offsets, m_rows, out_q, q_stride, out_s, s_stride);
 }
 
 extern "C" size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk) {
@@ -191,12 +192,13 @@ extern "C" int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes,
     return launch_status();
 }
 
-extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk,
+extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk, int act,
                                 const int32_t* slot_ids, const float* weights, int64_t n_slots,
                                 const uint8_t* w13_q, const float* w13_s,
                                 const uint8_t* w2_q, const float* w2_s,
                                 void* workspace, size_t ws_bytes, uint16_t* out_bf16, void* stream) {
     if (!decode_shape_ok(T, H, I, topk) || n_slots < 0) return MOE_ERR_SHAPE;
+    if (act < MOE_ACT_SILU_MUL || act > MOE_ACT_MUL) return MOE_ERR_SHAPE;
     if (T == 0) return MOE_OK;
     if (!x_bf16 || !slot_ids || !weights || !workspace || !out_bf16) return MOE_ERR_NULL;
     if (n_slots > 0 && (!w13_q || !w13_s || !w2_q || !w2_s)) return MOE_ERR_NULL;
@@ -221,7 +223,7 @@ extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, in
         a.w13 = w13_q; a.w13s = w13_s; a.w2 = w2_q; a.w2s = w2_s;
         a.c1 = c1; a.h = hbuf; a.aq = aq; a.as = as; a.c2 = c2; a.out = out_bf16;
         a.ctl = (uint32_t*)(ws + L.off[5]);
-        a.T = (int)T; a.H = (int)H; a.I = (int)I; a.topk = (int)topk;
+        a.T = (int)T; a.H = (int)H; a.I = (int)I; a.topk = (int)topk; a.act = act;
         a.tiles_a = 0; a.tiles_c = 0; a.n_a = 0;
         const int rc = fused_decode_one_launch(st, a);
         return rc == 1 ? fused_decode_two_launch(st, a) : rc;
@@ -230,8 +232,8 @@ extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, in
     // 1) gate/up per route, quantizing the bf16 token row on the fly
     int rc = slot_gemm_launch(st, true, x_bf16, H, nullptr, 0, w13_q, 2 * I * H, H, w13_s, g2I * gH, gH, 2 * I, H,
                               slot_ids, R, topk, c1, MOE_F32, 2 * I);
-    // 2) SiLU(gate)*up + 1x128 requant over every route (zero tiles stay zero)
-    if (rc == MOE_OK) rc = moe_act_quant(c1, MOE_F32, 2 * I, R, I, MOE_ACT_SILU_MUL, aq, I, as, gI, stream);
+    // 2) act(gate)*up + 1x128 requant over every route (zero tiles stay zero)
+    if (rc == MOE_OK) rc = moe_act_quant(c1, MOE_F32, 2 * I, R, I, act, aq, I, as, gI, stream);
     // 3) down per route
     if (rc == MOE_OK)
         rc = slot_gemm_launch(st, false, aq, I, as, gI, w2_q, H * I, I, w2_s, gH * gI, gI, H, I, slot_ids, R, 1, c2,

@@ -1,9 +1,10 @@
-// Per-row 1x128 fp8 quantization, optionally of SiLU(gate)*up.
+// Per-row 1x128 fp8 quantization, optionally of a gated activation act(gate)*up.
 //
 // IDENTITY mode quantizes an activation once before it is replicated per
 // routed expert ("[MoE] Gather the cutlass MoE activation and its scales in
-// one launch", Motivation).  SILU_MUL mode is the activation between the two
-// GEMMs; it also runs over the zeroed tiles of inactive routes, which it maps
+// one launch", Motivation).  The gated modes (SwiGLU and the other four GLU
+// variants) are the activation between the two GEMMs; they also run over the
+// zeroed tiles of inactive routes, which they map
 // to zero codes and zero scales ("perf(moe): skip inactive block-fp8 decode
 // routes", opening section).
 //
@@ -22,9 +23,9 @@ namespace {
 constexpr int kColsPerLane = 8;
 constexpr int kColsPerWave = kWave * kColsPerLane;   // 512 = 4 groups
 
-template <int DT, int ACT, bool VEC>
+template <int DT, bool GATED, bool VEC>
 __global__ void __launch_bounds__(256)
-act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, int64_t n,
+act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, int64_t n, int act,
                  uint8_t* __restrict__ out_q, int64_t q_stride, float* __restrict__ out_s, int64_t s_stride) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t segs = ceil_div(n, kColsPerWave);
@@ -42,12 +43,12 @@ act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, i
             const float4* p = reinterpret_cast<const float4*>((const float*)in + base + c0);
             float4 a = p[0], b = p[1];
             v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-            if constexpr (ACT == MOE_ACT_SILU_MUL) {
+            if constexpr (GATED) {
                 const float4* pu = reinterpret_cast<const float4*>((const float*)in + base + n + c0);
                 float4 ua = pu[0], ub = pu[1];
                 float u[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
 #pragma unroll
-                for (int i = 0; i < 8; i++) v[i] = (v[i] / (1.0f + expf(-v[i]))) * u[i];
+                for (int i = 0; i < 8; i++) v[i] = gated_act(act, v[i], u[i]);
             }
         } else {
             uint4 a = *reinterpret_cast<const uint4*>((const uint16_t*)in + base + c0);
@@ -57,15 +58,15 @@ act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, i
                 v[2 * i] = DT == kBF16 ? bf16_to_f32((uint16_t)(w[i] & 0xFFFF)) : f16_to_f32((uint16_t)(w[i] & 0xFFFF));
                 v[2 * i + 1] = DT == kBF16 ? bf16_to_f32((uint16_t)(w[i] >> 16)) : f16_to_f32((uint16_t)(w[i] >> 16));
             }
-            if constexpr (ACT == MOE_ACT_SILU_MUL) {
+            if constexpr (GATED) {
                 uint4 b = *reinterpret_cast<const uint4*>((const uint16_t*)in + base + n + c0);
                 uint32_t x[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     float u0 = DT == kBF16 ? bf16_to_f32((uint16_t)(x[i] & 0xFFFF)) : f16_to_f32((uint16_t)(x[i] & 0xFFFF));
                     float u1 = DT == kBF16 ? bf16_to_f32((uint16_t)(x[i] >> 16)) : f16_to_f32((uint16_t)(x[i] >> 16));
-                    v[2 * i] = (v[2 * i] / (1.0f + expf(-v[2 * i]))) * u0;
-                    v[2 * i + 1] = (v[2 * i + 1] / (1.0f + expf(-v[2 * i + 1]))) * u1;
+                    v[2 * i] = gated_act(act, v[2 * i], u0);
+                    v[2 * i + 1] = gated_act(act, v[2 * i + 1], u1);
                 }
             }
         }
@@ -76,9 +77,9 @@ act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, i
             float x = 0.0f;
             if (c < ncols) {
                 x = load_as_f32<DT>(in, base + c);
-                if constexpr (ACT == MOE_ACT_SILU_MUL) {
+                if constexpr (GATED) {
                     float u = load_as_f32<DT>(in, base + n + c);
-                    x = (x / (1.0f + expf(-x))) * u;
+                    x = gated_act(act, x, u);
                 }
             }
             v[i] = x;
@@ -106,13 +107,15 @@ act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, i
     }
 }
 
-template <int DT, int ACT>
+template <int DT, bool GATED>
 void launch_act(bool vec, dim3 grid, hipStream_t st, const void* in, int64_t in_stride, int64_t rows, int64_t n,
-                uint8_t* q, int64_t qs, float* s, int64_t ss) {
+                int act, uint8_t* q, int64_t qs, float* s, int64_t ss) {
     if (vec)
-        hipLaunchKernelGGL((act_quant_kernel<DT, ACT, true>), grid, dim3(256), 0, st, in, in_stride, rows, n, q, qs, s, ss);
+        hipLaunchKernelGGL((act_quant_kernel<DT, GATED, true>), grid, dim3(256), 0, st, in, in_stride, rows, n, act,
+                           q, qs, s, ss);
     else
-        hipLaunchKernelGGL((act_quant_kernel<DT, ACT, false>), grid, dim3(256), 0, st, in, in_stride, rows, n, q, qs, s, ss);
+        hipLaunchKernelGGL((act_quant_kernel<DT, GATED, false>), grid, dim3(256), 0, st, in, in_stride, rows, n, act,
+                           q, qs, s, ss);
 }
 
 }  // namespace
@@ -124,10 +127,10 @@ extern "C" int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64
                              uint8_t* out_q, int64_t q_stride, float* out_s, int64_t s_stride, void* stream) {
     if (rows < 0 || n < 0) return MOE_ERR_SHAPE;
     if (!dtype_ok(in_dt)) return MOE_ERR_DTYPE;
-    if (act != MOE_ACT_IDENTITY && act != MOE_ACT_SILU_MUL) return MOE_ERR_SHAPE;
+    if (act < MOE_ACT_IDENTITY || act > MOE_ACT_MUL) return MOE_ERR_SHAPE;
     if (rows == 0 || n == 0) return MOE_OK;
     if (!in || !out_q || !out_s) return MOE_ERR_NULL;
-    const int64_t width = act == MOE_ACT_SILU_MUL ? 2 * n : n;
+    const int64_t width = act != MOE_ACT_IDENTITY ? 2 * n : n;
     if (in_stride < width || q_stride < n || s_stride < ceil_div(n, 128)) return MOE_ERR_SHAPE;
     const int64_t esz = in_dt == MOE_F32 ? 4 : 2;
     // vector loads need every lane's 8 elements 16-byte aligned: base, stride and the up offset
@@ -138,13 +141,13 @@ extern "C" int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64
     dim3 grid((unsigned)blocks);
     auto st = as_stream(stream);
     if (act == MOE_ACT_IDENTITY) {
-        if (in_dt == MOE_F32) launch_act<kF32, MOE_ACT_IDENTITY>(vec, grid, st, in, in_stride, rows, n, out_q, q_stride, out_s, s_stride);
-        else if (in_dt == MOE_BF16) launch_act<kBF16, MOE_ACT_IDENTITY>(vec, grid, st, in, in_stride, rows, n, out_q, q_stride, out_s, s_stride);
-        else launch_act<kF16, MOE_ACT_IDENTITY>(vec, grid, st, in, in_stride, rows, n, out_q, q_stride, out_s, s_stride);
+        if (in_dt == MOE_F32) launch_act<kF32, false>(vec, grid, st, in, in_stride, rows, n, act, out_q, q_stride, out_s, s_stride);
+        else if (in_dt == MOE_BF16) launch_act<kBF16, false>(vec, grid, st, in, in_stride, rows, n, act, out_q, q_stride, out_s, s_stride);
+        else launch_act<kF16, false>(vec, grid, st, in, in_stride, rows, n, act, out_q, q_stride, out_s, s_stride);
     } else {
-        if (in_dt == MOE_F32) launch_act<kF32, MOE_ACT_SILU_MUL>(vec, grid, st, in, in_stride, rows, n, out_q, q_stride, out_s, s_stride);
-        else if (in_dt == MOE_BF16) launch_act<kBF16, MOE_ACT_SILU_MUL>(vec, grid, st, in, in_stride, rows, n, out_q, q_stride, out_s, s_stride);
-        else launch_act<kF16, MOE_ACT_SILU_MUL>(vec, grid, st, in, in_stride, rows, n, out_q, q_stride, out_s, s_stride);
+        if (in_dt == MOE_F32) launch_act<kF32, true>(vec, grid, st, in, in_stride, rows, n, act, out_q, q_stride, out_s, s_stride);
+        else if (in_dt == MOE_BF16) launch_act<kBF16, true>(vec, grid, st, in, in_stride, rows, n, act, out_q, q_stride, out_s, s_stride);
+        else launch_act<kF16, true>(vec, grid, st, in, in_stride, rows, n, act, out_q, q_stride, out_s, s_stride);
     }
     return launch_status();
 }

@@ -22,6 +22,7 @@ struct FusedDecodeArgs {
     uint16_t* out;           // [T][H] bf16
     uint32_t* ctl;           // control block of the one-launch step (decode_ctl_bytes)
     int T, H, I, topk;
+    int act;                 // gated activation (moe_act 1..5)
     int tiles_a;             // gate/up tiles per route (set by the launcher)
     int tiles_c;             // down tiles per token (set by the launcher)
     int n_a;                 // gate/up tiles in total (set by the launcher)

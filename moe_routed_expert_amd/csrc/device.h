@@ -71,6 +71,18 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, float v) {
     else ((uint16_t*)p)[i] = f32_to_f16(v);
 }
 
+// Gated activation of gate g and up u in fp32 (moe_act values 1..5: SwiGLU, GEGLU with the exact GELU,
+// ReGLU, GLU, bilinear -- the five GLU variants), one expression each in a fixed order of operations.
+__device__ __forceinline__ float gated_act(int act, float g, float u) {
+    switch (act) {
+        case 1: return (g / (1.0f + expf(-g))) * u;
+        case 2: return (g * (0.5f * (1.0f + erff(g * 0.70710678118654752f)))) * u;
+        case 3: return (g > 0.0f ? g : 0.0f) * u;
+        case 4: return (1.0f / (1.0f + expf(-g))) * u;
+        default: return g * u;
+    }
+}
+
 // Four consecutive elements i..i+3 from fp32 in one store; p + i must be aligned to 4 elements.
 template <int DT>
 __device__ __forceinline__ void store4_from_f32(void* p, int64_t i, v4f v) {

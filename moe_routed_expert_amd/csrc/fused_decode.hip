@@ -156,7 +156,7 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_gateup_kernel(FusedDe
         const int64_t rr = threadIdx.x < 8 ? c0 + threadIdx.x : a.I + c0 + (threadIdx.x - 8);
         a.c1[r * N + rr] = t;
         const float up = __shfl_down(t, 8, kFdTile);            // lanes 0..7 get their up value
-        if (threadIdx.x < 8) a.h[r * a.I + c0 + threadIdx.x] = (t / (1.0f + expf(-t))) * up;
+        if (threadIdx.x < 8) a.h[r * a.I + c0 + threadIdx.x] = gated_act(a.act, t, up);
     }
 }
 
@@ -530,7 +530,7 @@ __device__ __forceinline__ void gateup_tile_m(const FusedDecodeArgs& a, int b) {
 #pragma unroll
         for (int w = 1; w < kFdWaves; w++) t += red[w][g][c];
         const float up = __shfl_down(t, 8, kFdTile);            // lanes c < 8 get their up value
-        if (c < 8) store_coherent(&a.h[r * a.I + c0 + 8 * g + c], (t / (1.0f + expf(-t))) * up);
+        if (c < 8) store_coherent(&a.h[r * a.I + c0 + 8 * g + c], gated_act(a.act, t, up));
         // h of this tile is complete at the device-coherent level before the count moves
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (threadIdx.x == 0) {

@@ -38,11 +38,11 @@
 //    tiles meet in that XCD's L2, and every XCD gets the same number of tiles.
 //  * A tile's expert is a binary search of the LDS table; its scales are
 //    loaded row-contiguous, all requests in flight before the LDS stores.
-//  * Fused SiLU-mul requant (the gate/up GEMM of a prefill step with the
-//    activation in its epilogue): a tile covers one 128-column act group; each
-//    wave's two 16-column sub-tiles are gate rows and the matching up rows of
-//    W13, so a lane holds gate and up of the same four columns of one row and
-//    forms h = SiLU(gate)*up from the fp32 accumulators.  The group amax is a
+//  * Fused activation requant (the gate/up GEMM of a prefill step with the
+//    gated activation in its epilogue): a tile covers one 128-column act group;
+//    each wave's two 16-column sub-tiles are gate rows and the matching up rows
+//    of W13, so a lane holds gate and up of the same four columns of one row and
+//    forms h = act(gate)*up from the fp32 accumulators.  The group amax is a
 //    lane shuffle plus an 8-wave LDS max, then s = amax/448 and the codes
 //    e4m3(h/s) leave as one 4-byte store per lane; the [rows][2I] GEMM output
 //    is never written.
@@ -92,6 +92,7 @@ struct GgArgs {
     int64_t q_stride;
     float* s;                                 // fused: scales [rows][s_stride], I/128 used
     int64_t s_stride;
+    int act;                                  // fused: gated activation (moe_act 1..5)
 };
 
 // Exclusive scan of one int per thread over a block of WAVES waves.
@@ -112,7 +113,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* ldsw) {
 }
 
 // Fused epilogue: acc[m][0] holds gate and acc[m][1] up for row m*16 + lane%16, act columns
-// 128*n_tile + 16*wave + 4*(lane/16) + i.  h = SiLU(gate)*up in fp32; per row, the amax of the 128
+// 128*n_tile + 16*wave + 4*(lane/16) + i.  h = act(gate)*up in fp32; per row, the amax of the 128
 // columns (4 lanes by shuffle, then the 8 waves through LDS), s = amax/448 (correctly rounded), codes
 // e4m3(h/s) (zero codes when s == 0).
 template <int BM>
@@ -127,7 +128,7 @@ __device__ __forceinline__ void act_quant_epilogue(const GgArgs& g, v4f (&acc)[B
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const float gt = acc[m][0][i], up = acc[m][1][i];
-            acc[m][0][i] = (gt / (1.0f + expf(-gt))) * up;      // h replaces gate
+            acc[m][0][i] = gated_act(g.act, gt, up);             // h replaces gate
             a = __builtin_fmaxf(a, __builtin_fabsf(acc[m][0][i]));
         }
         a = __builtin_fmaxf(a, __shfl_xor(a, 16, kWave));
@@ -490,17 +491,17 @@ int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t
     return grouped_launch_bm(st, block_m, out_dt, false, g);
 }
 
-int grouped_gemm_silu_quant_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t a_stride,
-                                   const float* a_s, int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
-                                   int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
-                                   int64_t w_s_stride_n, int64_t E, int64_t I, int64_t K, const int32_t* offsets,
-                                   int64_t m_rows, uint8_t* q, int64_t q_stride, float* s, int64_t s_stride) {
+int grouped_gemm_act_quant_launch(hipStream_t st, int block_m, int act, const uint8_t* a_q, int64_t a_stride,
+                                  const float* a_s, int64_t a_s_stride, const uint8_t* w_q, int64_t w_stride_e,
+                                  int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
+                                  int64_t w_s_stride_n, int64_t E, int64_t I, int64_t K, const int32_t* offsets,
+                                  int64_t m_rows, uint8_t* q, int64_t q_stride, float* s, int64_t s_stride) {
     GgArgs g{};
     g.a_q = a_q; g.a_stride = a_stride; g.a_s = a_s; g.a_s_stride = a_s_stride;
     g.w_q = w_q; g.w_stride_e = w_stride_e; g.w_stride_n = w_stride_n;
     g.w_s = w_s; g.w_s_stride_e = w_s_stride_e; g.w_s_stride_n = w_s_stride_n;
     g.n_experts = (int)E; g.N = 2 * I; g.K = K; g.offsets = offsets; g.m_rows = (int)m_rows;
-    g.q = q; g.q_stride = q_stride; g.s = s; g.s_stride = s_stride;
+    g.q = q; g.q_stride = q_stride; g.s = s; g.s_stride = s_stride; g.act = act;
     return grouped_launch_bm(st, block_m, MOE_F32, true, g);
 }
 

@@ -110,7 +110,7 @@ def test_gather_act_reduce_argument_checks():
     assert L.moe_gather_rows_scales(FAKE, 16, FAKE, 1, 4, 32, 1, FAKE, 8, FAKE, 32, FAKE, 1, None) == m.MOE_ERR_SHAPE
     assert L.moe_gather_rows_scales(FAKE, 32, FAKE, 1, 0, 32, 1, FAKE, 8, FAKE, 32, FAKE, 1, None) == m.MOE_ERR_SHAPE
     assert L.moe_act_quant(FAKE, 7, 256, 4, 256, 0, FAKE, 256, FAKE, 2, None) == m.MOE_ERR_DTYPE
-    assert L.moe_act_quant(FAKE, 0, 256, 4, 256, 3, FAKE, 256, FAKE, 2, None) == m.MOE_ERR_SHAPE
+    assert L.moe_act_quant(FAKE, 0, 256, 4, 256, 6, FAKE, 256, FAKE, 2, None) == m.MOE_ERR_SHAPE
     assert L.moe_act_quant(FAKE, 0, 256, 4, 256, 1, FAKE, 256, FAKE, 2, None) == m.MOE_ERR_SHAPE  # SILU needs 2n
     assert L.moe_act_quant(FAKE, 0, 256, 0, 256, 0, None, 256, None, 2, None) == m.MOE_OK
     assert L.moe_act_quant(FAKE, 0, 256, 4, 256, 0, None, 256, FAKE, 2, None) == m.MOE_ERR_NULL
@@ -130,11 +130,14 @@ def test_fused_decode_workspace_and_checks():
     assert m.fused_decode_workspace_size(1, 2000, 768, 8) == 0          # H % 128
     assert m.fused_decode_workspace_size(1, 2048, 768, 0) == 0          # topk >= 1
     size = lay["total"]
-    args = [FAKE, 1, 2048, 768, 8, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, size, FAKE, None]
-    a = list(args); a[13] = size - 1
+    args = [FAKE, 1, 2048, 768, 8, 1, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, size, FAKE, None]
+    a = list(args); a[14] = size - 1
     assert L.moe_fused_decode(*a) == m.MOE_ERR_WORKSPACE
-    a = list(args); a[12] = P(0x1008)
+    a = list(args); a[13] = P(0x1008)
     assert L.moe_fused_decode(*a) == m.MOE_ERR_ALIGN
+    for bad_act in (0, 6):
+        a = list(args); a[5] = bad_act
+        assert L.moe_fused_decode(*a) == m.MOE_ERR_SHAPE
     a = list(args); a[0] = None
     assert L.moe_fused_decode(*a) == m.MOE_ERR_NULL
     a = list(args); a[2] = 2000
@@ -178,16 +181,16 @@ def test_route_prep_workspace_and_checks():
     assert call(a10=P(0x1008)) == m.MOE_ERR_ALIGN
 
 
-def test_fused_gate_up_silu_quant_checks():
+def test_fused_gate_up_act_quant_checks():
     L = m.lib()
     args = dict(a_q=FAKE, a_stride=256, a_s=FAKE, a_s_stride=2, w_q=FAKE, w_stride_e=256 * 256, w_stride_n=256,
                 w_s=FAKE, w_s_stride_e=4, w_s_stride_n=2, n_experts=4, I=128, K=256, offsets=FAKE, m_rows=8,
-                block_m=0, q=FAKE, q_stride=128, s=FAKE, s_stride=1, stream=None)
+                block_m=0, act=1, q=FAKE, q_stride=128, s=FAKE, s_stride=1, stream=None)
 
     def call(**kw):
         a = dict(args)
         a.update(kw)
-        return L.moe_bf8_grouped_gemm_silu_quant(*a.values())
+        return L.moe_bf8_grouped_gemm_act_quant(*a.values())
 
     assert call(I=200) == m.MOE_ERR_SHAPE                 # I % 128
     assert call(K=200) == m.MOE_ERR_SHAPE                 # K % 128
@@ -196,6 +199,8 @@ def test_fused_gate_up_silu_quant_checks():
     assert call(n_experts=0) == m.MOE_ERR_SHAPE
     assert call(n_experts=1025) == m.MOE_ERR_SHAPE
     assert call(block_m=48) == m.MOE_ERR_SHAPE
+    assert call(act=0) == m.MOE_ERR_SHAPE                 # a gated activation is required
+    assert call(act=6) == m.MOE_ERR_SHAPE
     assert call(m_rows=0, q=None, s=None) == m.MOE_OK   # no work, no launch
     assert call(q=None) == m.MOE_ERR_NULL
     assert call(offsets=None) == m.MOE_ERR_NULL

@@ -133,6 +133,36 @@ def test_act_quant_silu_mul_within_one_step(orc, dtype, rows, n):
     assert np.all(d <= np.abs(dec(ref_q))[diff] * 0.125 + 2.0 ** -9)
 
 
+@pytest.mark.parametrize("act", [2, 3, 4, 5])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_act_quant_other_gated_activations(orc, act, dtype):
+    """GEGLU, ReGLU, GLU and bilinear against the oracle on the same input: ReGLU and bilinear are exact
+    fp32 products, so codes and scales match bit for bit; GEGLU and GLU go through the device erff/expf,
+    so scales match to a few ulp and a code may move by one e4m3 step, rarely."""
+    rows, n = 37, 640
+    g = torch.Generator().manual_seed(rows + n + act)
+    c1 = (torch.randn((rows, 2 * n), generator=g) * 2).to(dtype)
+    c1[0] = 0                                                       # an inactive route's zero tile
+    c1[1, :n] = -c1[1, :n].abs()                                     # non-positive gates: ReGLU zeros
+    host = c1.view(torch.int16).numpy().view(np.uint16) if dtype == torch.bfloat16 else c1.numpy()
+    ref_q, ref_s = orc.gated_act_quant(host, act)
+    q = torch.empty((rows, n), dtype=torch.uint8, device=dev())
+    s = torch.empty((rows, n // 128), dtype=torch.float32, device=dev())
+    m.act_quant(c1.to(dev()), q, s, act=act)
+    torch.cuda.synchronize()
+    hq, hs = q.cpu().numpy(), s.cpu().numpy()
+    assert np.all(hq[0] == 0) and np.all(hs[0].view(np.uint32) == 0)
+    if act in (3, 5):
+        assert np.array_equal(hq, ref_q) and np.array_equal(hs.view(np.uint32), ref_s.view(np.uint32))
+        return
+    assert np.allclose(hs, ref_s, rtol=4e-7, atol=0)
+    dec = lambda c: orc.e4m3_decode(c).astype(np.float64)
+    diff = hq != ref_q
+    assert diff.mean() < 2e-3
+    d = np.abs(dec(hq) - dec(ref_q))[diff]
+    assert np.all(d <= np.abs(dec(ref_q))[diff] * 0.125 + 2.0 ** -9)
+
+
 # ------------------------------------------------------------------ reduce ---
 
 def assert_reduce_bound(got, ref, y, slots, w, rr):

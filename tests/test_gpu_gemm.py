@@ -176,13 +176,21 @@ def test_grouped_prefill_routes_chain(orc):
 
 # ------------------------------------------------- fused SiLU-mul requant ---
 
-def silu_h_bound(c1_ref, c1_bound, I):
-    """|h_gpu - h_oracle| bound from the two sides' fp32 c1 bound: SiLU' lies in [-0.1, 1.1], so
-    |dh| <= 1.1 |dg| (|u| + |du|) + |silu(g)| |du|, plus a few fp32 roundings of h itself."""
+def act64(act, g):
+    """The gate functions of the five gated activations in float64 (scipy's erf and expit)."""
+    from scipy.special import erf, expit
+    return {1: lambda x: x * expit(x), 2: lambda x: x * 0.5 * (1 + erf(x / np.sqrt(2))),
+            3: lambda x: np.maximum(x, 0), 4: expit, 5: lambda x: x}[act](g)
+
+
+def silu_h_bound(c1_ref, c1_bound, I, act=1):
+    """|h_gpu - h_oracle| bound from the two sides' fp32 c1 bound: every gate function here has slope at most
+    1.13 (GELU's maximum; SiLU 1.1, ReLU and identity 1, sigmoid 0.25), so |dh| <= 1.13 |dg| (|u| + |du|) +
+    |act(g)| |du|, plus a few fp32 roundings of h itself (the device erff/expf within a few ulp)."""
     g, u = c1_ref[:, :I].astype(np.float64), c1_ref[:, I:].astype(np.float64)
     dg, du = c1_bound[:, :I], c1_bound[:, I:]
-    sg = g / (1 + np.exp(-g))
-    return 1.1 * dg * (np.abs(u) + du) + np.abs(sg) * du + 8 * 2.0 ** -24 * np.abs(sg * u)
+    sg = act64(act, g)
+    return 1.13 * dg * (np.abs(u) + du) + np.abs(sg) * du + 16 * 2.0 ** -24 * np.abs(sg * u) + 1e-30
 
 
 def check_codes_and_scales(orc, q, s, ref_q, ref_s, h_bound):
@@ -204,29 +212,31 @@ def check_codes_and_scales(orc, q, s, ref_q, ref_s, h_bound):
     assert not bad.any(), "%d dequantized values beyond the bound" % bad.sum()
 
 
-@pytest.mark.parametrize("bm", [0, 16, 32, 64, 128])
-def test_grouped_silu_quant_vs_oracle_and_unfused(orc, bm):
-    """The fused gate/up + SiLU-mul requant equals the oracle's fp32 GEMM followed by its requant (within
-    the derived bound), and the device's own unfused pair (fp32 GEMM, then act_quant) bit for bit."""
+@pytest.mark.parametrize("bm,act", [(0, 1), (16, 1), (32, 1), (64, 1), (128, 1), (64, 2), (128, 3), (32, 4),
+                                    (16, 5)])
+def test_grouped_silu_quant_vs_oracle_and_unfused(orc, bm, act):
+    """The fused gate/up + gated-activation requant equals the oracle's fp32 GEMM followed by its requant
+    (within the derived bound), and the device's own unfused pair (fp32 GEMM, then act_quant) bit for bit;
+    every tile size with SwiGLU, and each other activation once."""
     E, I, K = 5, 256, 640
     counts = [3, 0, 40, 129, 17]        # empty expert, ragged tails, several M tiles
-    print("fused gate/up silu-quant BM=%d" % bm, flush=True)
-    w_q, w_s, a_q, a_s, offs = grouped_case(E, 2 * I, K, counts, seed=100 + bm)
+    print("fused gate/up act-quant BM=%d act=%d" % (bm, act), flush=True)
+    w_q, w_s, a_q, a_s, offs = grouped_case(E, 2 * I, K, counts, seed=100 + bm + act)
     R = int(offs[-1])
     c1 = orc.block_gemm(a_q.numpy(), a_s.numpy(), w_q.numpy(), w_s.numpy(), mode=orc.MODE_GROUPED,
                         expert_offsets=offs, out_dtype=np.float32)
-    ref_q, ref_s = orc.silu_mul_quant(c1)
+    ref_q, ref_s = orc.gated_act_quant(c1, act)
     d = dev()
     q = torch.full((R + 2, I), 0xAB, dtype=torch.uint8, device=d)          # 2 spare rows stay untouched
     s = torch.full((R + 2, I // 128), float("nan"), dtype=torch.float32, device=d)
     wq, ws, aq, as_, od = w_q.to(d), w_s.to(d), a_q.to(d), a_s.to(d), to_dev(offs)
-    m.bf8_grouped_gemm_silu_quant(aq, as_, wq, ws, od, q, s, m_rows=R + 2, block_m=bm)
+    m.bf8_grouped_gemm_act_quant(aq, as_, wq, ws, od, q, s, m_rows=R + 2, block_m=bm, act=act)
     # the unfused device pair
     c1_d = torch.empty((R, 2 * I), dtype=torch.float32, device=d)
     m.bf8_grouped_gemm(aq, as_, wq, ws, c1_d, mode=m.MOE_MODE_GROUPED, expert_offsets=od, block_m=bm)
     q2 = torch.empty((R, I), dtype=torch.uint8, device=d)
     s2 = torch.empty((R, I // 128), dtype=torch.float32, device=d)
-    m.act_quant(c1_d, q2, s2, act=m.MOE_ACT_SILU_MUL)
+    m.act_quant(c1_d, q2, s2, act=act)
     torch.cuda.synchronize()
     hq, hs = q.cpu().numpy(), s.cpu().numpy()
     assert np.all(hq[R:] == 0xAB) and np.all(np.isnan(hs[R:]))
@@ -234,7 +244,7 @@ def test_grouped_silu_quant_vs_oracle_and_unfused(orc, bm):
                                                                       s2.cpu().numpy().view(np.uint32))
     experts = np.repeat(np.arange(E), np.diff(offs))
     c1_bound = gemm_abs_bound(a_q.numpy(), a_s.numpy(), w_q.numpy(), w_s.numpy(), experts, np.arange(R))
-    check_codes_and_scales(orc, hq[:R], hs[:R], ref_q, ref_s, silu_h_bound(c1, c1_bound, I))
+    check_codes_and_scales(orc, hq[:R], hs[:R], ref_q, ref_s, silu_h_bound(c1, c1_bound, I, act))
 
 
 def test_grouped_silu_quant_zero_rows():
@@ -246,7 +256,7 @@ def test_grouped_silu_quant_zero_rows():
     d = dev()
     q = torch.full((12, I), 0xAB, dtype=torch.uint8, device=d)
     s = torch.full((12, 1), float("nan"), dtype=torch.float32, device=d)
-    m.bf8_grouped_gemm_silu_quant(a_q.to(d), a_s.to(d), w_q.to(d), w_s.to(d), to_dev(offs), q, s)
+    m.bf8_grouped_gemm_act_quant(a_q.to(d), a_s.to(d), w_q.to(d), w_s.to(d), to_dev(offs), q, s)
     torch.cuda.synchronize()
     assert np.all(q.cpu().numpy()[3] == 0) and s.cpu().numpy()[3, 0] == 0.0 and not np.signbit(s.cpu().numpy()[3, 0])
 
@@ -264,7 +274,7 @@ def test_grouped_silu_quant_full_prefill_size(orc):
     a_q, a_s = wl.fp8_rows(R, H, seed=23, device=d)
     q = torch.empty((R, I), dtype=torch.uint8, device=d)
     s = torch.empty((R, I // 128), dtype=torch.float32, device=d)
-    m.bf8_grouped_gemm_silu_quant(a_q, a_s, w_q, w_s, od, q, s)
+    m.bf8_grouped_gemm_act_quant(a_q, a_s, w_q, w_s, od, q, s)
     c1_d = torch.empty((R, 2 * I), dtype=torch.float32, device=d)
     m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c1_d, mode=m.MOE_MODE_GROUPED, expert_offsets=od)
     q2 = torch.empty_like(q)

@@ -132,7 +132,7 @@ def test_prefill_layer_on_device_from_logits(orc):
     m.gather_rows_scales(xq_d, xs_d, d2s, gq_d, gs_d)
     aq_d = torch.empty((R, I), dtype=torch.uint8, device=d)
     as_d = torch.empty((R, I // 128), dtype=torch.float32, device=d)
-    m.bf8_grouped_gemm_silu_quant(gq_d, gs_d, w13_q.to(d), w13_s.to(d), offs, aq_d, as_d)
+    m.bf8_grouped_gemm_act_quant(gq_d, gs_d, w13_q.to(d), w13_s.to(d), offs, aq_d, as_d)
     c2_d = torch.empty((R, H), dtype=torch.bfloat16, device=d)
     m.bf8_grouped_gemm(aq_d, as_d, w2_q.to(d), w2_s.to(d), c2_d, mode=m.MOE_MODE_GROUPED, expert_offsets=offs)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=d)
