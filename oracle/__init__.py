@@ -60,11 +60,18 @@ def lib():
         L.orc_silu_mul_quant.argtypes = [P, I32, I64, I64, I64, P, I64, P, I64]
         L.orc_gated_act_quant.argtypes = [P, I32, I64, I64, I64, I32, P, I64, P, I64]
         L.orc_topk_reduce.argtypes = [P, I32, I64, P, P, P, I64, I64, I64, P, I64]
+        L.orc_mxfp4_gemm.argtypes = [P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64,
+                                     I32, P, P, I64, I64, P, I32, I64]
+        L.orc_e2m1_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_to_f32.restype = ctypes.c_float
+        L.orc_e8m0_to_f32.argtypes = [ctypes.c_uint8]
+        L.orc_e8m0_to_f32.restype = ctypes.c_float
         L.orc_route_prep.argtypes = [P, I64, I64, I64, I64, P, P, P, P, P]
         L.orc_fused_decode.argtypes = [P, I64, I64, I64, I64, I32, P, P, I64, P, P, P, P, P,
                                        P, P, P, P, P, P]
         for name in ("orc_quant_groups", "orc_gather_rows_scales", "orc_block_gemm",
-                     "orc_silu_mul_quant", "orc_gated_act_quant", "orc_topk_reduce", "orc_fused_decode"):
+                     "orc_silu_mul_quant", "orc_gated_act_quant", "orc_topk_reduce", "orc_fused_decode",
+                     "orc_mxfp4_gemm"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -189,6 +196,40 @@ def block_gemm(a_q, a_s, w_q, w_s, *, mode, out_dtype=np.float32, expert_offsets
 
 
 # ---- O4 ---------------------------------------------------------------------
+
+# ---- O8 ---------------------------------------------------------------------
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes (low 4 bits of each entry) -> float32."""
+    return np.array([lib().orc_e2m1_to_f32(int(c) & 15) for c in np.asarray(codes).ravel()],
+                    np.float32).reshape(np.shape(codes))
+
+
+def e8m0_decode(codes: np.ndarray) -> np.ndarray:
+    return np.array([lib().orc_e8m0_to_f32(int(c)) for c in np.asarray(codes).ravel()],
+                    np.float32).reshape(np.shape(codes))
+
+
+def mxfp4_gemm(a_q, a_s, w4, w4_s, *, mode, out_dtype=np.float32, expert_offsets=None, slot_ids=None,
+               m_rows=None, a_row_div=1):
+    """a_q [Ra, K] u8, a_s [Ra, K/128] f32, w4 [E, N, K/2] u8 (two E2M1 per byte, even k low),
+    w4_s [E, N, K/32] u8 (E8M0).  Returns [m_rows, N] of out_dtype (np.float32, np.float16, np.uint16 = bf16)."""
+    a_q, a_s = _c(a_q, np.uint8), _c(a_s, np.float32)
+    w4, w4_s = _c(w4, np.uint8), _c(w4_s, np.uint8)
+    E, N, K2 = w4.shape
+    K = 2 * K2
+    if mode == MODE_GROUPED:
+        expert_offsets = _c(expert_offsets, np.int32)
+        m_rows = int(expert_offsets[-1]) if m_rows is None else m_rows
+    else:
+        slot_ids = _c(slot_ids, np.int32)
+        m_rows = slot_ids.size if m_rows is None else m_rows
+    out = np.empty((m_rows, N), out_dtype)
+    _check(lib().orc_mxfp4_gemm(_p(a_q), a_q.shape[1], _p(a_s), a_s.shape[1], _p(w4), N * K2, K2, _p(w4_s),
+                                N * (K // 32), K // 32, E, N, K, mode, _p(expert_offsets), _p(slot_ids), m_rows,
+                                a_row_div, _p(out), _dt_code(out_dtype), N))
+    return out
+
 
 # gated activations of O4 (the five GLU variants; values as in the C header)
 ACT_SILU_MUL, ACT_GELU_MUL, ACT_RELU_MUL, ACT_SIGMOID_MUL, ACT_MUL = 1, 2, 3, 4, 5

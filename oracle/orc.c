@@ -274,6 +274,82 @@ int orc_block_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64
 }
 
 /* ------------------------------------------------------------------ */
+/* O8: block-FP8 activations x MXFP4 weights                          */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 element (low 4 bits of code): sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; exponent
+ * 0 is subnormal: 0.5 * m. */
+float orc_e2m1_to_f32(uint8_t code) {
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    float v = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+    return s ? -v : v;
+}
+
+/* E8M0 scale: 2^(e - 127); e = 255 is NaN. */
+float orc_e8m0_to_f32(uint8_t e) {
+    if (e == 255) return NAN;
+    return ldexpf(1.0f, (int)e - 127);
+}
+
+static void mx_gemm_row(const float* lut8, const uint8_t* arow, const float* asrow, const uint8_t* w_e,
+                        int64_t w_stride_n, const uint8_t* ws_e, int64_t ws_stride_n, int64_t N, int64_t K,
+                        void* out, int out_dt, int64_t out_row) {
+    int64_t nkb = K / 128;
+    for (int64_t n = 0; n < N; n++) {
+        const uint8_t* wrow = w_e + n * w_stride_n;
+        const uint8_t* wsrow = ws_e + n * ws_stride_n;
+        float acc = 0.0f;
+        for (int64_t kb = 0; kb < nkb; kb++) {
+            float p = 0.0f;
+            for (int64_t k = kb * 128; k < kb * 128 + 128; k++) {
+                uint8_t byte = wrow[k / 2];
+                float w = orc_e2m1_to_f32(k % 2 == 0 ? (uint8_t)(byte & 15) : (uint8_t)(byte >> 4));
+                float ws = w * orc_e8m0_to_f32(wsrow[k / 32]);        /* exact: power-of-two scaling */
+                float prod = lut8[arow[k]] * ws;                        /* exact: 4 x 2 significant bits */
+                p = p + prod;
+            }
+            acc = acc + p * asrow[kb];
+        }
+        store_elem(out, out_dt, out_row + n, acc);
+    }
+}
+
+int orc_mxfp4_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                   const uint8_t* w4, int64_t w4_stride_e, int64_t w4_stride_n,
+                   const uint8_t* w4_s, int64_t w4s_stride_e, int64_t w4s_stride_n,
+                   int64_t n_experts, int64_t N, int64_t K,
+                   int mode, const int32_t* expert_offsets, const int32_t* slot_ids,
+                   int64_t m_rows, int64_t a_row_div,
+                   void* out, int out_dt, int64_t out_stride) {
+    float lut8[256];
+    if (N < 0 || K < 0 || K % 128 || m_rows < 0 || n_experts < 0 || !dt_ok(out_dt)) return -2;
+    for (int c = 0; c < 256; c++) lut8[c] = orc_e4m3_to_f32((uint8_t)c);
+    if (mode == ORC_MODE_GROUPED) {
+        if (expert_offsets[0] != 0 || expert_offsets[n_experts] != m_rows) return -2;
+        for (int64_t e = 0; e < n_experts; e++) {
+            if (expert_offsets[e + 1] < expert_offsets[e]) return -2;
+            for (int64_t r = expert_offsets[e]; r < expert_offsets[e + 1]; r++)
+                mx_gemm_row(lut8, a_q + r * a_stride, a_s + r * a_s_stride, w4 + e * w4_stride_e, w4_stride_n,
+                            w4_s + e * w4s_stride_e, w4s_stride_n, N, K, out, out_dt, r * out_stride);
+        }
+        return 0;
+    }
+    if (mode != ORC_MODE_SLOT || a_row_div < 1) return -2;
+    for (int64_t r = 0; r < m_rows; r++) {
+        int64_t slot = slot_ids[r];
+        int64_t ar = r / a_row_div;
+        if (slot < 0) {
+            for (int64_t n = 0; n < N; n++) store_elem(out, out_dt, r * out_stride + n, 0.0f);
+            continue;
+        }
+        if (slot >= n_experts) return -2;
+        mx_gemm_row(lut8, a_q + ar * a_stride, a_s + ar * a_s_stride, w4 + slot * w4_stride_e, w4_stride_n,
+                    w4_s + slot * w4s_stride_e, w4s_stride_n, N, K, out, out_dt, r * out_stride);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* O4                                                                 */
 /* ------------------------------------------------------------------ */
 

@@ -81,6 +81,26 @@ int orc_block_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64
                    int64_t m_rows, int64_t a_row_div,
                    void* out, int out_dt, int64_t out_stride);
 
+/* ---- O8: block-FP8 activations x MXFP4 weights ----
+ * The FP4 weight variant of O3 ("perf(dsfp4): pick the grouped-prefill tile from route density on
+ * sm_89": the routed-expert prefill kernel whose weights are FP4 and whose cost is dequantization).
+ * The page does not fix the FP4 format; the reading taken is OCP MXFP4: E2M1 elements (sign, 2
+ * exponent bits with bias 1, 1 mantissa bit: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}), two per byte with K
+ * element 2i in the low nibble, and one E8M0 scale (2^(e - 127), e = 255 NaN) per 32 consecutive K
+ * elements.  w4 [n_experts] x [N][K/2] bytes (strides in bytes), w4_s [n_experts] x [N][K/32] bytes.
+ * Activations and their 1x128 fp32 scales as in O3.  Per 128-K block kb, p = sum over its k in
+ * ascending order of dq8(a[k]) * (dq4(w[k]) * 2^(e[k/32] - 127)) (each product exact), then
+ * acc = acc + p * a_s[kb].  Modes as in O3.  K % 128 == 0. */
+float orc_e2m1_to_f32(uint8_t code);
+float orc_e8m0_to_f32(uint8_t e);
+int orc_mxfp4_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                   const uint8_t* w4, int64_t w4_stride_e, int64_t w4_stride_n,
+                   const uint8_t* w4_s, int64_t w4s_stride_e, int64_t w4s_stride_n,
+                   int64_t n_experts, int64_t N, int64_t K,
+                   int mode, const int32_t* expert_offsets, const int32_t* slot_ids,
+                   int64_t m_rows, int64_t a_row_div,
+                   void* out, int out_dt, int64_t out_stride);
+
 /* ---- O4: gated activation + requant ----
  * in: rows x 2n (gate g = columns [0,n), up u = columns [n,2n)) of type in_dt.  h in fp32, then O1
  * on h.  The activations are the five GLU variants ("GLU Variants Improve Transformer", the gated

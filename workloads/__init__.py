@@ -64,6 +64,17 @@ def block_fp8_weights(E: int, N: int, K: int, seed: int, std: float = 0.02, devi
     return w_q, w_s
 
 
+def mxfp4_weights(E: int, N: int, K: int, seed: int, device="cpu", e_lo: int = 120, e_hi: int = 122):
+    """MXFP4 expert weights drawn directly as codes: w4 [E, N, K/2] uint8 (two E2M1 codes per byte,
+    every nibble uniform over the 16 codes) and w4_s [E, N, K/32] uint8 E8M0 exponents uniform in
+    [e_lo, e_hi] (2^-7 .. 2^-5 by default, so weights span about +-0.2 like N(0, 0.02) banks' tails)."""
+    g = _gen(seed, device)
+    w4 = torch.randint(0, 256, (E, N, K // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    w4_s = torch.randint(e_lo, e_hi + 1, (E, N, K // 32), generator=g, device=device,
+                         dtype=torch.int32).to(torch.uint8)
+    return w4, w4_s
+
+
 def bf16_normal(shape, seed: int, device="cpu", std: float = 1.0) -> torch.Tensor:
     g = _gen(seed, device)
     return (torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std).to(torch.bfloat16)
