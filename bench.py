@@ -266,6 +266,49 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
 
 
+def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
+    """The grouped GEMMs with MXFP4 expert weights (E2M1 codes, an E8M0 scale per 32 K) on the same routes:
+    gate/up with the SiLU-mul requant fused, gate/up to bf16, and down to bf16."""
+    dev = torch.device("cuda")
+    rt = wl.prefill_routes(T, E, topk, seed=9)
+    R = T * topk
+    offs = torch.from_numpy(rt.expert_offsets).to(dev)
+    (w13, w13_s), (w2, w2_s) = weights
+    a1_q, a1_s = wl.fp8_rows(R, H, seed=23, device=dev)
+    a2_q, a2_s = wl.fp8_rows(R, I, seed=24, device=dev)
+    c1 = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev)
+    c2 = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+    aq = torch.empty((R, I), dtype=torch.uint8, device=dev)
+    as_ = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
+    touched = int((rt.expert_offsets[1:] > rt.expert_offsets[:-1]).sum())
+    calls = {
+        "gate_up_act_quant": (lambda: m.mxfp4_grouped_gemm_act_quant(a1_q, a1_s, w13, w13_s, offs, aq, as_),
+                              2 * I, H, R * (I + 4 * I // 128)),
+        "gate_up": (lambda: m.mxfp4_grouped_gemm(a1_q, a1_s, w13, w13_s, offs, c1), 2 * I, H, R * 2 * I * 2),
+        "down": (lambda: m.mxfp4_grouped_gemm(a2_q, a2_s, w2, w2_s, offs, c2), H, I, R * H * 2),
+    }
+    out = {}
+    for name, (fn, N, K, out_bytes) in calls.items():
+        for _ in range(3):
+            fn()
+        t = Timer(torch)
+        for _ in range(steps):
+            t.start()
+            fn()
+            t.stop()
+        us = statistics.median(t.us())
+        flops = 2.0 * R * N * K
+        nbytes = touched * (N * K // 2 + N * K // 32) + R * (K + 4 * K // 128) + out_bytes
+        tflops = flops / (us * 1e-6) / 1e12
+        ai = flops / nbytes
+        attainable = min(FP8_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1000.0)
+        out[name] = dict(us_median=us, tflops=tflops, fp8_peak_frac=tflops / FP8_PEAK_TFLOPS,
+                         roofline_frac=tflops / attainable, arithmetic_intensity=ai, bytes=nbytes,
+                         hbm_gbs=nbytes / (us * 1e-6) / 1e9)
+    return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=m.pick_block_m(R, E),
+                weights="MXFP4 (E2M1 + E8M0 per 32 K)", **out)
+
+
 def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     """One whole prefill layer on the device from router logits: routing prep, input quant, gather,
     fused gate/up + SiLU-mul requant, down GEMM, top-k reduce (timed per layer with events)."""
@@ -317,13 +360,22 @@ def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
 
 
 def prefill_all(torch, m, wl):
-    """The grouped GEMMs at 1536, 6144 and 24576 routes (E=256, top-6, H=4096, I=1024)."""
+    """The grouped GEMMs at 1536, 6144 and 24576 routes (E=256, top-6, H=4096, I=1024), with block-FP8 and
+    with MXFP4 expert weights."""
     weights = prefill_weights(torch, wl, 256, 4096, 1024)
     res = []
     for T in (256, 1024, 4096):
         log("prefill %d routes" % (T * 6))
         res.append(prefill_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights))
         res[-1]["layer"] = prefill_layer_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights)
+    del weights
+    torch.cuda.empty_cache()
+    dev = torch.device("cuda")
+    weights = (wl.mxfp4_weights(256, 2048, 4096, seed=31, device=dev), wl.mxfp4_weights(256, 4096, 1024, seed=32,
+                                                                                        device=dev))
+    for i, T in enumerate((256, 1024, 4096)):
+        log("prefill mxfp4 %d routes" % (T * 6))
+        res[i]["mxfp4"] = prefill_mxfp4_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights)
     del weights
     torch.cuda.empty_cache()
     return res

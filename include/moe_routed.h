@@ -24,10 +24,12 @@
  *               the row's k//128 fp32 scales; row bases in 64-bit; tails
  *               masked (k = 896 has 7 scale groups); an empty map is a no-op.
  *   [tile]      "perf(dsfp4): pick the grouped-prefill tile from route
- *               density on sm_89", Measurements / What is not the mechanism /
- *               Testing: the best M tile follows rows per expert (16, 32,
- *               128 at about 6, 24, 96 rows) and BLOCK_K is 128; the picker
- *               is a pure function of route and expert counts.
+ *               density on sm_89", The Hopper assumption / Measurements /
+ *               What is not the mechanism / Testing: the prefill kernel's
+ *               expert weights are FP4 and dequantizing them bounds it; the
+ *               best M tile follows rows per expert (16, 32, 128 at about 6,
+ *               24, 96 rows) and BLOCK_K is 128; the picker is a pure
+ *               function of route and expert counts.
  *
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
@@ -198,6 +200,52 @@ int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const f
                                    int64_t n_experts, int64_t I, int64_t K, const int32_t* expert_offsets,
                                    int64_t m_rows, int32_t block_m, int act, uint8_t* out_q, int64_t q_stride,
                                    float* out_s, int64_t s_stride, void* stream);
+
+/*
+ * moe_mxfp4_grouped_gemm  -- the grouped (prefill) GEMM with FP4 expert weights
+ *   [tile]: the routed-expert prefill kernel of that page takes FP4 weights and
+ *   is limited by dequantizing them.  The page does not fix the FP4 format;
+ *   the one taken is OCP MXFP4: E2M1 elements (+-{0, 0.5, 1, 1.5, 2, 3, 4, 6}),
+ *   two per byte with K element 2i in the low nibble, and one E8M0 scale byte
+ *   (2^(e-127)) per 32 consecutive K elements.
+ *   out[r, n] = sum_kb ( sum_{k in kb} A[r, k] * W[e, n, k] * 2^(w4_s[e, n, k/32] - 127) ) * a_s[r, kb]
+ *   with products exact and fp32 accumulation (kb = 128-wide K blocks).
+ *   a_q, a_s: fp8 activations with 1x128 fp32 scales, as moe_bf8_grouped_gemm.
+ *   w4   [n_experts] x [N][K/2] bytes: the byte of (e, n, k) is at
+ *        e*w4_stride_e + n*w4_stride_n + k/2 (strides in BYTES).
+ *   w4_s [n_experts] x [N][K/32] E8M0 bytes: block (e, n, k/32) at
+ *        e*w4s_stride_e + n*w4s_stride_n + k/32 (strides in bytes).
+ *   expert_offsets, m_rows, block_m, out, out_dt, out_stride: as
+ *   moe_bf8_grouped_gemm in MOE_MODE_GROUPED.
+ *   Requirements: N % 128 == 0, K % 128 == 0, K <= 8192, 1 <= n_experts <=
+ *   1024 (MOE_ERR_SHAPE); a_q, w4 and their strides 16-byte aligned, w4_s and
+ *   its strides 4-byte aligned (MOE_ERR_ALIGN).  A scale byte of 255 (NaN in
+ *   the format) gives results this library does not define, and so do scaled
+ *   products below the fp32 normal range.  m_rows == 0 launches nothing.
+ */
+int moe_mxfp4_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                           const uint8_t* w4, int64_t w4_stride_e, int64_t w4_stride_n,
+                           const uint8_t* w4_s, int64_t w4s_stride_e, int64_t w4s_stride_n,
+                           int64_t n_experts, int64_t N, int64_t K, const int32_t* expert_offsets,
+                           int64_t m_rows, int32_t block_m, void* out, int out_dt, int64_t out_stride,
+                           void* stream);
+
+/*
+ * moe_mxfp4_grouped_gemm_act_quant  -- moe_bf8_grouped_gemm_act_quant with
+ *   MXFP4 gate/up weights  [tile] [inactive]
+ *   c1 is the fp32 result of moe_mxfp4_grouped_gemm with N = 2I (W13 rows
+ *   0..I-1 gate, I..2I-1 up), never stored; the gated activation and its
+ *   1x128 requant into out_q / out_s are those of
+ *   moe_bf8_grouped_gemm_act_quant.  The results equal moe_mxfp4_grouped_gemm
+ *   with MOE_F32 output followed by moe_act_quant with the same act, bit for
+ *   bit.  Requirements: I % 128 == 0 and the rest as moe_mxfp4_grouped_gemm.
+ */
+int moe_mxfp4_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                                     const uint8_t* w4, int64_t w4_stride_e, int64_t w4_stride_n,
+                                     const uint8_t* w4_s, int64_t w4s_stride_e, int64_t w4s_stride_n,
+                                     int64_t n_experts, int64_t I, int64_t K, const int32_t* expert_offsets,
+                                     int64_t m_rows, int32_t block_m, int act, uint8_t* out_q, int64_t q_stride,
+                                     float* out_s, int64_t s_stride, void* stream);
 
 /*
  * moe_topk_reduce  -- routing-weighted sum over each token's top-k routes

@@ -30,6 +30,7 @@ EXPORTS = (
     "moe_pick_block_m", "moe_bf8_grouped_gemm", "moe_topk_reduce", "moe_fused_decode_workspace_size",
     "moe_fused_decode_workspace_layout", "moe_fused_decode_workspace_init", "moe_fused_decode",
     "moe_route_prep_workspace_size", "moe_route_prep", "moe_bf8_grouped_gemm_act_quant",
+    "moe_mxfp4_grouped_gemm", "moe_mxfp4_grouped_gemm_act_quant",
 )
 
 _lib = None
@@ -72,6 +73,10 @@ def lib():
             "moe_route_prep": ([P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
             "moe_bf8_grouped_gemm_act_quant": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, P, I64,
                                                 I32, I32, P, I64, P, I64, P], I32),
+            "moe_mxfp4_grouped_gemm": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, P, I64,
+                                        I32, P, I32, I64, P], I32),
+            "moe_mxfp4_grouped_gemm_act_quant": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, P,
+                                                  I64, I32, I32, P, I64, P, I64, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -161,6 +166,38 @@ def bf8_grouped_gemm_act_quant(a_q, a_s, w13_q, w13_s, expert_offsets, out_q, ou
     _check("moe_bf8_grouped_gemm_act_quant", lib().moe_bf8_grouped_gemm_act_quant(
         _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
         _ptr(w13_q), w13_q.stride(0), w13_q.stride(1), _ptr(w13_s), w13_s.stride(0), w13_s.stride(1),
+        E, N // 2, K, _ptr(expert_offsets), m_rows, block_m, act, _ptr(out_q), _rowstride(out_q),
+        _ptr(out_s), _rowstride(out_s), _stream(stream)))
+
+
+def _mxfp4_weights(w4, w4_s):
+    E, N, K2 = w4.shape
+    assert w4.dtype == torch.uint8 and w4_s.dtype == torch.uint8, "MXFP4 weights are byte tensors"
+    assert w4.stride(2) == 1 and w4_s.stride(2) == 1 and tuple(w4_s.shape) == (E, N, K2 // 16)
+    return E, N, 2 * K2
+
+
+def mxfp4_grouped_gemm(a_q, a_s, w4, w4_s, expert_offsets, out, m_rows=None, block_m=0, stream=None):
+    """Grouped GEMM with MXFP4 weights: w4 [E, N, K/2] bytes (two E2M1 codes, even k in the low nibble),
+    w4_s [E, N, K/32] E8M0 bytes; a_q/a_s/out as bf8_grouped_gemm in grouped mode."""
+    E, N, K = _mxfp4_weights(w4, w4_s)
+    if m_rows is None:
+        m_rows = out.shape[0]
+    _check("moe_mxfp4_grouped_gemm", lib().moe_mxfp4_grouped_gemm(
+        _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
+        _ptr(w4), w4.stride(0), w4.stride(1), _ptr(w4_s), w4_s.stride(0), w4_s.stride(1),
+        E, N, K, _ptr(expert_offsets), m_rows, block_m, _ptr(out), _dt(out), _rowstride(out), _stream(stream)))
+
+
+def mxfp4_grouped_gemm_act_quant(a_q, a_s, w4, w4_s, expert_offsets, out_q, out_s, m_rows=None, block_m=0,
+                                 act=1, stream=None):
+    """bf8_grouped_gemm_act_quant with MXFP4 gate/up weights w4 [E, 2I, K/2], w4_s [E, 2I, K/32]."""
+    E, N, K = _mxfp4_weights(w4, w4_s)
+    if m_rows is None:
+        m_rows = out_q.shape[0]
+    _check("moe_mxfp4_grouped_gemm_act_quant", lib().moe_mxfp4_grouped_gemm_act_quant(
+        _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
+        _ptr(w4), w4.stride(0), w4.stride(1), _ptr(w4_s), w4_s.stride(0), w4_s.stride(1),
         E, N // 2, K, _ptr(expert_offsets), m_rows, block_m, act, _ptr(out_q), _rowstride(out_q),
         _ptr(out_s), _rowstride(out_s), _stream(stream)))
 

@@ -24,6 +24,12 @@ int grouped_gemm_act_quant_launch(hipStream_t st, int block_m, int act, const ui
                                   int64_t w_stride_n, const float* w_s, int64_t w_s_stride_e,
                                   int64_t w_s_stride_n, int64_t E, int64_t I, int64_t K, const int32_t* offsets,
                                   int64_t m_rows, uint8_t* q, int64_t q_stride, float* s, int64_t s_stride);
+int mxfp4_grouped_gemm_launch(hipStream_t st, int block_m, int act, const uint8_t* a_q, int64_t a_stride,
+                              const float* a_s, int64_t a_s_stride, const uint8_t* w4, int64_t w4_stride_e,
+                              int64_t w4_stride_n, const uint8_t* w4s, int64_t w4s_stride_e, int64_t w4s_stride_n,
+                              int64_t E, int64_t N, int64_t K, const int32_t* offsets, int64_t m_rows, void* out,
+                              int out_dt, int64_t out_stride, uint8_t* q, int64_t q_stride, float* s,
+                              int64_t s_stride);
 int topk_reduce_launch(hipStream_t st, const void* y, int y_dt, int64_t y_stride, const int32_t* slot_ids,
                        const int32_t* route_rows, const float* weights, int64_t T, int64_t topk, int64_t H,
                        uint16_t* out, int64_t out_stride);
@@ -164,6 +170,69 @@ extern "C" int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stri
     return grouped_gemm_act_quant_launch(as_stream(stream), bm, act, a_q, a_stride, a_s, a_s_stride, w_q,
                                          w_stride_e, w_stride_n, w_s, w_s_stride_e, w_s_stride_n, n_experts, I, K,
                                          expert_offsets, m_rows, out_q, q_stride, out_s, s_stride);
+}
+
+namespace {
+
+// Checks shared by the two MXFP4 entry points (N = 2I for the fused one); MOE_OK when the operands fit.
+int mxfp4_args_ok(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                  const uint8_t* w4, int64_t w4_stride_e, int64_t w4_stride_n, const uint8_t* w4s,
+                  int64_t w4s_stride_e, int64_t w4s_stride_n, int64_t n_experts, int64_t N, int64_t K,
+                  const int32_t* expert_offsets) {
+    if (!a_q || !a_s || !w4 || !w4s || !expert_offsets) return MOE_ERR_NULL;
+    if (a_stride < K || a_s_stride < K / 128 || w4_stride_n < K / 2 || w4s_stride_n < K / 32) return MOE_ERR_SHAPE;
+    if (n_experts > 1 && (w4_stride_e < N * w4_stride_n || w4s_stride_e < N * w4s_stride_n)) return MOE_ERR_SHAPE;
+    if (!aligned16(a_q) || a_stride % 16 || !aligned16(w4) || w4_stride_n % 16 || w4_stride_e % 16)
+        return MOE_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(w4s) % 4 || w4s_stride_n % 4 || w4s_stride_e % 4) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" int moe_mxfp4_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
+                                      const uint8_t* w4, int64_t w4_stride_e, int64_t w4_stride_n,
+                                      const uint8_t* w4_s, int64_t w4s_stride_e, int64_t w4s_stride_n,
+                                      int64_t n_experts, int64_t N, int64_t K, const int32_t* expert_offsets,
+                                      int64_t m_rows, int32_t block_m, void* out, int out_dt, int64_t out_stride,
+                                      void* stream) {
+    if (!dtype_ok(out_dt)) return MOE_ERR_DTYPE;
+    if (m_rows < 0 || n_experts < 1 || n_experts > 1024 || N < 128 || N % 128 || K < 128 || K % 128 || K > 8192)
+        return MOE_ERR_SHAPE;
+    if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_SHAPE;
+    if (m_rows == 0) return MOE_OK;
+    if (!out) return MOE_ERR_NULL;
+    if (out_stride < N) return MOE_ERR_SHAPE;
+    const int rc = mxfp4_args_ok(a_q, a_stride, a_s, a_s_stride, w4, w4_stride_e, w4_stride_n, w4_s, w4s_stride_e,
+                                 w4s_stride_n, n_experts, N, K, expert_offsets);
+    if (rc != MOE_OK) return rc;
+    const int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
+    return mxfp4_grouped_gemm_launch(as_stream(stream), bm, 0, a_q, a_stride, a_s, a_s_stride, w4, w4_stride_e,
+                                     w4_stride_n, w4_s, w4s_stride_e, w4s_stride_n, n_experts, N, K, expert_offsets,
+                                     m_rows, out, out_dt, out_stride, nullptr, 0, nullptr, 0);
+}
+
+extern "C" int moe_mxfp4_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s,
+                                                int64_t a_s_stride, const uint8_t* w4, int64_t w4_stride_e,
+                                                int64_t w4_stride_n, const uint8_t* w4_s, int64_t w4s_stride_e,
+                                                int64_t w4s_stride_n, int64_t n_experts, int64_t I, int64_t K,
+                                                const int32_t* expert_offsets, int64_t m_rows, int32_t block_m,
+                                                int act, uint8_t* out_q, int64_t q_stride, float* out_s,
+                                                int64_t s_stride, void* stream) {
+    if (m_rows < 0 || n_experts < 1 || n_experts > 1024 || I < 128 || I % 128 || K < 128 || K % 128 || K > 8192)
+        return MOE_ERR_SHAPE;
+    if (act < MOE_ACT_SILU_MUL || act > MOE_ACT_MUL) return MOE_ERR_SHAPE;
+    if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_SHAPE;
+    if (m_rows == 0) return MOE_OK;
+    if (!out_q || !out_s) return MOE_ERR_NULL;
+    if (q_stride < I || s_stride < I / 128) return MOE_ERR_SHAPE;
+    const int rc = mxfp4_args_ok(a_q, a_stride, a_s, a_s_stride, w4, w4_stride_e, w4_stride_n, w4_s, w4s_stride_e,
+                                 w4s_stride_n, n_experts, 2 * I, K, expert_offsets);
+    if (rc != MOE_OK) return rc;
+    const int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
+    return mxfp4_grouped_gemm_launch(as_stream(stream), bm, act, a_q, a_stride, a_s, a_s_stride, w4, w4_stride_e,
+                                     w4_stride_n, w4_s, w4s_stride_e, w4s_stride_n, n_experts, 2 * I, K,
+                                     expert_offsets, m_rows, nullptr, MOE_F32, 0, out_q, q_stride, out_s, s_stride);
 }
 
 extern "C" size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk) {

@@ -143,6 +143,17 @@ __device__ __forceinline__ v4f mfma16x16x128_e4m3(const v8i& a, const v8i& b, co
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// 16x16x128 MFMA with an MXFP4 row operand and an fp8 (e4m3) column operand (layout checked on gfx950):
+// the fp4 operand's lane l holds row l%16 and the 32 consecutive K elements 32*(l/16) .. +31 as 16 bytes
+// in the low four dwords of w, K element 2i in the low nibble; the fp8 operand is laid out as in
+// mfma16x16x128_e4m3.  Scales are E8M0 bytes (low byte of the word): the scale of K block b for row x
+// comes from lane 16b + x, which is the lane that holds that block, so each lane passes its own block's
+// scale; the column operand's scale is 2^0.
+__device__ __forceinline__ v4f mfma16x16x128_fp4_e4m3(const v4i& w, uint32_t w_scale, const v8i& a, const v4f& c) {
+    const v8i w8 = {w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w8, a, c, 4, 0, 0, (int)w_scale, 0, 127);
+}
+
 // Orders this wave's LDS accesses before/after the call (compiler and memory
 // model, wavefront scope).  Valid only for data written and read by one wave.
 __device__ __forceinline__ void wave_lds_fence() {

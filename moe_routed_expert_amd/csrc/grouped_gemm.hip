@@ -36,6 +36,14 @@
 //    XCD's workgroups take its range in order, so the tiles in flight on an XCD
 //    are neighbouring N tiles of neighbouring M tiles: their A rows and weight
 //    tiles meet in that XCD's L2, and every XCD gets the same number of tiles.
+//  * MXFP4 weights (the FP4 variant): a lane's 32 K elements of a step are one
+//    MX block, 16 contiguous bytes, and the block's E8M0 scale is applied inside
+//    v_mfma_scale_f32_16x16x128_f8f6f4, so the weight stream is half the bytes
+//    and there is no per-block fp32 weight scale.  The scale bytes do not ride
+//    in the ring: a 4-byte load per row and step touches 16 rows for 64 bytes,
+//    and those loads cost as much as the weights.  Each wave instead copies its
+//    32 rows' scales for 32 steps into LDS with row-contiguous loads (one per
+//    lane per row pair) and reads a step's dword from there.
 //  * A tile's expert is a binary search of the LDS table; its scales are
 //    loaded row-contiguous, all requests in flight before the LDS stores.
 //  * Fused activation requant (the gate/up GEMM of a prefill step with the
@@ -54,6 +62,7 @@ namespace moe {
 constexpr int kXcds = 8;
 constexpr int kMaxExpertsScan = 1024;            // experts handled by the in-kernel scan
 constexpr int kGgMaxKb = 64;                     // K/128 blocks whose scales a tile keeps in LDS (K <= 8192)
+constexpr int kScRow = 132;                      // MXFP4: LDS bytes per weight row of a 128-block scale chunk
 
 // Tile configuration per M tile: always 8 waves of two 16-column MFMA tiles, 256 columns (which
 // halves how often the A tile is re-read compared with a 128-column tile).  Up to 64 rows the
@@ -93,6 +102,9 @@ struct GgArgs {
     float* s;                                 // fused: scales [rows][s_stride], I/128 used
     int64_t s_stride;
     int act;                                  // fused: gated activation (moe_act 1..5)
+    // MXFP4 weights (W4 variant): w_q holds [e][n][K/2] bytes (strides in bytes), w4s [e][n][K/32] E8M0
+    const uint8_t* w4s;
+    int64_t w4s_stride_e, w4s_stride_n;
 };
 
 // Exclusive scan of one int per thread over a block of WAVES waves.
@@ -163,7 +175,7 @@ __device__ __forceinline__ void act_quant_epilogue(const GgArgs& g, v4f (&acc)[B
 // One tile: rows [row0, min(row0 + BM, row_end)) of expert `expert`, N tile n_tile (256 output
 // columns, or act group n_tile when FUSED).  The caller's workgroup runs it with all threads; it
 // leaves LDS free for the next tile (its last LDS read is before its last barrier).
-template <int BM, int OUT_DT, bool FUSED>
+template <int BM, int OUT_DT, bool FUSED, bool W4>
 __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, int row0, int row_end, int n_tile) {
     const uint8_t* __restrict__ a_q = g.a_q;
     const float* __restrict__ a_s = g.a_s;
@@ -176,7 +188,8 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     constexpr int TPW = C::TPW;
     constexpr int CPW = 16 * TPW;               // columns per wave
     constexpr int MS = BM / 16;                 // 16-row MFMA sub-tiles
-    constexpr int S = C::S;                     // W ring depth
+    constexpr int SA = C::S;                    // A register stages
+    constexpr int S = C::S;                     // W ring depth; SA divides it, so both indices stay static
     constexpr int NT = C::THREADS;
     constexpr int A_CHUNKS = BM * 8;            // 16-byte chunks of one A K-step
     constexpr int A_PER_THREAD = (A_CHUNKS + NT - 1) / NT;
@@ -184,6 +197,9 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     __shared__ __attribute__((aligned(32))) uint8_t a_lds[2][BM * 128];
     __shared__ __attribute__((aligned(16))) float sa_lds[kGgMaxKb * SA_ROW];   // A scales, [kb][row]
     __shared__ float ws_lds[2][kGgMaxKb];                                       // weight scales, [block][kb]
+    // MXFP4: each wave's E8M0 bytes of its 32 weight rows, 128 blocks (32 K steps) at a time; a row
+    // takes kScRow bytes so the 16 rows one read touches fall in different banks
+    __shared__ __attribute__((aligned(16))) uint8_t sc_lds[W4 ? C::WAVES * 32 * kScRow : 4];
 
     // A fresh copy of the thread index per tile: without it the compiler hoists every thread-index
     // expression of the tile out of the caller's tile loop and keeps them all live across it.
@@ -203,6 +219,32 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     const int64_t wcol = FUSED ? (int64_t)n_tile * 128 + 16 * wv : (cols ? n0 + wv * CPW : n0);
     const uint8_t* wp0 = w_q + (int64_t)expert * w_stride_e + (wcol + (lane & 15)) * w_stride_n + q16;
     const uint8_t* wp1 = wp0 + (FUSED ? I : 16) * w_stride_n;
+    // MXFP4 scales.  A chunk is 128 blocks (32 K steps) of the wave's 32 rows: lanes 0-31 read one row's
+    // 128 bytes as 32 dwords and lanes 32-63 the next row, 16 loads per lane, all requested before the
+    // first LDS store.  In a step the lane's K block is 4 kb + lane/16; it reads the row's dword of the
+    // step from LDS and takes its byte.
+    uint8_t* const sc_wave = sc_lds + wave * 32 * kScRow;
+    // (a wave-uniform row base plus one 32-bit lane offset, so the 16 addresses cost no vector registers)
+    const uint8_t* const sc_base = W4 ? g.w4s + (int64_t)expert * g.w4s_stride_e + wcol * g.w4s_stride_n : nullptr;
+    const int64_t sc_sub = (FUSED ? I : 16) * g.w4s_stride_n;     // sub-tile 1 rows
+    uint32_t sc_v[16];
+    auto sc_issue = [&](int kb0, int i0, int ni) {  // words i0 .. i0+ni-1 of the chunk from step kb0
+        int l = lane;
+        asm volatile("" : "+v"(l));                 // per call: keeps the lane terms out of the step loop
+        const bool in = (l & 31) < nkb - kb0;     // a chunk stage may load a step beyond the chunk: unused
+        const uint32_t lo = (uint32_t)((l >> 5) * g.w4s_stride_n + 4 * (l & 31));
+#pragma unroll
+        for (int i = i0; i < i0 + ni; i++) {        // rows 2i + lane/32 of the wave: sub-tile i/8
+            const uint8_t* u = sc_base + (i / 8) * sc_sub + (2 * (i % 8)) * g.w4s_stride_n + 4 * (int64_t)kb0;
+            sc_v[i] = in ? *reinterpret_cast<const uint32_t*>(u + lo) : 0u;
+        }
+    };
+    auto sc_commit = [&](int i0, int ni) {
+#pragma unroll
+        for (int i = i0; i < i0 + ni; i++)
+            *reinterpret_cast<uint32_t*>(sc_wave + (2 * i + (lane >> 5)) * kScRow + 4 * (lane & 31)) = sc_v[i];
+    };
+    const int sshift = 8 * (lane / 16);
     const int wsb = FUSED ? 0 : (int)((wcol - n0) / 128);   // this wave's 128-column scale block
 
     // All scales of the tile go to LDS once: A scales [kb][row] (wave w reads rows w, w + WAVES, ...,
@@ -220,14 +262,14 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     }
     const int64_t nblk = (N - n0) >= 256 ? 2 : 1;
     float ws_v = 0.0f;
-    if (wave < 2) {
+    if (!W4 && wave < 2) {
         const int64_t b = FUSED ? (wave == 0 ? n_tile : I / 128 + n_tile) : n0 / 128 + (wave < nblk ? wave : 0);
         ws_v = w_s[(int64_t)expert * w_s_stride_e + b * w_s_stride_n + kbl];
     }
     if (lane < nkb) {
 #pragma unroll
         for (int j = 0; j < SA_ROWS; j++) sa_lds[lane * SA_ROW + wave + j * C::WAVES] = sa_v[j];
-        if (wave < 2) ws_lds[wave][lane] = ws_v;
+        if (!W4 && wave < 2) ws_lds[wave][lane] = ws_v;
     }
 
     // A staging: chunk c of the BM x 128 K-step -> row c/8, byte 16*(c%8); stored in fragment order.
@@ -246,13 +288,13 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
         a_dst[j] = (rr / 16) * 2048 + ((rr % 16) + 16 * (ch % 4)) * 32 + (ch / 4) * 16;
     }
 
-    // A K steps pass through S register stages (step kb in stage kb % S) on their way to LDS, W K
+    // A K steps pass through SA register stages (step kb in stage kb % SA) on their way to LDS, W K
     // steps through an S-slot register ring.  Every load in the loop is unconditional (indices
     // past the last step are clamped to it; those steps skip their multiply), so the compiler can
     // count loads in flight exactly: loads retire in order, and a load it cannot count would make
     // a step wait for all of them.  Each step's A is requested before its W, so copying A step
     // kb+1 into LDS never waits on W steps issued after it, and W keeps S-1 steps of lead.
-    v4i a_reg[S][A_PER_THREAD];
+    v4i a_reg[SA][A_PER_THREAD];
     auto load_a = [&](int kb, int stage) {
 #pragma unroll
         for (int j = 0; j < A_PER_THREAD; j++)
@@ -266,6 +308,12 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     };
     v4i w_ring[S][2 * TPW];
     auto load_w = [&](int kb, v4i* w) {
+        if constexpr (W4) {
+            const int64_t o = (int64_t)kb * 64;
+            w[0] = *reinterpret_cast<const v4i*>(wp0 + o);
+            w[1] = *reinterpret_cast<const v4i*>(wp1 + o);
+            return;
+        }
         const int64_t o = (int64_t)kb * 128;
         w[0] = *reinterpret_cast<const v4i*>(wp0 + o);
         w[1] = *reinterpret_cast<const v4i*>(wp0 + o + 64);
@@ -282,30 +330,58 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
         for (int c = 0; c < TPW; c++) acc[m][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int last = nkb - 1;
-    // prologue: A steps 0 and 1, W steps 0..S-2 requested; A step 0 in LDS
+    // prologue: the first scale chunk, A steps 0 and 1, W steps 0..S-2 requested; scales and A step 0
+    // in LDS (the chunk's loads are the oldest, so its stores wait for nothing else)
+    if constexpr (W4) sc_issue(0, 0, 16);
     load_a(0, 0);
-    load_a(1 < last ? 1 : last, 1 % S);
+    load_a(1 < last ? 1 : last, 1 % SA);
 #pragma unroll
     for (int s = 0; s < S - 1; s++) load_w(s < last ? s : last, w_ring[s]);
+    if constexpr (W4) sc_commit(0, 16);
     store_a(0, 0);
     __syncthreads();
     const int nsteps = (nkb + S - 1) / S * S;
+    // MXFP4: a scale chunk spans kScSteps K steps (a multiple of S, at most 32); sc_kb is its first step
+    constexpr int kScSteps = 32 / S * S;
+    int sc_kb = 0;
     for (int kb0 = 0; kb0 < nsteps; kb0 += S) {
+        if constexpr (W4) {
+            if (kb0 - sc_kb == kScSteps && kb0 < nkb) {  // next chunk (K > 32 steps): this wave's rows only,
+                sc_kb = kb0;                              // a few words at a time to bound the registers
+                wave_lds_fence();
+#pragma unroll
+                for (int i0 = 0; i0 < 16; i0 += 4) {
+                    sc_issue(kb0, i0, 4);
+                    sc_commit(i0, 4);
+                }
+                wave_lds_fence();
+            }
+        }
 #pragma unroll
         for (int s = 0; s < S; s++) {
             const int kb = kb0 + s;
             // A step kb+2 into the stage step kb-1 left, W step kb+S-1 into the slot freed last step
-            load_a(kb + 2 < last ? kb + 2 : last, (s + 2) % S);
+            load_a(kb + 2 < last ? kb + 2 : last, (s + 2) % SA);
             load_w(kb + S - 1 < last ? kb + S - 1 : last, w_ring[(s + S - 1) % S]);
             const int buf = kb & 1;
             if (kb < nkb) {
+                uint32_t scw[TPW];                        // MXFP4: the E8M0 dword of the step, per sub-tile
+                if constexpr (W4) {
+#pragma unroll
+                    for (int c = 0; c < TPW; c++)
+                        scw[c] = *reinterpret_cast<const uint32_t*>(sc_wave + (16 * c + (lane & 15)) * kScRow +
+                                                                    4 * (kb - sc_kb));
+                }
                 float sw[TPW];                            // sub-tile c's weight scale (fused: gate, up)
 #pragma unroll
-                for (int c = 0; c < TPW; c++) sw[c] = ws_lds[FUSED ? c : wsb][kb];
+                for (int c = 0; c < TPW; c++) sw[c] = W4 ? 1.0f : ws_lds[FUSED ? c : wsb][kb];
                 v8i b[TPW];
+                uint32_t e8[TPW];
 #pragma unroll
-                for (int c = 0; c < TPW; c++)
+                for (int c = 0; c < TPW; c++) {
                     b[c] = __builtin_shufflevector(w_ring[s][2 * c], w_ring[s][2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    if constexpr (W4) e8[c] = (scw[c] >> sshift) & 0xFFu;
+                }
 #pragma unroll
                 for (int m = 0; m < MS; m++) {
                     // W is the MFMA's row operand and A its column operand, so a lane's four results
@@ -314,10 +390,15 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                     const float sa = sa_lds[kb * SA_ROW + m * 16 + (lane & 15)];
 #pragma unroll
-                    for (int c = 0; c < TPW; c++) acc[m][c] += mfma16x16x128_e4m3(b[c], a, zero) * (sa * sw[c]);
+                    for (int c = 0; c < TPW; c++) {
+                        if constexpr (W4)
+                            acc[m][c] += mfma16x16x128_fp4_e4m3(w_ring[s][c], e8[c], a, zero) * sa;
+                        else
+                            acc[m][c] += mfma16x16x128_e4m3(b[c], a, zero) * (sa * sw[c]);
+                    }
                 }
             }
-            store_a((s + 1) % S, buf ^ 1);            // A step kb+1 (requested a step ago)
+            store_a((s + 1) % SA, buf ^ 1);           // A step kb+1 (requested a step ago)
             __syncthreads();
         }
     }
@@ -349,7 +430,7 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     }
 }
 
-template <int BM, int OUT_DT, bool FUSED>
+template <int BM, int OUT_DT, bool FUSED, bool W4>
 __global__ void __launch_bounds__(GgCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(GgCfg<BM>::WAVES_PER_EU, 8)))
 grouped_gemm_kernel(GgArgs g) {
     const int32_t* __restrict__ offsets = g.offsets;
@@ -410,7 +491,7 @@ grouped_gemm_kernel(GgArgs g) {
         const int row0 = __builtin_amdgcn_readfirstlane(off_lds[expert]) +
                          (m_tile - __builtin_amdgcn_readfirstlane(cum_lds[expert])) * BM;
         const int row_end = __builtin_amdgcn_readfirstlane(off_lds[expert + 1]);
-        grouped_gemm_tile<BM, OUT_DT, FUSED>(g, expert, row0, row_end, n_tile);
+        grouped_gemm_tile<BM, OUT_DT, FUSED, W4>(g, expert, row0, row_end, n_tile);
         m_tile += step_m;
         n_tile += step_n;
         if (n_tile >= n_tiles_n) {
@@ -421,7 +502,7 @@ grouped_gemm_kernel(GgArgs g) {
 }
 
 // Workgroups of one configuration the device holds at once (cached per device and variant).
-template <int BM, int OUT_DT, bool FUSED>
+template <int BM, int OUT_DT, bool FUSED, bool W4>
 static int gg_resident_blocks() {
     using C = GgCfg<BM>;
     static int cached[64];
@@ -430,7 +511,7 @@ static int gg_resident_blocks() {
     int& c = cached[dev];
     if (c == 0) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, OUT_DT, FUSED>, C::THREADS,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, OUT_DT, FUSED, W4>, C::THREADS,
                                                          0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -440,41 +521,47 @@ static int gg_resident_blocks() {
 }
 
 // Fills the tile walk of g (N tiles of BN columns, or I/128 act groups when fused) and launches.
-template <int BM, int OUT_DT, bool FUSED>
+template <int BM, int OUT_DT, bool FUSED, bool W4>
 static int launch_grouped(hipStream_t st, GgArgs g) {
     using C = GgCfg<BM>;
     if (g.N % 128 != 0 || (FUSED && g.N % 256 != 0)) return MOE_ERR_SHAPE;
     const int64_t n_tiles_n = FUSED ? g.N / 256 : ceil_div(g.N, C::BN);
     if (g.m_rows > 0x7FFFFFFF || n_tiles_n * (ceil_div(g.m_rows, BM) + g.n_experts) > 0x7FFFFFFF - (1 << 20))
         return MOE_ERR_SHAPE;
-    const int wgs = gg_resident_blocks<BM, OUT_DT, FUSED>();
+    const int wgs = gg_resident_blocks<BM, OUT_DT, FUSED, W4>();
     if (wgs < kXcds) return MOE_ERR_HIP;
     g.n_tiles_n = (int)n_tiles_n;
     g.per_xcd = wgs / kXcds;
     g.step_m = g.per_xcd / g.n_tiles_n;
     g.step_n = g.per_xcd % g.n_tiles_n;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, OUT_DT, FUSED>), dim3((unsigned)(g.per_xcd * kXcds)),
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, OUT_DT, FUSED, W4>), dim3((unsigned)(g.per_xcd * kXcds)),
                        dim3(C::THREADS), 0, st, g);
     return launch_status();
 }
 
-template <int BM>
+template <int BM, bool W4>
 static int launch_grouped_dt(hipStream_t st, int out_dt, bool fused, const GgArgs& g) {
-    if (fused) return launch_grouped<BM, kF32, true>(st, g);
-    if (out_dt == MOE_F32) return launch_grouped<BM, kF32, false>(st, g);
-    if (out_dt == MOE_BF16) return launch_grouped<BM, kBF16, false>(st, g);
-    return launch_grouped<BM, kF16, false>(st, g);
+    if (fused) return launch_grouped<BM, kF32, true, W4>(st, g);
+    if (out_dt == MOE_F32) return launch_grouped<BM, kF32, false, W4>(st, g);
+    if (out_dt == MOE_BF16) return launch_grouped<BM, kBF16, false, W4>(st, g);
+    return launch_grouped<BM, kF16, false, W4>(st, g);
+}
+
+template <bool W4>
+static int grouped_launch_w(hipStream_t st, int block_m, int out_dt, bool fused, const GgArgs& g) {
+    switch (block_m) {
+        case 16: return launch_grouped_dt<16, W4>(st, out_dt, fused, g);
+        case 32: return launch_grouped_dt<32, W4>(st, out_dt, fused, g);
+        case 64: return launch_grouped_dt<64, W4>(st, out_dt, fused, g);
+        case 128: return launch_grouped_dt<128, W4>(st, out_dt, fused, g);
+        default: return MOE_ERR_SHAPE;
+    }
 }
 
 static int grouped_launch_bm(hipStream_t st, int block_m, int out_dt, bool fused, const GgArgs& g) {
     if (g.n_experts > kMaxExpertsScan || g.K / 128 > kGgMaxKb) return MOE_ERR_SHAPE;
-    switch (block_m) {
-        case 16: return launch_grouped_dt<16>(st, out_dt, fused, g);
-        case 32: return launch_grouped_dt<32>(st, out_dt, fused, g);
-        case 64: return launch_grouped_dt<64>(st, out_dt, fused, g);
-        case 128: return launch_grouped_dt<128>(st, out_dt, fused, g);
-        default: return MOE_ERR_SHAPE;
-    }
+    return g.w4s ? grouped_launch_w<true>(st, block_m, out_dt, fused, g)
+                 : grouped_launch_w<false>(st, block_m, out_dt, fused, g);
 }
 
 int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t a_stride, const float* a_s,
@@ -489,6 +576,24 @@ int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t
     g.n_experts = (int)E; g.N = N; g.K = K; g.offsets = offsets; g.m_rows = (int)m_rows;
     g.out = out; g.out_stride = out_stride;
     return grouped_launch_bm(st, block_m, out_dt, false, g);
+}
+
+// MXFP4 weights: w4 [E][N][K/2] bytes, w4s [E][N][K/32] E8M0 (strides in bytes); out as the plain GEMM, or
+// (act > 0) the fused gated-activation requant into q/s.
+int mxfp4_grouped_gemm_launch(hipStream_t st, int block_m, int act, const uint8_t* a_q, int64_t a_stride,
+                              const float* a_s, int64_t a_s_stride, const uint8_t* w4, int64_t w4_stride_e,
+                              int64_t w4_stride_n, const uint8_t* w4s, int64_t w4s_stride_e, int64_t w4s_stride_n,
+                              int64_t E, int64_t N, int64_t K, const int32_t* offsets, int64_t m_rows, void* out,
+                              int out_dt, int64_t out_stride, uint8_t* q, int64_t q_stride, float* s,
+                              int64_t s_stride) {
+    GgArgs g{};
+    g.a_q = a_q; g.a_stride = a_stride; g.a_s = a_s; g.a_s_stride = a_s_stride;
+    g.w_q = w4; g.w_stride_e = w4_stride_e; g.w_stride_n = w4_stride_n;
+    g.w4s = w4s; g.w4s_stride_e = w4s_stride_e; g.w4s_stride_n = w4s_stride_n;
+    g.n_experts = (int)E; g.N = N; g.K = K; g.offsets = offsets; g.m_rows = (int)m_rows;
+    g.out = out; g.out_stride = out_stride;
+    g.q = q; g.q_stride = q_stride; g.s = s; g.s_stride = s_stride; g.act = act;
+    return grouped_launch_bm(st, block_m, out_dt, act > 0, g);
 }
 
 int grouped_gemm_act_quant_launch(hipStream_t st, int block_m, int act, const uint8_t* a_q, int64_t a_stride,

@@ -1,6 +1,8 @@
-"""Helpers shared by the GPU parity tests (comparison rules and tensor moves)."""
+"""Helpers shared by the GPU parity tests (comparison rules, error bounds and tensor moves)."""
 import numpy as np
 import torch
+
+import oracle
 
 REL_L2 = 5e-3       # bf16 outputs: relative L2 error bound
 MAX_ABS = 2e-2      # and max-abs error bound, relative to max |oracle|
@@ -69,6 +71,28 @@ def gemm_abs_bound(a_q, a_s, w_q, w_s, experts_of_rows, a_rows):
     return 2.0 * out * (K + 4 * K / 128 + 4) * 2.0 ** -23
 
 
+E2M1_ABS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0] * 2)   # |value| of each E2M1 code
+
+
+def mxfp4_abs_bound(a_q, a_s, w4, w4_s, experts_of_rows, a_rows):
+    """gemm_abs_bound for MXFP4 weights: the same (K + 4K/128 + 4) * 2^-23 * sum|terms| per side, with
+    |w[e, n, k]| = |e2m1(nibble)| * 2^(w4_s[e, n, k/32] - 127)."""
+    E, N, K2 = w4.shape
+    K = 2 * K2
+    A = _t_dec(a_q).abs() * torch.from_numpy(np.repeat(a_s, 128, axis=1)[:, :K]).double()
+    out = np.zeros((len(experts_of_rows), N))
+    cache = {}
+    for r, e in enumerate(experts_of_rows):
+        if e < 0:
+            continue
+        if e not in cache:
+            codes = np.stack([w4[e] & 15, w4[e] >> 4], axis=2).reshape(N, K)
+            scale = np.exp2(np.repeat(w4_s[e].astype(np.float64), 32, axis=1) - 127.0)
+            cache = {e: torch.from_numpy(E2M1_ABS[codes] * scale)}
+        out[r] = (cache[e] @ A[a_rows[r]]).numpy()
+    return 2.0 * out * (K + 4 * K / 128 + 4) * 2.0 ** -23
+
+
 def assert_within_bound(got, ref, bound, what=""):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
@@ -77,3 +101,56 @@ def assert_within_bound(got, ref, bound, what=""):
     bad = err > bound
     assert not bad.any(), "%s: %d elements beyond the fp32 accumulation bound (worst %.3e vs %.3e)" % (
         what, bad.sum(), err[bad].max(), bound[bad][np.argmax(err[bad])])
+
+
+NP_OUT = {torch.float32: np.float32, torch.bfloat16: np.uint16, torch.float16: np.float16}
+
+
+def host_out(t):
+    if t.dtype == torch.float32:
+        return t.cpu().numpy().astype(np.float64)
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def ref_as_f64(ref, dtype):
+    if dtype == torch.bfloat16:
+        return oracle.bf16_decode(ref).astype(np.float64)
+    return ref.astype(np.float64)
+
+
+def act64(act, g):
+    """The gate functions of the five gated activations in float64 (scipy's erf and expit)."""
+    from scipy.special import erf, expit
+    return {1: lambda x: x * expit(x), 2: lambda x: x * 0.5 * (1 + erf(x / np.sqrt(2))),
+            3: lambda x: np.maximum(x, 0), 4: expit, 5: lambda x: x}[act](g)
+
+
+def silu_h_bound(c1_ref, c1_bound, I, act=1):
+    """|h_gpu - h_oracle| bound from the two sides' fp32 c1 bound: every gate function here has slope at most
+    1.13 (GELU's maximum; SiLU 1.1, ReLU and identity 1, sigmoid 0.25), so |dh| <= 1.13 |dg| (|u| + |du|) +
+    |act(g)| |du|, plus a few fp32 roundings of h itself (the device erff/expf within a few ulp)."""
+    g, u = c1_ref[:, :I].astype(np.float64), c1_ref[:, I:].astype(np.float64)
+    dg, du = c1_bound[:, :I], c1_bound[:, I:]
+    sg = act64(act, g)
+    return 1.13 * dg * (np.abs(u) + du) + np.abs(sg) * du + 16 * 2.0 ** -24 * np.abs(sg * u) + 1e-30
+
+
+def check_codes_and_scales(orc, q, s, ref_q, ref_s, h_bound):
+    """Scales within the h bound / 448 of the oracle's.  Each side's dequantized value is within half an
+    e4m3 step of its own h (a step is at most 1/8 of the value, or 2^-9 scale units below the normal
+    range), and the two h are within h_bound of each other, so the dequantized values may differ by
+    h_bound plus both half steps.  Codes rarely differ at all."""
+    groups = ref_s.shape[1]
+    hb = h_bound.reshape(h_bound.shape[0], groups, 128).max(axis=2)
+    assert np.all(np.abs(s.astype(np.float64) - ref_s) <= hb / 448 * 1.01 + 2.0 ** -24 * np.abs(ref_s)), "scales"
+    diff = q != ref_q
+    assert diff.mean() < 1e-2, "codes differ at %.3g of positions" % diff.mean()
+    dec = lambda c: orc.e4m3_decode(c).astype(np.float64)
+    sg = np.repeat(s.astype(np.float64), 128, axis=1)
+    sr = np.repeat(ref_s.astype(np.float64), 128, axis=1)
+    dq, dr = dec(q) * sg, dec(ref_q) * sr
+    allowed = 1.01 * h_bound + 0.0625 * (np.abs(dq) + np.abs(dr)) + 2.0 ** -10 * (sg + sr)
+    bad = np.abs(dq - dr) > allowed
+    assert not bad.any(), "%d dequantized values beyond the bound" % bad.sum()

@@ -207,3 +207,63 @@ def test_fused_gate_up_act_quant_checks():
     assert call(q_stride=100) == m.MOE_ERR_SHAPE
     assert call(w_stride_e=128 * 256) == m.MOE_ERR_SHAPE  # experts overlap: 2I rows of 256 each
     assert call(w_q=P(0x1008)) == m.MOE_ERR_ALIGN
+
+
+def test_mxfp4_gemm_checks():
+    L = m.lib()
+    # K = 256: 128 weight bytes and 8 E8M0 bytes per row; N = 256 rows per expert
+    args = dict(a_q=FAKE, a_stride=256, a_s=FAKE, a_s_stride=2, w4=FAKE, w4_stride_e=256 * 128, w4_stride_n=128,
+                w4s=FAKE, w4s_stride_e=256 * 8, w4s_stride_n=8, n_experts=4, N=256, K=256, offsets=FAKE, m_rows=8,
+                block_m=0, out=FAKE, out_dt=m.MOE_BF16, out_stride=256, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.moe_mxfp4_grouped_gemm(*a.values())
+
+    assert call(out_dt=9) == m.MOE_ERR_DTYPE
+    assert call(N=200) == m.MOE_ERR_SHAPE                 # N % 128
+    assert call(K=192) == m.MOE_ERR_SHAPE                 # K % 128
+    assert call(K=8320, a_stride=8320, w4_stride_n=4160, w4_stride_e=4160 * 256, a_s_stride=65,
+                w4s_stride_n=260, w4s_stride_e=260 * 256) == m.MOE_ERR_SHAPE   # K <= 8192
+    assert call(n_experts=0) == m.MOE_ERR_SHAPE
+    assert call(n_experts=1025) == m.MOE_ERR_SHAPE
+    assert call(block_m=48) == m.MOE_ERR_SHAPE
+    assert call(m_rows=0, out=None, w4=None) == m.MOE_OK   # no work, no launch
+    assert call(out=None) == m.MOE_ERR_NULL
+    assert call(w4s=None) == m.MOE_ERR_NULL
+    assert call(offsets=None) == m.MOE_ERR_NULL
+    assert call(out_stride=100) == m.MOE_ERR_SHAPE
+    assert call(w4_stride_n=64) == m.MOE_ERR_SHAPE       # a row holds K/2 bytes
+    assert call(w4s_stride_n=4) == m.MOE_ERR_SHAPE       # and K/32 scale bytes
+    assert call(w4_stride_e=128 * 128) == m.MOE_ERR_SHAPE  # experts overlap
+    assert call(w4s_stride_e=128 * 8) == m.MOE_ERR_SHAPE
+    assert call(w4=P(0x1008)) == m.MOE_ERR_ALIGN
+    assert call(w4_stride_n=136, w4_stride_e=136 * 256) == m.MOE_ERR_ALIGN
+    assert call(w4s=P(0x1002)) == m.MOE_ERR_ALIGN
+    assert call(w4s_stride_n=10, w4s_stride_e=10 * 256) == m.MOE_ERR_ALIGN
+
+
+def test_mxfp4_fused_gate_up_act_quant_checks():
+    L = m.lib()
+    # I = 128: 2I = 256 W13 rows; K = 256
+    args = dict(a_q=FAKE, a_stride=256, a_s=FAKE, a_s_stride=2, w4=FAKE, w4_stride_e=256 * 128, w4_stride_n=128,
+                w4s=FAKE, w4s_stride_e=256 * 8, w4s_stride_n=8, n_experts=4, I=128, K=256, offsets=FAKE, m_rows=8,
+                block_m=0, act=1, q=FAKE, q_stride=128, s=FAKE, s_stride=1, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return L.moe_mxfp4_grouped_gemm_act_quant(*a.values())
+
+    assert call(I=192) == m.MOE_ERR_SHAPE
+    assert call(K=192) == m.MOE_ERR_SHAPE
+    assert call(n_experts=1025) == m.MOE_ERR_SHAPE
+    assert call(act=0) == m.MOE_ERR_SHAPE
+    assert call(act=6) == m.MOE_ERR_SHAPE
+    assert call(m_rows=0, q=None, s=None) == m.MOE_OK
+    assert call(s=None) == m.MOE_ERR_NULL
+    assert call(w4=None) == m.MOE_ERR_NULL
+    assert call(s_stride=0) == m.MOE_ERR_SHAPE
+    assert call(w4_stride_e=128 * 128) == m.MOE_ERR_SHAPE   # 2I rows per expert
+    assert call(w4s=P(0x1001)) == m.MOE_ERR_ALIGN

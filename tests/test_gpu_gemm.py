@@ -6,26 +6,10 @@ import torch
 import moe_routed_expert_amd as m
 import oracle
 import workloads as wl
-from gpu_util import assert_bf16_close, assert_close, assert_within_bound, dev, gemm_abs_bound, to_dev, u16
+from gpu_util import (NP_OUT, assert_bf16_close, assert_close, assert_within_bound, check_codes_and_scales, dev,
+                      gemm_abs_bound, host_out, ref_as_f64, silu_h_bound, to_dev, u16)
 
 pytestmark = pytest.mark.gpu
-
-NP_OUT = {torch.float32: np.float32, torch.bfloat16: np.uint16, torch.float16: np.float16}
-
-
-def host_out(t):
-    if t.dtype == torch.float32:
-        return t.cpu().numpy().astype(np.float64)
-    if t.dtype == torch.bfloat16:
-        return t.float().cpu().numpy().astype(np.float64)
-    return t.float().cpu().numpy().astype(np.float64)
-
-
-def ref_as_f64(ref, dtype):
-    if dtype == torch.bfloat16:
-        return oracle.bf16_decode(ref).astype(np.float64)
-    return ref.astype(np.float64)
-
 
 # --------------------------------------------------------------- slot mode ---
 
@@ -175,42 +159,6 @@ def test_grouped_prefill_routes_chain(orc):
 
 
 # ------------------------------------------------- fused SiLU-mul requant ---
-
-def act64(act, g):
-    """The gate functions of the five gated activations in float64 (scipy's erf and expit)."""
-    from scipy.special import erf, expit
-    return {1: lambda x: x * expit(x), 2: lambda x: x * 0.5 * (1 + erf(x / np.sqrt(2))),
-            3: lambda x: np.maximum(x, 0), 4: expit, 5: lambda x: x}[act](g)
-
-
-def silu_h_bound(c1_ref, c1_bound, I, act=1):
-    """|h_gpu - h_oracle| bound from the two sides' fp32 c1 bound: every gate function here has slope at most
-    1.13 (GELU's maximum; SiLU 1.1, ReLU and identity 1, sigmoid 0.25), so |dh| <= 1.13 |dg| (|u| + |du|) +
-    |act(g)| |du|, plus a few fp32 roundings of h itself (the device erff/expf within a few ulp)."""
-    g, u = c1_ref[:, :I].astype(np.float64), c1_ref[:, I:].astype(np.float64)
-    dg, du = c1_bound[:, :I], c1_bound[:, I:]
-    sg = act64(act, g)
-    return 1.13 * dg * (np.abs(u) + du) + np.abs(sg) * du + 16 * 2.0 ** -24 * np.abs(sg * u) + 1e-30
-
-
-def check_codes_and_scales(orc, q, s, ref_q, ref_s, h_bound):
-    """Scales within the h bound / 448 of the oracle's.  Each side's dequantized value is within half an
-    e4m3 step of its own h (a step is at most 1/8 of the value, or 2^-9 scale units below the normal
-    range), and the two h are within h_bound of each other, so the dequantized values may differ by
-    h_bound plus both half steps.  Codes rarely differ at all."""
-    groups = ref_s.shape[1]
-    hb = h_bound.reshape(h_bound.shape[0], groups, 128).max(axis=2)
-    assert np.all(np.abs(s.astype(np.float64) - ref_s) <= hb / 448 * 1.01 + 2.0 ** -24 * np.abs(ref_s)), "scales"
-    diff = q != ref_q
-    assert diff.mean() < 1e-2, "codes differ at %.3g of positions" % diff.mean()
-    dec = lambda c: orc.e4m3_decode(c).astype(np.float64)
-    sg = np.repeat(s.astype(np.float64), 128, axis=1)
-    sr = np.repeat(ref_s.astype(np.float64), 128, axis=1)
-    dq, dr = dec(q) * sg, dec(ref_q) * sr
-    allowed = 1.01 * h_bound + 0.0625 * (np.abs(dq) + np.abs(dr)) + 2.0 ** -10 * (sg + sr)
-    bad = np.abs(dq - dr) > allowed
-    assert not bad.any(), "%d dequantized values beyond the bound" % bad.sum()
-
 
 @pytest.mark.parametrize("bm,act", [(0, 1), (16, 1), (32, 1), (64, 1), (128, 1), (64, 2), (128, 3), (32, 4),
                                     (16, 5)])

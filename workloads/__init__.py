@@ -215,6 +215,22 @@ def powers_of_two_case(E: int, N: int, K: int, rows: int, seed: int):
     return a_q, a_s, w_q, w_s
 
 
+def mxfp4_exact_case(E: int, N: int, K: int, rows: int, seed: int):
+    """Exact operands for the MXFP4 GEMM (K <= 1024): activation codes of -4..4 with scales in {1/2, 1, 2},
+    every E2M1 weight code, E8M0 exponents 126..128.  Every partial sum is a multiple of 2^-3 below 2^17, so
+    fp32 holds each one exactly in any order.  Returns numpy arrays
+    (a_q [rows,K], a_s [rows,K/128], w4 [E,N,K/2], w4_s [E,N,K/32])."""
+    assert K <= 1024
+    rng = np.random.default_rng(seed)
+    pos = np.array([0x00, 0x38, 0x40, 0x44, 0x48], np.uint8)
+    v = rng.integers(-4, 5, size=(rows, K))
+    a_q = np.where(v < 0, pos[np.abs(v)] | 0x80, pos[np.abs(v)]).astype(np.uint8)
+    a_s = np.exp2(rng.integers(-1, 2, size=(rows, K // 128))).astype(np.float32)
+    w4 = rng.integers(0, 256, size=(E, N, K // 2)).astype(np.uint8)
+    w4_s = rng.integers(126, 129, size=(E, N, K // 32)).astype(np.uint8)
+    return a_q, a_s, w4, w4_s
+
+
 def nbytes_expert(H: int, I: int) -> int:
     """Bytes one active decode route streams: W13 + W2 fp8 plus their fp32 block scales."""
     return 2 * I * H + H * I + 4 * (math.ceil(2 * I / 128) * math.ceil(H / 128) + math.ceil(H / 128) * math.ceil(I / 128))
