@@ -268,9 +268,9 @@ int moe_topk_reduce(const void* y, int y_dt, int64_t y_stride,
  *   [2] aq   R x I            fp8 activation (1x128 requant of h)
  *   [3] as   R x ceil(I/128)  fp32 activation scales
  *   [4] c2   R x H            fp32 down output
- *   [5] ctl  control block: the error word, per-route tile counters and
- *            publish words, and the last-seen publish value of each down
- *            tile (hand-off state of the one-launch step)
+ *   [5] ctl  control block: the error word and the hand-off state of the
+ *            one-launch step (per-tile call counters, ready words and a
+ *            tagged copy of h)
  *   [6] total size in bytes
  * Regions [0]..[4] may hold anything between calls: every call rewrites them
  * completely, and an inactive route's c1/h/aq/as/c2 rows become exact zeros

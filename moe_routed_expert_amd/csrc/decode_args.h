@@ -21,6 +21,9 @@ struct FusedDecodeArgs {
     float* c2;               // [R][H] down output
     uint16_t* out;           // [T][H] bf16
     uint32_t* ctl;           // control block of the one-launch step (decode_ctl_bytes)
+    uint64_t* hx;            // [R][I] tagged h of the one-launch step (set by the launcher)
+    uint32_t* flags;         // ready-word copies of the one-launch step (set by the launcher)
+    int flag_stride;         // words per route in one copy (set by the launcher)
     int T, H, I, topk;
     int act;                 // gated activation (moe_act 1..5)
     int tiles_a;             // gate/up tiles per route (set by the launcher)
@@ -37,7 +40,7 @@ constexpr int kDecodeCtlLineWords = 32;
 // W2 rows per down tile of the one-launch step.
 constexpr int kDecodeDownRows = 8;
 
-// Largest number of last-seen words (routes x down tiles) the one-launch step keeps.
+// Largest number of down-tile epoch words (routes x down tiles) the one-launch step keeps.
 constexpr int64_t kDecodeMaxLastSeen = 1 << 18;
 
 // Shapes the one-launch step can take: I/128 in [1, 8], I/8 even or a multiple of 3, H/128 <= 16
@@ -48,12 +51,39 @@ inline bool decode_one_launch_ok(int64_t T, int64_t H, int64_t I, int64_t topk) 
            H % kDecodeDownRows == 0 && T * topk * (H / kDecodeDownRows) <= kDecodeMaxLastSeen;
 }
 
-// Bytes of the control block: the error word's line, a counter line and a publish line per route,
-// and one last-seen word per (route, down tile) for shapes the one-launch step can take.
+// Act columns per gate/up tile of the one-launch step are 8 * decode_step_m(I).
+inline int decode_step_m(int64_t I) { return (I / 8) % 3 == 0 ? 3 : 2; }
+
+// Epoch words of the one-launch step: one per gate/up tile and one per (token, down tile, route).
+inline int64_t decode_epoch_words(int64_t T, int64_t H, int64_t I, int64_t topk) {
+    return T * topk * (I / (8 * decode_step_m(I))) + T * (H / kDecodeDownRows) * topk;
+}
+
+// Copies of each gate/up tile's ready word (readers spread their polls over them) and words per
+// route in one copy (the route's gate/up tiles, padded to whole 128-byte lines).
+constexpr int kDecodeFlagCopies = 8;
+inline int64_t decode_flag_stride(int64_t I) {
+    const int64_t tiles = I / (8 * decode_step_m(I));
+    return (tiles + kDecodeCtlLineWords - 1) / kDecodeCtlLineWords * kDecodeCtlLineWords;
+}
+
+// Word offset, inside the control block, of the ready-word copies ([copy][route][flag stride]).
+inline int64_t decode_flag_offset(int64_t T, int64_t H, int64_t I, int64_t topk) {
+    const int64_t w = kDecodeCtlLineWords + decode_epoch_words(T, H, I, topk);
+    return (w + kDecodeCtlLineWords - 1) / kDecodeCtlLineWords * kDecodeCtlLineWords;
+}
+
+// Byte offset, inside the control block, of the tagged h ([T*topk][I] 64-bit words).
+inline int64_t decode_tagged_h_offset(int64_t T, int64_t H, int64_t I, int64_t topk) {
+    const int64_t w = decode_flag_offset(T, H, I, topk) + kDecodeFlagCopies * T * topk * decode_flag_stride(I);
+    return (4 * w + 255) / 256 * 256;
+}
+
+// Bytes of the control block: the error word's line and, for shapes the one-launch step can take,
+// its epoch words, the ready-word copies and the tagged h.
 inline int64_t decode_ctl_bytes(int64_t T, int64_t H, int64_t I, int64_t topk) {
-    const int64_t R = T * topk;
-    const int64_t seen = decode_one_launch_ok(T, H, I, topk) ? R * (H / kDecodeDownRows) : 0;
-    return 4 * (kDecodeCtlLineWords * (1 + 2 * R) + seen);
+    if (!decode_one_launch_ok(T, H, I, topk)) return 4 * kDecodeCtlLineWords;
+    return decode_tagged_h_offset(T, H, I, topk) + 8 * T * topk * I;
 }
 
 // Enqueues the decode step as one launch when the shape allows it and all its blocks fit on the

@@ -116,11 +116,17 @@ __device__ __forceinline__ float dpp_f32(float old, float v) {
                                                                   0xF, false));
 }
 
-// Max over each row of 16 lanes, returned in every lane of the row (register-only DPP moves).
-__device__ __forceinline__ float row16_max(float v) {
+// Max over each aligned group of 8 lanes, returned in every lane of the group (register-only DPP moves).
+__device__ __forceinline__ float group8_max(float v) {
     v = __builtin_fmaxf(v, dpp_f32<0xB1>(v, v));    // quad_perm [1,0,3,2]
     v = __builtin_fmaxf(v, dpp_f32<0x4E>(v, v));    // quad_perm [2,3,0,1]
     v = __builtin_fmaxf(v, dpp_f32<0x141>(v, v));   // row_half_mirror: lane i <- 7-i within 8
+    return v;
+}
+
+// Max over each row of 16 lanes, returned in every lane of the row (register-only DPP moves).
+__device__ __forceinline__ float row16_max(float v) {
+    v = group8_max(v);
     v = __builtin_fmaxf(v, dpp_f32<0x140>(v, v));   // row_mirror: lane i <- 15-i within 16
     return v;
 }
@@ -163,5 +169,16 @@ __device__ __forceinline__ void wave_lds_fence() {
 }
 
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Reads two 32-bit words through the scalar data cache with one wait; each pointer must be the same in
+// every lane (the values are wave-uniform).  For the few small words a wave needs before its first
+// large vector loads: a scalar read does not wait behind the vector loads the CU already has in
+// flight, which under a full weight stream take microseconds to drain.
+__device__ __forceinline__ void scalar_read2(const void* p, const void* q, uint32_t& a, uint32_t& b) {
+    asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&s"(a), "=&s"(b)
+                 : "s"(p), "s"(q)
+                 : "memory");
+}
 
 }  // namespace moe
