@@ -345,29 +345,6 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDe
     }
 }
 
-int fused_decode_two_launch(hipStream_t st, FusedDecodeArgs a) {
-    if (a.I / 128 < 1 || a.I / 128 > kFdMaxNkb2) return MOE_ERR_SHAPE;
-    a.tiles_a = a.I / 8;
-    a.n_a = a.T * a.topk * a.tiles_a;
-    // 16-row down tiles once they alone give a workgroup per CU (each tile re-reads the token's h,
-    // so fewer, wider tiles read less of it); 8-row tiles otherwise
-    const bool wide = (int64_t)a.T * (a.H / kFdTile) >= kWideDownTiles;
-    a.tiles_c = a.H / (wide ? kFdTile : kDnRows);
-    hipLaunchKernelGGL(decode_gateup_kernel, dim3((unsigned)a.n_a), dim3(kWave * kFdWaves), 0, st, a);
-    const unsigned down = (unsigned)(a.T * a.tiles_c);
-    switch (a.I / 128) {
-#define MOE_FD_CASE(n)                                                                                                  \
-    case n:                                                                                                             \
-        if (wide) hipLaunchKernelGGL((decode_down16_kernel<n>), dim3(down), dim3(kWave * kFdWaves), 0, st, a);         \
-        else hipLaunchKernelGGL((decode_down8_kernel<n>), dim3(down), dim3(kWave * kFdWaves), 0, st, a);               \
-        break;
-        MOE_FD_CASE(1) MOE_FD_CASE(2) MOE_FD_CASE(3) MOE_FD_CASE(4)
-        MOE_FD_CASE(5) MOE_FD_CASE(6) MOE_FD_CASE(7) MOE_FD_CASE(8)
-#undef MOE_FD_CASE
-        default: return MOE_ERR_SHAPE;
-    }
-    return launch_status();
-}
 
 
 // ---------------------------------------------------------------------------
@@ -525,7 +502,7 @@ __device__ __forceinline__ void gateup_tile_m(const FusedDecodeArgs& a, int b) {
 #pragma unroll
     for (int g = 0; g < M; g++) acc[g] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     for (int kb = kb0; kb < kb1; kb += kFdUnroll) {
-        v4i blo[M][kFdUnroll], bhi[M][kFdUnroll], alo[kFdUnroll], ahi[kFdUnroll];
+        v4i blo[M][kFdUnroll], bhi[M][kFdUnroll];
         float sa[kFdUnroll], sw[M][kFdUnroll];
         uint32_t pair[kFdUnroll];
         // token row first: its quantization then overlaps the weight stream (loads retire in order)
@@ -555,23 +532,20 @@ __device__ __forceinline__ void gateup_tile_m(const FusedDecodeArgs& a, int b) {
             }
         }
         wave_lds_fence();
+        // one K block at a time: its token-row fragment from LDS, then its M products
 #pragma unroll
         for (int u = 0; u < kFdUnroll; u++) {
             if (kb + u < kb1) {
-                alo[u] = *reinterpret_cast<const v4i*>(&xq[wave][u][q16]);
-                ahi[u] = *reinterpret_cast<const v4i*>(&xq[wave][u][64 + q16]);
-            }
-        }
+                const v4i alo = *reinterpret_cast<const v4i*>(&xq[wave][u][q16]);
+                const v4i ahi = *reinterpret_cast<const v4i*>(&xq[wave][u][64 + q16]);
 #pragma unroll
-        for (int g = 0; g < M; g++)
-#pragma unroll
-            for (int u = 0; u < kFdUnroll; u++) {
-                if (kb + u < kb1) {
+                for (int g = 0; g < M; g++) {
                     const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-                    const v4f p = mfma16x16x128_e4m3(frag(alo[u], ahi[u]), frag(blo[g][u], bhi[g][u]), z);
+                    const v4f p = mfma16x16x128_e4m3(frag(alo, ahi), frag(blo[g][u], bhi[g][u]), z);
                     acc[g] += p * (sa[u] * sw[g][u]);
                 }
             }
+        }
         wave_lds_fence();
     }
 #pragma unroll
@@ -598,12 +572,77 @@ __device__ __forceinline__ void gateup_tile_m(const FusedDecodeArgs& a, int b) {
     }
 }
 
-// Down tile b of the one-launch step: as decode_down8_kernel, but the W2
-// fragments are requested before the route's h is ready, and h comes from its
-// tagged copy once every element this wave needs carries the call's tag.
+// h of route r in a down tile's wave, requantized per 1x128 group: waits for the
+// call's h (wait_route_h), transposes it through the wave's LDS rows so that
+// lane l owns columns 16*(l%8) .. +15 of 128-group l/8 (lanes past the last group
+// repeat it and store nothing), and writes the codes as MFMA operands into hq.
+// A group's maximum is then an in-lane maximum and three DPP steps.
+template <int NKB2>
+struct RouteAct {
+    float sa[NKB2];     // scale of each group (wave-uniform)
+    uint32_t q[4];      // this lane's 16 codes
+    float s;            // this lane's group scale
+    int rg, rc;         // this lane's group and first column in it
+    bool owner;         // whether this lane's codes are its own (stored)
+};
+
+template <int NKB2>
+__device__ __forceinline__ bool route_act(const FusedDecodeArgs& a, int64_t r, uint32_t tag, float* hfw,
+                                          uint8_t (*hqw)[128], RouteAct<NKB2>& ra) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float hp[2 * NKB2];
+    const bool ok = wait_route_h<NKB2>(a, r, tag, hp);
+#pragma unroll
+    for (int kb = 0; kb < NKB2; kb++)
+        *reinterpret_cast<float2*>(&hfw[kb * 128 + 2 * lane]) = make_float2(hp[2 * kb], hp[2 * kb + 1]);
+    wave_lds_fence();
+    ra.owner = (lane >> 3) < NKB2;
+    ra.rg = ra.owner ? (lane >> 3) : NKB2 - 1;
+    ra.rc = (lane & 7) * 16;
+    float hv[16];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float4 f = *reinterpret_cast<const float4*>(&hfw[ra.rg * 128 + ra.rc + 4 * i]);
+        hv[4 * i] = f.x; hv[4 * i + 1] = f.y; hv[4 * i + 2] = f.z; hv[4 * i + 3] = f.w;
+    }
+    float m16 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) m16 = __builtin_fmaxf(m16, __builtin_fabsf(hv[i]));
+    const float amax = group8_max(m16);
+    if (amax >= 0x1p-100f) {
+        ra.s = amax / 448.0f;
+        // |v| * inv stays below 448 * (1 + 2^-21), which the conversion rounds to 448 as a clamp
+        // to +-448 would, so the products go to it unclamped
+        const float inv = 448.0f * __builtin_amdgcn_rcpf(amax);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(hv[4 * i] * inv, hv[4 * i + 1] * inv, 0, false);
+            ra.q[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hv[4 * i + 2] * inv, hv[4 * i + 3] * inv, lo, true);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            float s2;
+            const uint32_t lo = requant_pair(hv[4 * i], hv[4 * i + 1], amax, s2);
+            const uint32_t hi = requant_pair(hv[4 * i + 2], hv[4 * i + 3], amax, ra.s);
+            ra.q[i] = lo | (hi << 16);
+        }
+    }
+    if (ra.owner) *reinterpret_cast<uint4*>(&hqw[ra.rg][ra.rc]) = make_uint4(ra.q[0], ra.q[1], ra.q[2], ra.q[3]);
+#pragma unroll
+    for (int kb = 0; kb < NKB2; kb++)
+        ra.sa[kb] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ra.s), 8 * kb));
+    wave_lds_fence();
+    return ok;
+}
+
+// Down tile b of the one-launch step: token t, 8 rows of W2 for all of t's
+// routes, wave j owning route j (then j+8, ...).  As decode_down8_kernel (the
+// 16 MFMA columns are the 8 rows on two K streams), but the W2 fragments are
+// requested before the route's h is ready.
 template <int NKB2>
 __device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
-    constexpr int NS = (NKB2 + 1) / 2;
+    constexpr int NS = (NKB2 + 1) / 2;                         // W2 blocks per lane
     constexpr bool kOdd = (NKB2 & 1) != 0;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int64_t t = b / a.tiles_c;
@@ -631,6 +670,7 @@ __device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
             v4i blo[NS], bhi[NS];
 #pragma unroll
             for (int i = 0; i < NS; i++) {
+                // odd NKB2: stream 1's missing last block reads a valid one, zeroed below
                 const int kb = strm * NS + i < NKB2 ? strm * NS + i : NKB2 - 1;
                 blo[i] = *reinterpret_cast<const v4i*>(wrow + kb * 128);
                 bhi[i] = *reinterpret_cast<const v4i*>(wrow + kb * 128 + 64);
@@ -641,54 +681,11 @@ __device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
             float sw[NKB2];
 #pragma unroll
             for (int kb = 0; kb < NKB2; kb++) sw[kb] = wsrow[kb];
-            float hp[2 * NKB2];
-            if (!wait_route_h<NKB2>(a, r, tag, hp)) timed_out = true;
-            // requant layout: lane l owns columns 16*(l%8) .. +15 of 128-group l/8 (lanes past the
-            // last group repeat it and store nothing), so a group's maximum is an in-lane maximum
-            // and three DPP steps; the loads above are lane-contiguous, so h is transposed in LDS
-#pragma unroll
-            for (int kb = 0; kb < NKB2; kb++)
-                *reinterpret_cast<float2*>(&hf[wave][kb * 128 + 2 * lane]) = make_float2(hp[2 * kb], hp[2 * kb + 1]);
-            wave_lds_fence();
-            const int rg = (lane >> 3) < NKB2 ? (lane >> 3) : NKB2 - 1, rc = (lane & 7) * 16;
-            float hv[16];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float4 f = *reinterpret_cast<const float4*>(&hf[wave][rg * 128 + rc + 4 * i]);
-                hv[4 * i] = f.x; hv[4 * i + 1] = f.y; hv[4 * i + 2] = f.z; hv[4 * i + 3] = f.w;
-            }
-            float m16 = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; i++) m16 = __builtin_fmaxf(m16, __builtin_fabsf(hv[i]));
-            const float amax = group8_max(m16);
-            float s;
-            uint32_t q[4];
-            if (amax >= 0x1p-100f) {
-                s = amax / 448.0f;
-                // |v| * inv stays below 448 * (1 + 2^-21), which the conversion rounds to 448 as a clamp
-                // to +-448 would, so the products go to it unclamped
-                const float inv = 448.0f * __builtin_amdgcn_rcpf(amax);
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(hv[4 * i] * inv, hv[4 * i + 1] * inv, 0, false);
-                    q[i] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(hv[4 * i + 2] * inv, hv[4 * i + 3] * inv, lo, true);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    float s2;
-                    const uint32_t lo = requant_pair(hv[4 * i], hv[4 * i + 1], amax, s2);
-                    const uint32_t hi = requant_pair(hv[4 * i + 2], hv[4 * i + 3], amax, s);
-                    q[i] = lo | (hi << 16);
-                }
-            }
-            const bool owner = (lane >> 3) < NKB2;
-            if (owner) *reinterpret_cast<uint4*>(&hq[wave][rg][rc]) = make_uint4(q[0], q[1], q[2], q[3]);
-            float sa[NKB2];
-#pragma unroll
-            for (int kb = 0; kb < NKB2; kb++)
-                sa[kb] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 8 * kb));
-            wave_lds_fence();
+            RouteAct<NKB2> ra;
+            if (!route_act<NKB2>(a, r, tag, hf[wave], hq[wave], ra)) timed_out = true;
+            // A row 0 carries stream 0's block, A row 1 stream 1's; C[0][c < 8] and C[1][c >= 8] are
+            // the two streams' partials of W2 row n0 + (c & 7)
+            const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
             const int m = lane & 15;
             const v4i zero4 = {0, 0, 0, 0};
             float acc = 0.0f;
@@ -703,17 +700,16 @@ __device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
                 ahi = a_on ? ahi : zero4;
                 const bool b_on = strm == 0 || has1;
                 const v4i bl = b_on ? blo[i] : zero4, bh = b_on ? bhi[i] : zero4;
-                const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
                 const v4f p = mfma16x16x128_e4m3(frag(alo, ahi), frag(bl, bh), z);
-                const float f0 = sa[i] * sw[i];
-                const float f1 = has1 ? sa[(NS + i) % NKB2] * sw[(NS + i) % NKB2] : 0.0f;
+                const float f0 = ra.sa[i] * sw[i];
+                const float f1 = has1 ? ra.sa[(NS + i) % NKB2] * sw[(NS + i) % NKB2] : 0.0f;
                 acc += strm == 0 ? p[0] * f0 : p[1] * f1;
             }
             wave_lds_fence();
             val = acc + __shfl_down(acc, 8, 16);
-            if (ntile == 0 && owner) {
-                *reinterpret_cast<uint4*>(a.aq + r * a.I + rg * 128 + rc) = make_uint4(q[0], q[1], q[2], q[3]);
-                if ((lane & 7) == 0) a.as[r * NKB2 + rg] = s;
+            if (ntile == 0 && ra.owner) {
+                *reinterpret_cast<uint4*>(a.aq + r * a.I + ra.rg * 128 + ra.rc) = make_uint4(ra.q[0], ra.q[1], ra.q[2], ra.q[3]);
+                if ((lane & 7) == 0) a.as[r * NKB2 + ra.rg] = ra.s;
             }
         } else if (ntile == 0) {
             for (int i = lane; i < a.I / 4; i += kWave) reinterpret_cast<uint32_t*>(a.aq + r * a.I)[i] = 0u;
@@ -780,6 +776,30 @@ int try_step_m(hipStream_t st, const FusedDecodeArgs& a) {
     if (decode_step_m(a.I) == 3) return try_step<NKB2, 3>(st, a);
     if ((a.I / 8) % 2 == 0) return try_step<NKB2, 2>(st, a);
     return 1;
+}
+
+int fused_decode_two_launch(hipStream_t st, FusedDecodeArgs a) {
+    if (a.I / 128 < 1 || a.I / 128 > kFdMaxNkb2) return MOE_ERR_SHAPE;
+    a.tiles_a = a.I / 8;
+    a.n_a = a.T * a.topk * a.tiles_a;
+    // 16-row down tiles once they alone give a workgroup per CU (each tile re-reads the token's h,
+    // so fewer, wider tiles read less of it); 8-row tiles otherwise
+    const bool wide = (int64_t)a.T * (a.H / kFdTile) >= kWideDownTiles;
+    a.tiles_c = a.H / (wide ? kFdTile : kDnRows);
+    hipLaunchKernelGGL(decode_gateup_kernel, dim3((unsigned)a.n_a), dim3(kWave * kFdWaves), 0, st, a);
+    const unsigned down = (unsigned)(a.T * a.tiles_c);
+    switch (a.I / 128) {
+#define MOE_FD_CASE(n)                                                                                                  \
+    case n:                                                                                                             \
+        if (wide) hipLaunchKernelGGL((decode_down16_kernel<n>), dim3(down), dim3(kWave * kFdWaves), 0, st, a);         \
+        else hipLaunchKernelGGL((decode_down8_kernel<n>), dim3(down), dim3(kWave * kFdWaves), 0, st, a);               \
+        break;
+        MOE_FD_CASE(1) MOE_FD_CASE(2) MOE_FD_CASE(3) MOE_FD_CASE(4)
+        MOE_FD_CASE(5) MOE_FD_CASE(6) MOE_FD_CASE(7) MOE_FD_CASE(8)
+#undef MOE_FD_CASE
+        default: return MOE_ERR_SHAPE;
+    }
+    return launch_status();
 }
 
 int fused_decode_one_launch(hipStream_t st, FusedDecodeArgs a) {

@@ -330,13 +330,15 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
         for (int c = 0; c < TPW; c++) acc[m][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int last = nkb - 1;
-    // prologue: the first scale chunk, A steps 0 and 1, W steps 0..S-2 requested; scales and A step 0
-    // in LDS (the chunk's loads are the oldest, so its stores wait for nothing else)
+    // prologue: the first scale chunk, then A and W steps 0..S-2 (each A step ahead of its W step)
+    // requested; scales and A step 0 in LDS (the chunk's loads are the oldest, so its stores wait for
+    // nothing else)
     if constexpr (W4) sc_issue(0, 0, 16);
-    load_a(0, 0);
-    load_a(1 < last ? 1 : last, 1 % SA);
 #pragma unroll
-    for (int s = 0; s < S - 1; s++) load_w(s < last ? s : last, w_ring[s]);
+    for (int s = 0; s < S - 1; s++) {
+        load_a(s < last ? s : last, s % SA);
+        load_w(s < last ? s : last, w_ring[s]);
+    }
     if constexpr (W4) sc_commit(0, 16);
     store_a(0, 0);
     __syncthreads();
@@ -360,8 +362,10 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
 #pragma unroll
         for (int s = 0; s < S; s++) {
             const int kb = kb0 + s;
-            // A step kb+2 into the stage step kb-1 left, W step kb+S-1 into the slot freed last step
-            load_a(kb + 2 < last ? kb + 2 : last, (s + 2) % SA);
+            // A and W step kb+S-1 into the stage and slot step kb-1 left.  A runs as far ahead as W:
+            // loads retire in order, so waiting for A step kb+1 at the end of this step waits for no
+            // W step beyond kb, and W keeps S-1 steps of lead through the whole step
+            load_a(kb + S - 1 < last ? kb + S - 1 : last, (s + S - 1) % SA);
             load_w(kb + S - 1 < last ? kb + S - 1 : last, w_ring[(s + S - 1) % S]);
             const int buf = kb & 1;
             if (kb < nkb) {

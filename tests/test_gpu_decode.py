@@ -77,6 +77,19 @@ def check_ctl(dd: DevDecode):
     return int(ep[0]) if n else None
 
 
+def one_launch_flag_words(T, H, I, topk):
+    """(first word, word count) of the one-launch step's ready-word copies inside the control block:
+    8 copies x routes x the route's gate/up tiles padded to 32 words, after the line-aligned epoch
+    words; 0 words for shapes the step never takes."""
+    n = one_launch_epoch_words(T, H, I, topk)
+    if n == 0:
+        return 0, 0
+    g = I // 8
+    tiles = I // (8 * (3 if g % 3 == 0 else 2))
+    first = (32 + n + 31) // 32 * 32
+    return first, 8 * T * topk * ((tiles + 31) // 32 * 32)
+
+
 def check_against_oracle(dd: DevDecode, ref, im, host_weights=None, act=1):
     c = dd.c
     R = c.T * c.topk
@@ -265,3 +278,25 @@ def test_chained_layers_in_one_graph_like_the_benchmark(orc):
         assert_bf16_close(got, ref, what="layer %d" % l)
         x_in = got
     assert np.all(u16(outs[3]) == 0)                 # layer 3 has no active route
+
+
+def test_ready_words_ahead_of_h_fall_back_to_coherent_loads(orc):
+    """A ready word seen before its tile's h: every ready word is set to the next call's tag before the
+    call, so the down tiles read h at once, find the previous call's tags (and, on each XCD, stale L2
+    lines), and must wait on coherent loads of h itself; the output still equals the oracle's."""
+    c = wl.decode_case(H=2048, I=768, topk=8, n_slots=16, active=6, seed=41)
+    dd = DevDecode(c)
+    dd.run()
+    torch.cuda.synchronize()
+    calls = check_ctl(dd)
+    if calls is None or calls == 0:
+        pytest.skip("the step did not run as one launch on this device")
+    first, count = one_launch_flag_words(c.T, c.H, c.I, c.topk)
+    ctl = dd.ws[dd.lay["ctl"]:dd.lay["total"]].view(torch.int32)
+    ctl[first:first + count] = calls + 1
+    dd.poison()
+    dd.run()
+    torch.cuda.synchronize()
+    ref, im = oracle_decode(c)
+    check_against_oracle(dd, ref, im)
+    assert check_ctl(dd) == calls + 1
