@@ -330,6 +330,7 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
         for (int c = 0; c < TPW; c++) acc[m][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int last = nkb - 1;
+    const int tile_rows = __builtin_amdgcn_readfirstlane(row_end - row0);
     // prologue: the first scale chunk, then A and W steps 0..S-2 (each A step ahead of its W step)
     // requested; scales and A step 0 in LDS (the chunk's loads are the oldest, so its stores wait for
     // nothing else)
@@ -388,6 +389,9 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
                 }
 #pragma unroll
                 for (int m = 0; m < MS; m++) {
+                    // 16-row sub-tiles past the tile's rows are skipped (wave-uniform): an expert with
+                    // 96 rows in a 128-row tile does 6 of the 8
+                    if (MS > 4 && m * 16 >= tile_rows) continue;
                     // W is the MFMA's row operand and A its column operand, so a lane's four results
                     // share one A row (lane % 16) and take a single scale
                     const v8i a = *reinterpret_cast<const v8i*>(&a_lds[buf][m * 2048 + lane * 32]);
