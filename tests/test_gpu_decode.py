@@ -161,6 +161,24 @@ def test_fused_decode_gated_activations(orc, act, H, I, T):
     check_against_oracle(dd, ref, im, act=act)
 
 
+@pytest.mark.parametrize("T,H,I,topk,active", [(2, 512, 256, 4, 3), (3, 256, 384, 2, 1), (1, 1024, 128, 1, 1),
+                                                (2, 1024, 768, 4, 3)])
+def test_fused_decode_one_launch_shapes(orc, T, H, I, topk, active):
+    """Shapes the one-launch step takes beyond batch 1 and top-8: several tokens (down tiles and
+    epoch words per token), top-1, I/8 a multiple of 3 (24-column tiles) and of 2 only (16-column),
+    a 128-wide I (one act group); every one checked against the oracle, twice in a row."""
+    print("fused decode T=%d H=%d I=%d topk=%d" % (T, H, I, topk), flush=True)
+    c = wl.decode_case(H=H, I=I, topk=topk, n_slots=12, active=active, seed=T * 100 + H + I, T=T)
+    dd = DevDecode(c)
+    ref, im = oracle_decode(c)
+    for _ in range(2):
+        dd.poison()
+        dd.run()
+        torch.cuda.synchronize()
+        check_against_oracle(dd, ref, im)
+    assert check_ctl(dd) == 2, "the step did not run as one launch"
+
+
 def test_fused_decode_batch_of_tokens(orc):
     c = wl.decode_case(H=512, I=256, topk=4, n_slots=10, active=3, seed=11, T=5)
     dd = DevDecode(c)
