@@ -18,7 +18,8 @@ peak and against the HBM roofline, the
 roofline of the dominant kernel (the single fused decode kernel), and the
 CPU oracle timed on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-prefill]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-prefill] [--skip-cpu]
+       python bench.py --only-headline | --only-prefill | --only-gather     (for counter passes)
 """
 from __future__ import annotations
 
@@ -166,6 +167,13 @@ def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup):
     res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
     del g
     return res
+
+
+def gather_all(torch, m, wl):
+    """The gather at k=7168 for 1, 8, 64 and 1024 tokens (top-8) and at k=896 for 64 tokens."""
+    rows = [gather_bench(torch, m, wl, 7168, t, 8, 20) for t in (1, 8, 64, 1024)]
+    rows.append(gather_bench(torch, m, wl, 896, 64, 8, 20))
+    return rows
 
 
 def gather_bench(torch, m, wl, k, tokens, topk, reps):
@@ -448,6 +456,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only-prefill", action="store_true", help="copy calibration and the prefill GEMMs only")
+    ap.add_argument("--only-gather", action="store_true", help="copy calibration and the gather configurations only")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -463,6 +472,10 @@ def main():
     if args.only_prefill:
         print(json.dumps({"metric": "prefill fp8 TFLOP/s (grouped GEMMs only)", "copy_calibration": calib,
                           "prefill_densities": prefill_all(torch, m, wl)}))
+        return
+    if args.only_gather:
+        print(json.dumps({"metric": "gather us/call (gather only)", "copy_calibration": calib,
+                          "gather": gather_all(torch, m, wl)}))
         return
 
     log("decode H=2048 I=768: building %d layer pools" % LAYERS)
@@ -484,8 +497,7 @@ def main():
         del pools
         torch.cuda.empty_cache()
         log("gather")
-        extra["gather"] = [gather_bench(torch, m, wl, 7168, t, 8, 20) for t in (1, 8, 64, 1024)]
-        extra["gather"].append(gather_bench(torch, m, wl, 896, 64, 8, 20))
+        extra["gather"] = gather_all(torch, m, wl)
         log("route prep")
         extra["route_prep"] = [route_prep_bench(torch, m, wl, T, 256, 6, 20) for T in (256, 4096)]
         if not args.skip_prefill:
