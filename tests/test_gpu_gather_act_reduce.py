@@ -50,6 +50,36 @@ def test_gather_strided_negative_and_empty(orc):
     assert np.array_equal(dq.cpu().numpy(), hq)
 
 
+@pytest.mark.parametrize("case", ["ragged_strided_negative", "one_source", "identity"])
+def test_gather_long_maps(orc, case):
+    """Maps of 1024 rows and more: every copy of a source row is made on one XCD.  Ragged map
+    lengths, negative entries, more than 64 scale words, padded destination rows, a map whose
+    rows all name one source, and the identity map."""
+    print("gather long map case=%s" % case, flush=True)
+    rng = np.random.default_rng({"ragged_strided_negative": 11, "one_source": 12, "identity": 13}[case])
+    if case == "ragged_strided_negative":
+        k, n_src, n_dst, pad_q, pad_s = 16400, 300, 1027, 32, 3      # g = 129, 1025 vectors per row
+        mp = rng.integers(-2, n_src, n_dst).astype(np.int32)
+    elif case == "one_source":
+        k, n_src, n_dst, pad_q, pad_s = 7168, 5, 2048, 0, 0
+        mp = np.full(n_dst, 3, np.int32)
+    else:
+        k, n_src, n_dst, pad_q, pad_s = 4096, 1536, 1536, 0, 0
+        mp = np.arange(n_dst, dtype=np.int32)
+    g = (k + 127) // 128
+    src_q = rng.integers(0, 256, (n_src, k), dtype=np.uint8)
+    src_s = rng.integers(0, 2**32, (n_src, g), dtype=np.uint32).view(np.int32)
+    dq = torch.full((n_dst, k + pad_q), 0xCD, dtype=torch.uint8, device=dev())
+    ds = torch.full((n_dst, g + pad_s), 12345, dtype=torch.int32, device=dev())
+    m.gather_rows_scales(to_dev(src_q), to_dev(src_s).view(torch.float32), to_dev(mp),
+                         dq, ds.view(torch.float32), k=k, g=g)
+    torch.cuda.synchronize()
+    ref_q, ref_s = orc.gather_rows_scales(src_q, src_s.view(np.float32), mp)
+    hq, hs = dq.cpu().numpy(), ds.cpu().numpy()
+    assert np.array_equal(hq[:, :k], ref_q) and np.all(hq[:, k:] == 0xCD)
+    assert np.array_equal(hs[:, :g], ref_s.view(np.int32)) and np.all(hs[:, g:] == 12345)
+
+
 def test_gather_unaligned_source_takes_byte_path(orc):
     k, tokens = 256, 6
     src_q, src_s, mp = wl.gather_case(k, tokens, 8, seed=78)
