@@ -364,13 +364,16 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDe
 // gate/up tile stores the tag into its ready word (in several copies, so that
 // each line is polled by a fraction of the readers); it never waits for its
 // stores to complete and counts nothing.  A down tile polls the ready words of
-// the route's gate/up tiles (one small load per poll), then reads h with plain
-// loads that the XCD's L2 shares among its down tiles, and checks every tag;
-// a ready word seen before its tile's h (or a stale line) sends the reader to
-// coherent loads until the tags match.  Measured on one MI355X (2048/768, 8/8
-// active), this cut the step from 14.1-15.7 us (a route counter that each
-// gate/up tile bumped after waiting for its h stores) to about 13.1-13.5 us;
-// polling h itself with coherent loads was slower (every poll moved 12.6 MB).
+// the route's gate/up tiles (one small load per poll) until all but a few are
+// set, then reads h with plain loads that the XCD's L2 shares among its down
+// tiles, and checks every tag; each element still carrying an old tag (a late
+// tile, a ready word seen before its tile's h, a stale line) is re-polled on
+// its own with coherent loads until its tag matches, so the last tiles' h comes
+// back with the poll that sees it.  Measured on one MI355X (2048/768, 8/8
+// active), ready words cut the step from 14.1-15.7 us (a route counter that
+// each gate/up tile bumped after waiting for its h stores) to about 13.1-13.5
+// us, and not waiting for the last few of them saved about 0.4 us more;
+// polling all of h with coherent loads was slower (every poll moved 12.6 MB).
 // Down tiles have higher block ids than every gate/up tile they wait for, and
 // workgroups are dispatched in block order, so every awaited tile is already
 // running or done and the waits always end.  A wait is still bounded; if one
@@ -398,39 +401,20 @@ __device__ __forceinline__ uint64_t load_coherent(const uint64_t* p) {
     return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Loads this lane's 2*NKB2 h values of one route (columns kb*128 + 2*lane and +1: each load covers
-// 512 contiguous bytes), repeating until every one carries `tag` in all lanes; false if the spin limit
-// ran out first.
-template <int NKB2>
-__device__ __forceinline__ bool wait_tagged(const uint64_t* p, uint32_t tag, float (&v)[2 * NKB2]) {
-    for (int it = 0; it < kSpinLimit; it++) {
-        uint64_t w[2 * NKB2];
-#pragma unroll
-        for (int kb = 0; kb < NKB2; kb++) {
-            w[2 * kb] = load_coherent(p + kb * 128);
-            w[2 * kb + 1] = load_coherent(p + kb * 128 + 1);
-        }
-        bool stale = false;
-#pragma unroll
-        for (int i = 0; i < 2 * NKB2; i++) {
-            stale |= (uint32_t)(w[i] >> 32) != tag;
-            v[i] = __uint_as_float((uint32_t)w[i]);
-        }
-        if (__builtin_amdgcn_ballot_w64(stale) == 0) return true;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return false;
-}
-
 __device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
     return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// h of route r for this lane (as wait_tagged).  First polls the ready words of the route's gate/up
-// tiles (one 4-byte word per tile, one load per poll) until all show `tag`, then reads h with plain
-// loads, which the XCD's L2 shares between the down tiles on it (h is never in an L2 at the start
-// of a call: a kernel boundary lies between); if an element still carries an old tag (an epoch word
-// became visible before the tile's h, or a stale line was hit), it falls back to coherent loads.
+constexpr int kLateTiles = 4;   // ready words a down tile may still miss when it starts reading h
+
+// This lane's 2*NKB2 h values of route r (columns kb*128 + 2*lane and +1; each plain load covers 512
+// contiguous bytes).  First polls the ready words of the route's gate/up tiles (one 4-byte word per
+// tile, one load per poll) until at most kLateTiles of them lack `tag`, then reads h with plain
+// loads, which the XCD's L2 shares between the down tiles on it (h is never in an L2 at the start of
+// a call: a kernel boundary lies between).  Every element whose tag is still old (its tile was late,
+// its ready word became visible before its h, or a stale line was hit) is then re-polled on its own
+// with coherent loads until it carries `tag`: the last tiles' h arrives with the poll that sees it,
+// without a second round trip after a ready word.  False if the spin limit ran out first.
 template <int NKB2>
 __device__ __forceinline__ bool wait_route_h(const FusedDecodeArgs& a, int64_t r, uint32_t tag, float (&v)[2 * NKB2]) {
     // the copy this block polls: a copy's line is polled by 1/kDecodeFlagCopies of the down tiles
@@ -440,23 +424,37 @@ __device__ __forceinline__ bool wait_route_h(const FusedDecodeArgs& a, int64_t r
     const uint32_t* ep = a.flags + ((int64_t)copy * a.T * a.topk + r) * a.flag_stride + (lane < a.tiles_a ? lane : 0);
     int it = 0;
     for (; it < kSpinLimit; it++) {
-        if (__builtin_amdgcn_ballot_w64(load_coherent(ep) != tag) == 0) break;
+        if (__popcll(__builtin_amdgcn_ballot_w64(lane < a.tiles_a && load_coherent(ep) != tag)) <= kLateTiles) break;
         __builtin_amdgcn_s_sleep(1);
     }
     if (it >= kSpinLimit) return false;
     asm volatile("" ::: "memory");     // the plain loads below stay after the poll
     const uint64_t* p = a.hx + r * a.I + 2 * lane;
-    bool stale = false;
+    uint32_t stale = 0;                // bit i: element i still carries an old tag
 #pragma unroll
     for (int kb = 0; kb < NKB2; kb++) {
         const uint4 w = *reinterpret_cast<const uint4*>(p + kb * 128);
-        stale |= w.y != tag;
-        stale |= w.w != tag;
+        if (w.y != tag) stale |= 1u << (2 * kb);
+        if (w.w != tag) stale |= 1u << (2 * kb + 1);
         v[2 * kb] = __uint_as_float(w.x);
         v[2 * kb + 1] = __uint_as_float(w.z);
     }
-    if (__builtin_amdgcn_ballot_w64(stale) == 0) return true;
-    return wait_tagged<NKB2>(p, tag, v);
+    if (__builtin_amdgcn_ballot_w64(stale != 0) == 0) return true;
+    for (; it < kSpinLimit; it++) {
+#pragma unroll
+        for (int i = 0; i < 2 * NKB2; i++) {
+            if (stale & (1u << i)) {
+                const uint64_t w = load_coherent(p + (i >> 1) * 128 + (i & 1));
+                if ((uint32_t)(w >> 32) == tag) {
+                    v[i] = __uint_as_float((uint32_t)w);
+                    stale &= ~(1u << i);
+                }
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(stale != 0) == 0) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
 }
 
 // Gate/up tile b of the one-launch step: route r, act columns [c0, c0 + 8M).
