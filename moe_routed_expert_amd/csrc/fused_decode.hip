@@ -262,8 +262,9 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down8_kernel(FusedDec
 
 // Launch 2, wide form (used when H/16 tiles already fill the GPU): token t,
 // 16 rows of W2, 8 waves, wave j owns route j (then j+8, ...); the routes' C2
-// rows meet in LDS.  The token's slots and the routing
-// weights of its active routes are fetched once into LDS.
+// rows meet in LDS.  Each wave reads its route's slot itself, so its h and W2
+// loads wait for that one load only; the routing weight is read (for an active
+// route only) after them and is first needed at the end.
 template <int NKB2>
 __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDecodeArgs a) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -271,21 +272,14 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDe
     const int ntile = blockIdx.x % a.tiles_c;
     const int64_t n0 = (int64_t)ntile * kFdTile;
     const int q16 = (lane / 16) * 16;
-    __shared__ float part[64][kFdTile];
-    __shared__ int s_slot[64];
-    __shared__ float s_w[64];
+    __shared__ float part[64][kFdTile];                          // routing weight x C2 of route j (+0 if inactive)
     __shared__ __attribute__((aligned(16))) uint8_t hq[kFdWaves][NKB2][128];
-    if (threadIdx.x < a.topk) {
-        const int sl = a.slots[t * a.topk + threadIdx.x];
-        s_slot[threadIdx.x] = sl;
-        s_w[threadIdx.x] = sl >= 0 ? a.weights[t * a.topk + threadIdx.x] : 0.0f;
-    }
-    __syncthreads();
     for (int j = wave; j < a.topk; j += kFdWaves) {
         const int64_t r = t * a.topk + j;
-        const int slot = s_slot[j];
-        float val = 0.0f;
+        const int slot = a.slots[r];
+        float val = 0.0f, wgt = 0.0f;
         if (slot >= 0) {
+            // h first: its requant then overlaps the W2 stream (loads retire in order)
             const float* hrow = a.h + r * a.I + 2 * lane;
             float2 hv[NKB2];
 #pragma unroll
@@ -302,6 +296,7 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDe
             float sw[NKB2];
 #pragma unroll
             for (int kb = 0; kb < NKB2; kb++) sw[kb] = wsrow[kb];
+            wgt = a.weights[r];
             float sa[NKB2];
 #pragma unroll
             for (int kb = 0; kb < NKB2; kb++) {
@@ -332,15 +327,15 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_down16_kernel(FusedDe
             if (lane < NKB2) a.as[r * NKB2 + lane] = 0.0f;
         }
         if (lane < kFdTile) {
-            part[j][lane] = val;
+            // an inactive route adds +0, which leaves the sum unchanged (it is never -0: it starts at +0)
+            part[j][lane] = slot >= 0 ? wgt * val : 0.0f;
             a.c2[r * a.H + n0 + lane] = val;
         }
     }
     __syncthreads();
     if (threadIdx.x < kFdTile) {
         float o = 0.0f;
-        for (int j = 0; j < a.topk; j++)
-            if (s_slot[j] >= 0) o += s_w[j] * part[j][threadIdx.x];
+        for (int j = 0; j < a.topk; j++) o += part[j][threadIdx.x];
         a.out[t * a.H + n0 + threadIdx.x] = f32_to_bf16(o);
     }
 }
