@@ -19,7 +19,7 @@ roofline of the dominant kernel (the single fused decode kernel), and the
 CPU oracle timed on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-prefill] [--skip-cpu]
-       python bench.py --only-headline | --only-prefill | --only-gather     (for counter passes)
+       python bench.py --only-headline | --only-prefill | --only-gather | --only-stream   (for counter passes)
 """
 from __future__ import annotations
 
@@ -389,6 +389,63 @@ def prefill_all(torch, m, wl):
     return res
 
 
+def stream_ops_bench(torch, m, wl, reps=10):
+    """The bandwidth-bound steps at the prefill sizes (T=4096 tokens, top-6, H=4096, I=1024): input quant
+    of x [4096, 4096], the SiLU-mul requant of C1 [24576, 2048] (the unfused path) and the top-k reduce of
+    C2 [24576, 4096]. Each runs in a graph over enough disjoint buffer sets (more than 256 MB in all) that
+    no call finds its inputs in the GPU's caches; bytes = inputs read + outputs written."""
+    dev = torch.device("cuda")
+    T, topk, H, I = 4096, 6, 4096, 1024
+    R = T * topk
+
+    def timed(calls, nbytes):
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=torch.cuda.Stream()):
+            for c in calls:
+                c()
+        for _ in range(3):
+            gr.replay()
+        t = Timer(torch)
+        for _ in range(reps):
+            t.start()
+            gr.replay()
+            t.stop()
+        us = statistics.median(t.us()) / len(calls)
+        del gr
+        return dict(us_per_call=us, bytes=nbytes, gbs=nbytes / (us * 1e-6) / 1e9,
+                    hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
+
+    res = {}
+    sets = [(wl.bf16_normal((T, H), seed=60 + i, device=dev), torch.empty((T, H), dtype=torch.uint8, device=dev),
+             torch.empty((T, H // 128), dtype=torch.float32, device=dev)) for i in range(6)]
+    res["act_quant_identity"] = dict(rows=T, cols=H, **timed(
+        [lambda s=s: m.act_quant(s[0], s[1], s[2]) for s in sets], T * H * 2 + T * H + T * (H // 128) * 4))
+    del sets
+    sets = [(wl.bf16_normal((R, 2 * I), seed=70 + i, device=dev), torch.empty((R, I), dtype=torch.uint8, device=dev),
+             torch.empty((R, I // 128), dtype=torch.float32, device=dev)) for i in range(3)]
+    res["act_quant_silu_mul"] = dict(rows=R, cols=I, **timed(
+        [lambda s=s: m.act_quant(s[0], s[1], s[2], act=m.MOE_ACT_SILU_MUL) for s in sets],
+        R * 2 * I * 2 + R * I + R * (I // 128) * 4))
+    del sets
+    sets = []
+    for i in range(2):
+        g = torch.Generator(device="cpu").manual_seed(80 + i)
+        rows = torch.randperm(R, generator=g).to(torch.int32).view(T, topk).to(dev)
+        ids = torch.zeros((T, topk), dtype=torch.int32, device=dev)          # every route active
+        w = torch.rand((T, topk), generator=g).to(dev)
+        sets.append((wl.bf16_normal((R, H), seed=90 + i, device=dev), ids, w,
+                     torch.empty((T, H), dtype=torch.bfloat16, device=dev), rows))
+    res["topk_reduce"] = dict(tokens=T, topk=topk, H=H, **timed(
+        [lambda s=s: m.topk_reduce(s[0], s[1], s[2], s[3], route_rows=s[4]) for s in sets],
+        R * H * 2 + T * H * 2 + T * topk * 12))
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
 def route_prep_bench(torch, m, wl, T, E, topk, reps):
     """Device routing prep (top-k, weights, route maps) on skewed router logits: 16 calls over 16
     logit sets in one graph, so the time is the device's, not the host's launch latency."""
@@ -473,6 +530,7 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--only-prefill", action="store_true", help="copy calibration and the prefill GEMMs only")
     ap.add_argument("--only-gather", action="store_true", help="copy calibration and the gather configurations only")
+    ap.add_argument("--only-stream", action="store_true", help="copy calibration, input quant, requant and reduce only")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -488,6 +546,10 @@ def main():
     if args.only_prefill:
         print(json.dumps({"metric": "prefill fp8 TFLOP/s (grouped GEMMs only)", "copy_calibration": calib,
                           "prefill_densities": prefill_all(torch, m, wl)}))
+        return
+    if args.only_stream:
+        print(json.dumps({"metric": "bandwidth-bound steps at prefill sizes", "copy_calibration": calib,
+                          "stream_ops": stream_ops_bench(torch, m, wl)}))
         return
     if args.only_gather:
         print(json.dumps({"metric": "gather us/call (gather only)", "copy_calibration": calib,
@@ -514,6 +576,8 @@ def main():
         torch.cuda.empty_cache()
         log("gather")
         extra["gather"] = gather_all(torch, m, wl)
+        log("input quant, requant and reduce at prefill sizes")
+        extra["stream_ops"] = stream_ops_bench(torch, m, wl)
         log("route prep")
         extra["route_prep"] = [route_prep_bench(torch, m, wl, T, 256, 6, 20) for T in (256, 4096)]
         if not args.skip_prefill:

@@ -33,6 +33,20 @@ __device__ __forceinline__ uint32_t enc2_e4m3(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false) & 0xFFFFu;
 }
 
+// v / s where only the e4m3 code of the correctly rounded quotient is wanted; r is 1/s correctly
+// rounded.  v * r is within 2.5 ulp of RN(v / s) (two roundings of relative size 2^-24 each, plus
+// RN's half ulp), and e4m3 codes change only at midpoints between e4m3 values, which in fp32 have
+// low 20 bits 0x80000 (normal range) and lie 2^20 ulp apart.  So v * r names the same code as
+// RN(v / s) unless its low bits lie within 16 of a midpoint's, or it is below the e4m3 normal range
+// (2^-6, where the code grid is finer), or not finite; those take the exact division.
+__device__ __forceinline__ float e4m3_quot(float v, float s, float r) {
+    const float q = v * r;
+    const uint32_t b = __float_as_uint(q) & 0x7FFFFFFFu;
+    const bool edge = (b & 0xFFFFFu) - 0x7FFF0u <= 0x20u;
+    if (b != 0u && (edge || b < 0x3C800000u || b >= 0x7F800000u)) return v / s;
+    return q;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }

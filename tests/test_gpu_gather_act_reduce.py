@@ -139,6 +139,48 @@ def test_act_quant_identity_rounding_edges(orc):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
 
 
+def test_act_quant_identity_quotients_near_code_boundaries(orc):
+    """Groups with arbitrary scales whose values divide to within a few ulp of an e4m3 rounding midpoint
+    (and to midpoints exactly): the kernel's quotient shortcut must give the same codes as the exact
+    division, bit for bit."""
+    rng = np.random.default_rng(5)
+    rows, n = 64, 1024
+    codes = np.arange(0, 0x7F, dtype=np.uint8)
+    vals = orc.e4m3_decode(codes).astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.empty((rows, n), np.float32)
+    for r in range(rows):
+        for g in range(n // 128):
+            amax = np.float32(448.0 * 2.0 ** rng.uniform(-40, 40))
+            s = np.float32(amax / np.float32(448.0))
+            q = rng.choice(mids, 127).astype(np.float32)
+            q = (q.view(np.int32) + rng.integers(-6, 7, 127).astype(np.int32)).view(np.float32)   # +- a few ulp
+            v = (q * s).astype(np.float32) * rng.choice([-1.0, 1.0], 127).astype(np.float32)
+            v = np.clip(v, -amax, amax)
+            x[r, g * 128:(g + 1) * 128] = np.concatenate([[amax], v])
+    ref_q, ref_s = orc.quant_groups(x)
+    q = torch.empty((rows, n), dtype=torch.uint8, device=dev())
+    s = torch.empty((rows, n // 128), dtype=torch.float32, device=dev())
+    m.act_quant(to_dev(x), q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), ref_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+def test_act_quant_more_rows_than_one_grid_column(orc):
+    """70000 rows: more than the 65535 rows one launch column covers, so rows are taken in strides."""
+    rows, n = 70000, 128
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn((rows, n), generator=g).to(torch.bfloat16)
+    ref_q, ref_s = orc.quant_groups(x.view(torch.int16).numpy().view(np.uint16))
+    q = torch.full((rows, n), 0x55, dtype=torch.uint8, device=dev())
+    s = torch.full((rows, 1), float("nan"), dtype=torch.float32, device=dev())
+    m.act_quant(x.to(dev()), q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), ref_q)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("rows,n", [(8, 768), (8, 1024), (37, 1024), (4, 200)])
 def test_act_quant_silu_mul_within_one_step(orc, dtype, rows, n):
