@@ -80,6 +80,28 @@ def test_gather_long_maps(orc, case):
     assert np.array_equal(hs[:, :g], ref_s.view(np.int32)) and np.all(hs[:, g:] == 12345)
 
 
+@pytest.mark.parametrize("k,tokens,topk", [(4096, 4096, 6), (896, 256, 8)])
+def test_gather_prefill_size_route_map(orc, k, tokens, topk):
+    """A route map of the prefill shape (every token once per routed expert, rows in expert order) at
+    full size (24576 rows of 4096 bytes) and at the 896-byte width, both on the XCD-aware kernel."""
+    print("gather route map k=%d tokens=%d top-%d" % (k, tokens, topk), flush=True)
+    rng = np.random.default_rng(k + tokens)
+    g = (k + 127) // 128
+    src_q = rng.integers(0, 256, (tokens, k), dtype=np.uint8)
+    src_s = rng.integers(0, 2**32, (tokens, g), dtype=np.uint32).view(np.int32)
+    experts = np.stack([rng.choice(256, topk, replace=False) for _ in range(tokens)])   # [T, topk]
+    order = np.lexsort((np.repeat(np.arange(tokens), topk), experts.ravel()))          # (expert, token)
+    mp = np.repeat(np.arange(tokens, dtype=np.int32), topk)[order]
+    dq = torch.empty((len(mp), k), dtype=torch.uint8, device=dev())
+    ds = torch.empty((len(mp), g), dtype=torch.int32, device=dev())
+    m.gather_rows_scales(to_dev(src_q), to_dev(src_s).view(torch.float32), to_dev(mp), dq, ds.view(torch.float32))
+    torch.cuda.synchronize()
+    ref_q, ref_s = orc.gather_rows_scales(src_q, src_s.view(np.float32), mp)
+    assert np.array_equal(dq.cpu().numpy(), ref_q)
+    assert np.array_equal(ds.cpu().numpy(), ref_s.view(np.int32))
+    assert np.array_equal(dq.cpu().numpy(), src_q[mp])
+
+
 def test_gather_unaligned_source_takes_byte_path(orc):
     k, tokens = 256, 6
     src_q, src_s, mp = wl.gather_case(k, tokens, 8, seed=78)
