@@ -19,7 +19,8 @@
 // a source row is made on one XCD.  A negative entry (a zero row) goes by its
 // destination index instead.  Shorter maps keep one wavefront per row on its
 // own: there, spreading rows over more CUs beats the saved fetches.  Rows or
-// strides that are not 16-byte aligned fall back to a byte loop.
+// strides that are not 16-byte aligned fall back to a byte loop.  Map entries
+// outside [0, n_src) write a zero row, so no entry reads outside the sources.
 #include "device.h"
 #include "host.h"
 
@@ -50,7 +51,8 @@ __device__ __forceinline__ void copy_row_vec(const uint8_t* __restrict__ sq, con
     for (int64_t base = 0; base < nvec; base += kWave * kVecInFlight) {
         v4i buf[kVecInFlight];
         const bool sv = base == 0 && lane < g;      // the row's scales ride with its first chunk
-        const uint32_t sw = ss[sv ? lane : 0];
+        uint32_t sw = 0;
+        if (sv) sw = ss[lane];                      // (g == 0: no scale word is read at all)
         // unconditional loads (indices clamped to the row) so all of them issue back to back
 #pragma unroll
         for (int i = 0; i < kVecInFlight; i++) {
@@ -79,7 +81,7 @@ __device__ __forceinline__ void zero_row_vec(uint8_t* __restrict__ dq, uint32_t*
 __global__ void __launch_bounds__(64 * kXWaves)
 gather_rows_scales_xcd_kernel(const uint8_t* __restrict__ src_q, int64_t src_q_stride,
                               const uint32_t* __restrict__ src_s, int64_t src_s_stride,
-                              int64_t k, int64_t g, const int32_t* __restrict__ dst2src, int64_t n_dst,
+                              int64_t n_src, int64_t k, int64_t g, const int32_t* __restrict__ dst2src, int64_t n_dst,
                               uint8_t* __restrict__ dst_q, int64_t dst_q_stride,
                               uint32_t* __restrict__ dst_s, int64_t dst_s_stride) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -88,7 +90,8 @@ gather_rows_scales_xcd_kernel(const uint8_t* __restrict__ src_q, int64_t src_q_s
     const int64_t row_base = (int64_t)(blockIdx.x / kXcds) * kChunk;
     const int64_t my_row = row_base + lane;
     const bool in_map = lane < kChunk && my_row < n_dst;
-    const int32_t my_src = in_map ? dst2src[my_row] : -1;
+    int32_t my_src = in_map ? dst2src[my_row] : -1;
+    if (my_src >= n_src) my_src = -1;               // out of range: a zero row, like a negative entry
     const int home = my_src >= 0 ? my_src % kXcds : (int)(my_row % kXcds);
     const bool mine = in_map && home == xcd;
     const uint64_t mask = __ballot(mine);
@@ -114,13 +117,14 @@ template <bool VEC>
 __global__ void __launch_bounds__(64 * kRowsPerBlock)
 gather_rows_scales_kernel(const uint8_t* __restrict__ src_q, int64_t src_q_stride,
                           const uint32_t* __restrict__ src_s, int64_t src_s_stride,
-                          int64_t k, int64_t g, const int32_t* __restrict__ dst2src, int64_t n_dst,
+                          int64_t n_src, int64_t k, int64_t g, const int32_t* __restrict__ dst2src, int64_t n_dst,
                           uint8_t* __restrict__ dst_q, int64_t dst_q_stride,
                           uint32_t* __restrict__ dst_s, int64_t dst_s_stride) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
     if (row >= n_dst) return;
-    const int64_t src = dst2src[row];
+    int64_t src = dst2src[row];
+    if (src >= n_src) src = -1;                     // out of range: a zero row, like a negative entry
     uint8_t* dq = dst_q + row * dst_q_stride;   // int64 row base
     uint32_t* ds = dst_s + row * dst_s_stride;
     if constexpr (VEC) {
@@ -166,7 +170,7 @@ extern "C" int moe_gather_rows_scales(const void* src_q, int64_t src_q_stride,
         const int64_t blocks = ceil_div(n_dst, kChunk) * kXcds;
         if (blocks > 0x7FFFFFFF) return MOE_ERR_SHAPE;
         hipLaunchKernelGGL(gather_rows_scales_xcd_kernel, dim3((unsigned)blocks), dim3(64 * kXWaves), 0, s,
-                           (const uint8_t*)src_q, src_q_stride, (const uint32_t*)src_s, src_s_stride, k, g,
+                           (const uint8_t*)src_q, src_q_stride, (const uint32_t*)src_s, src_s_stride, n_src, k, g,
                            dst2src, n_dst, (uint8_t*)dst_q, dst_q_stride, (uint32_t*)dst_s, dst_s_stride);
         return launch_status();
     }
@@ -174,7 +178,7 @@ extern "C" int moe_gather_rows_scales(const void* src_q, int64_t src_q_stride,
     if (blocks > 0x7FFFFFFF) return MOE_ERR_SHAPE;
     auto kern = vec ? gather_rows_scales_kernel<true> : gather_rows_scales_kernel<false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * kRowsPerBlock), 0, s,
-                       (const uint8_t*)src_q, src_q_stride, (const uint32_t*)src_s, src_s_stride, k, g,
+                       (const uint8_t*)src_q, src_q_stride, (const uint32_t*)src_s, src_s_stride, n_src, k, g,
                        dst2src, n_dst, (uint8_t*)dst_q, dst_q_stride, (uint32_t*)dst_s, dst_s_stride);
     return launch_status();
 }

@@ -50,6 +50,33 @@ def test_gather_strided_negative_and_empty(orc):
     assert np.array_equal(dq.cpu().numpy(), hq)
 
 
+@pytest.mark.parametrize("tokens", [8, 300])
+def test_gather_without_scales_and_out_of_range_entries(orc, tokens):
+    """g = 0 with NULL scale buffers reads and writes no scale word; map entries >= n_src write a zero row
+    like negative ones.  Short maps (row per wave) and long ones (XCD-aware kernel)."""
+    k = 4096
+    src_q, src_s, mp = wl.gather_case(k, tokens, 8, seed=90 + tokens)
+    rng = np.random.default_rng(tokens)
+    bad = rng.random(len(mp)) < 0.2
+    mp = np.where(bad, tokens + rng.integers(0, 1 << 20, len(mp)), mp).astype(np.int32)
+    mp[0] = 2 ** 31 - 1
+    d = dev()
+    dq = torch.full((len(mp), k), 0xAB, dtype=torch.uint8, device=d)
+    sq = to_dev(src_q)
+    st = m.lib().moe_gather_rows_scales(sq.data_ptr(), k, None, 0, tokens, k, 0, to_dev(mp).data_ptr(), len(mp),
+                                        dq.data_ptr(), k, None, 0, m._stream())
+    assert st == m.MOE_OK
+    ds = torch.full((len(mp), src_s.shape[1]), -1, dtype=torch.int32, device=d)
+    dq2 = torch.full((len(mp), k), 0xAB, dtype=torch.uint8, device=d)
+    m.gather_rows_scales(sq, to_dev(src_s).view(torch.float32), to_dev(mp), dq2, ds.view(torch.float32))
+    torch.cuda.synchronize()
+    in_range = np.where(mp >= tokens, -1, mp).astype(np.int32)
+    ref_q, ref_s = orc.gather_rows_scales(src_q, src_s.view(np.float32), in_range)
+    assert np.array_equal(dq.cpu().numpy(), ref_q)
+    assert np.array_equal(dq2.cpu().numpy(), ref_q)
+    assert np.array_equal(ds.cpu().numpy(), ref_s.view(np.int32))
+
+
 @pytest.mark.parametrize("case", ["ragged_strided_negative", "one_source", "identity"])
 def test_gather_long_maps(orc, case):
     """Maps of 1024 rows and more: every copy of a source row is made on one XCD.  Ragged map
