@@ -41,9 +41,9 @@
  *   - Every output element named in a call is overwritten; outputs never need
  *     to be cleared by the caller.
  *   - Argument checks are host-side and look at scalars and pointers only.
- *     Device contents are not validated: a slot id >= the number of slots, a
- *     map entry >= n_src, or offsets that disagree with m_rows are undefined
- *     behaviour.
+ *     Device contents are not validated: a slot id >= the number of slots or
+ *     offsets that disagree with m_rows are undefined behaviour (the gather's
+ *     map entries are bounds-checked on the device, see below).
  *   - A call with no work (zero rows) returns MOE_OK without launching.
  *   - Results are deterministic: no floating-point atomics are used.
  */
@@ -88,7 +88,7 @@ int moe_abi_version(void);
 /* Human-readable text for a moe_status value (static storage). */
 const char* moe_status_string(int status);
 
-/* Text of the last HIP error seen by a launch in this process (static storage). */
+/* Text of the last HIP error seen by a launch on the calling host thread (thread-local storage). */
 const char* moe_last_hip_error(void);
 
 /*
@@ -96,10 +96,13 @@ const char* moe_last_hip_error(void);
  *   for i in [0, n_dst):  src = dst2src[i]
  *     src >= 0: dst_q[i, 0:k] = src_q[src, 0:k]   (bytes, never decoded)
  *               dst_s[i, 0:g] = src_s[src, 0:g]   (raw 32-bit words)
- *     src <  0: dst_q[i, 0:k] = 0 and dst_s[i, 0:g] = +0.0
+ *     src <  0 or src >= n_src: dst_q[i, 0:k] = 0 and dst_s[i, 0:g] = +0.0
+ *       (the page defines in-range entries only; an out-of-range entry is
+ *       caught on the device and reads no source row)
  *   src_q  [n_src][src_q_stride] bytes;  src_s [n_src][src_s_stride] fp32
  *   dst_q  [n_dst][dst_q_stride] bytes;  dst_s [n_dst][dst_s_stride] fp32
- *   g is passed explicitly (normally ceil(k/128)).  Strides >= widths.
+ *   g is passed explicitly (normally ceil(k/128)); g == 0 reads and writes no
+ *   scale word, so src_s and dst_s may then be NULL.  Strides >= widths.
  *   Alignment: none required; 16-byte aligned rows take the vector path.
  *   n_dst == 0 returns MOE_OK with no launch.
  */
@@ -280,8 +283,12 @@ int moe_topk_reduce(const void* y, int y_dt, int64_t y_stride,
  * from call to call: a workspace serves one shape (T, H, I, topk), and calls
  * that share it must not overlap in time (e.g. on two streams without an
  * event between them).  Its first 32-bit word is the error word: nonzero
- * after a call means a hand-off wait gave up, the step's output is not valid,
- * and the workspace must be initialized again.  Size 0 / MOE_ERR_SHAPE for
+ * after a call means the step's output is not valid and the workspace must
+ * be initialized again -- 1: a hand-off wait gave up; 2: the workspace was
+ * initialized for another (T, H, I, topk) (init writes the shape into word 1
+ * of the control block, and the one-launch step checks it before it waits on
+ * any hand-off word).  The library never reads the word on the host; callers
+ * that need the check copy it back themselves.  Size 0 / MOE_ERR_SHAPE for
  * shapes moe_fused_decode rejects.
  */
 size_t moe_fused_decode_workspace_size(int64_t T, int64_t H, int64_t I, int64_t topk);

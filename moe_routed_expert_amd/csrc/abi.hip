@@ -36,7 +36,8 @@ int topk_reduce_launch(hipStream_t st, const void* y, int y_dt, int64_t y_stride
 
 
 
-static char g_last_hip_error[256] = "no HIP error recorded";
+// Per host thread, so that concurrent callers never write one buffer at once.
+static thread_local char g_last_hip_error[256] = "no HIP error recorded";
 
 void note_hip_error(hipError_t e) {
     const char* s = hipGetErrorString(e);
@@ -46,9 +47,10 @@ void note_hip_error(hipError_t e) {
 
 namespace {
 
-__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+// Clears the control block and writes the shape signature into its word 1.
+__global__ void init_ctl_kernel(uint32_t* p, int64_t n, uint32_t sig) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = v;
+    if (i < n) p[i] = i == 1 ? sig : 0u;
 }
 
 struct DecodeLayout {
@@ -256,8 +258,8 @@ extern "C" int moe_fused_decode_workspace_init(void* workspace, size_t ws_bytes,
     if ((int64_t)ws_bytes < L.off[6]) return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MOE_ERR_ALIGN;
     const int64_t words = (L.off[6] - L.off[5]) / 4;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, as_stream(stream),
-                       (uint32_t*)((char*)workspace + L.off[5]), words, 0u);
+    hipLaunchKernelGGL(init_ctl_kernel, dim3((unsigned)ceil_div(words, 256)), dim3(256), 0, as_stream(stream),
+                       (uint32_t*)((char*)workspace + L.off[5]), words, decode_ctl_signature(T, H, I, topk));
     return launch_status();
 }
 

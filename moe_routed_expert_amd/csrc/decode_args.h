@@ -26,6 +26,7 @@ struct FusedDecodeArgs {
     int flag_stride;         // words per route in one copy (set by the launcher)
     int T, H, I, topk;
     int act;                 // gated activation (moe_act 1..5)
+    uint32_t sig;            // decode_ctl_signature of (T, H, I, topk) (set by the launcher)
     int tiles_a;             // gate/up tiles per route (set by the launcher)
     int tiles_c;             // down tiles per token (set by the launcher)
     int n_a;                 // gate/up tiles in total (set by the launcher)
@@ -85,6 +86,18 @@ inline int64_t decode_ctl_bytes(int64_t T, int64_t H, int64_t I, int64_t topk) {
     if (!decode_one_launch_ok(T, H, I, topk)) return 4 * kDecodeCtlLineWords;
     return decode_tagged_h_offset(T, H, I, topk) + 8 * T * topk * I;
 }
+
+// Word 1 of the control block: the shape the workspace was initialized for, packed exactly for every
+// shape the one-launch step takes (T < 2^16, topk <= 64, H/128 <= 16, I/128 <= 8), bit 31 set.  The
+// one-launch step compares it with its own shape before it trusts any hand-off word.
+inline uint32_t decode_ctl_signature(int64_t T, int64_t H, int64_t I, int64_t topk) {
+    return 0x80000000u | (uint32_t)(T & 0xFFFF) | (uint32_t)((topk - 1) & 63) << 16 |
+           (uint32_t)((H / 128 - 1) & 15) << 22 | (uint32_t)((I / 128 - 1) & 7) << 26;
+}
+
+// Values of the error word (word 0 of the control block) after a one-launch step.
+constexpr uint32_t kDecodeErrWait = 1;    // a hand-off wait gave up
+constexpr uint32_t kDecodeErrShape = 2;   // the workspace was initialized for another shape
 
 // Enqueues the decode step as one launch when the shape allows it and all its blocks fit on the
 // device at once; returns 1 without launching otherwise, else a status.

@@ -195,4 +195,14 @@ __device__ __forceinline__ void scalar_read2(const void* p, const void* q, uint3
                  : "memory");
 }
 
+// As scalar_read2, for three words.
+__device__ __forceinline__ void scalar_read3(const void* p, const void* q, const void* r, uint32_t& a, uint32_t& b,
+                                             uint32_t& c) {
+    asm volatile("s_load_dword %0, %3, 0x0\n\ts_load_dword %1, %4, 0x0\n\ts_load_dword %2, %5, 0x0\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&s"(a), "=&s"(b), "=&s"(c)
+                 : "s"(p), "s"(q), "s"(r)
+                 : "memory");
+}
+
 }  // namespace moe

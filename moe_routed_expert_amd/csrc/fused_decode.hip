@@ -34,6 +34,8 @@
 //
 // Results are deterministic: split-K partials and routes are combined in a
 // fixed order, and no floating-point atomics are used.
+#include <atomic>
+
 #include "device.h"
 #include "host.h"
 #include "decode_args.h"
@@ -411,7 +413,13 @@ constexpr int kLateTiles = 4;   // ready words a down tile may still miss when i
 // with coherent loads until it carries `tag`: the last tiles' h arrives with the poll that sees it,
 // without a second round trip after a ready word.  False if the spin limit ran out first.
 template <int NKB2>
-__device__ __forceinline__ bool wait_route_h(const FusedDecodeArgs& a, int64_t r, uint32_t tag, float (&v)[2 * NKB2]) {
+__device__ __forceinline__ bool wait_route_h(const FusedDecodeArgs& a, int64_t r, uint32_t tag, bool shape_ok,
+                                             float (&v)[2 * NKB2]) {
+    if (!shape_ok) {                   // the hand-off words belong to another shape: do not wait on them
+#pragma unroll
+        for (int i = 0; i < 2 * NKB2; i++) v[i] = 0.0f;
+        return false;
+    }
     // the copy this block polls: a copy's line is polled by 1/kDecodeFlagCopies of the down tiles
     const int copy = (int)(blockIdx.x % kDecodeFlagCopies);
     // lanes past the route's tiles read tile 0's word again: no lane branches around a load
@@ -580,11 +588,11 @@ struct RouteAct {
 };
 
 template <int NKB2>
-__device__ __forceinline__ bool route_act(const FusedDecodeArgs& a, int64_t r, uint32_t tag, float* hfw,
-                                          uint8_t (*hqw)[128], RouteAct<NKB2>& ra) {
+__device__ __forceinline__ bool route_act(const FusedDecodeArgs& a, int64_t r, uint32_t tag, bool shape_ok,
+                                          float* hfw, uint8_t (*hqw)[128], RouteAct<NKB2>& ra) {
     const int lane = threadIdx.x & (kWave - 1);
     float hp[2 * NKB2];
-    const bool ok = wait_route_h<NKB2>(a, r, tag, hp);
+    const bool ok = wait_route_h<NKB2>(a, r, tag, shape_ok, hp);
 #pragma unroll
     for (int kb = 0; kb < NKB2; kb++)
         *reinterpret_cast<float2*>(&hfw[kb * 128 + 2 * lane]) = make_float2(hp[2 * kb], hp[2 * kb + 1]);
@@ -647,13 +655,15 @@ __device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
     __shared__ float part[64][kDnRows];
     __shared__ __attribute__((aligned(16))) uint8_t hq[kFdWaves][NKB2][128];
     __shared__ __attribute__((aligned(16))) float hf[kFdWaves][NKB2 * 128];
-    bool timed_out = false;
+    bool timed_out = false, shape_ok = true;
     for (int j = wave_uniform(wave); j < a.topk; j += kFdWaves) {
         const int64_t r = t * a.topk + j;
         // through the scalar cache: a vector load here would return only after this CU's share of
-        // the W13 stream, and the W2 stream could not start before it
-        uint32_t slot_bits, epoch;
-        scalar_read2(a.slots + r, epochs + j, slot_bits, epoch);
+        // the W13 stream, and the W2 stream could not start before it.  Word 1 of the control block
+        // is the shape the workspace was initialized for.
+        uint32_t slot_bits, epoch, sig;
+        scalar_read3(a.slots + r, epochs + j, a.ctl + 1, slot_bits, epoch, sig);
+        shape_ok = sig == a.sig;
         const int slot = (int)slot_bits;
         const uint32_t tag = epoch + 1;
         float val = 0.0f, wgt = 0.0f;
@@ -675,7 +685,7 @@ __device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
 #pragma unroll
             for (int kb = 0; kb < NKB2; kb++) sw[kb] = wsrow[kb];
             RouteAct<NKB2> ra;
-            if (!route_act<NKB2>(a, r, tag, hf[wave], hq[wave], ra)) timed_out = true;
+            if (!route_act<NKB2>(a, r, tag, shape_ok, hf[wave], hq[wave], ra)) timed_out = true;
             // A row 0 carries stream 0's block, A row 1 stream 1's; C[0][c < 8] and C[1][c >= 8] are
             // the two streams' partials of W2 row n0 + (c & 7)
             const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -715,7 +725,7 @@ __device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
         }
         if (lane == 0) store_coherent(epochs + j, tag);
     }
-    if (timed_out && lane == 0) store_coherent(a.ctl, 1u);
+    if ((timed_out || !shape_ok) && lane == 0) store_coherent(a.ctl, shape_ok ? kDecodeErrWait : kDecodeErrShape);
     __syncthreads();
     if (threadIdx.x < kDnRows) {
         float o = 0.0f;
@@ -731,20 +741,23 @@ __global__ void __launch_bounds__(kWave * kFdWaves) decode_step_kernel(FusedDeco
 }
 
 // Workgroups of decode_step_kernel<NKB2, M> that fit on the current device at once (0 if unknown).
+// The value is cached per device; concurrent first calls may both compute it, and store the same value.
 template <int NKB2, int M>
 int step_resident_blocks() {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
+    int c = cached[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_step_kernel<NKB2, M>, kWave * kFdWaves, 0) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
-        cached[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
+        c = per_cu * cus > 0 ? per_cu * cus : -1;
+        cached[dev].store(c, std::memory_order_relaxed);
     }
-    return cached[dev] > 0 ? cached[dev] : 0;
+    return c > 0 ? c : 0;
 }
 
 // Launches the one-launch step if its blocks all fit on the device at once; returns 1 if it did not
@@ -757,6 +770,7 @@ int try_step(hipStream_t st, FusedDecodeArgs a) {
     a.hx = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(a.ctl) + decode_tagged_h_offset(a.T, a.H, a.I, a.topk));
     a.flags = a.ctl + decode_flag_offset(a.T, a.H, a.I, a.topk);
     a.flag_stride = (int)decode_flag_stride(a.I);
+    a.sig = decode_ctl_signature(a.T, a.H, a.I, a.topk);
     const int64_t blocks = (int64_t)a.n_a + (int64_t)a.T * a.tiles_c;
     if (blocks > step_resident_blocks<NKB2, M>()) return 1;
     hipLaunchKernelGGL((decode_step_kernel<NKB2, M>), dim3((unsigned)blocks), dim3(kWave * kFdWaves), 0, st, a);

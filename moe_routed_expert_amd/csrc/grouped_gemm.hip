@@ -54,6 +54,8 @@
 //    lane shuffle plus an 8-wave LDS max, then s = amax/448 and the codes
 //    e4m3(h/s) leave as one 4-byte store per lane; the [rows][2I] GEMM output
 //    is never written.
+#include <atomic>
+
 #include "device.h"
 #include "host.h"
 
@@ -513,10 +515,10 @@ grouped_gemm_kernel(GgArgs g) {
 template <int BM, int OUT_DT, bool FUSED, bool W4>
 static int gg_resident_blocks() {
     using C = GgCfg<BM>;
-    static int cached[64];
+    static std::atomic<int> cached[64];   // concurrent first calls may both fill it, with the same value
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int& c = cached[dev];
+    int c = cached[dev].load(std::memory_order_relaxed);
     if (c == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, OUT_DT, FUSED, W4>, C::THREADS,
@@ -524,6 +526,7 @@ static int gg_resident_blocks() {
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
         c = per_cu * cus > 0 ? per_cu * cus : -1;
+        cached[dev].store(c, std::memory_order_relaxed);
     }
     return c > 0 ? c : 0;
 }

@@ -296,6 +296,52 @@ def test_chained_layers_in_one_graph_like_the_benchmark(orc):
         assert_bf16_close(got, ref, what="layer %d" % l)
         x_in = got
     assert np.all(u16(outs[3]) == 0)                 # layer 3 has no active route
+    ctl = ws[m.fused_decode_workspace_layout(1, H, I, topk)["ctl"]:].view(torch.int32)
+    assert int(ctl[0]) == 0, "a hand-off wait gave up"
+    # one eager call, then two replays of L layers sharing the workspace: each call bumps every epoch
+    assert int(ctl[32]) == 3 * L
+
+
+@pytest.mark.parametrize("active", [8, 5, 0])
+def test_fused_decode_narrow_two_launch_down_tiles(orc, active):
+    """H = 3072 (H/128 = 24 > 16, so never one launch; 3072/16 = 192 wide tiles would not fill the CUs, so the
+    8-row down tiles run): against the oracle with a NaN-poisoned workspace, and the one-launch step's epoch
+    words stay 0."""
+    print("fused decode H=3072 I=768 active=%d/8" % active, flush=True)
+    c = wl.decode_case(H=3072, I=768, topk=8, n_slots=16, active=active, seed=3072 + active)
+    dd = DevDecode(c)
+    assert one_launch_epoch_words(c.T, c.H, c.I, c.topk) == 0
+    dd.poison()
+    dd.run()
+    torch.cuda.synchronize()
+    ref, im = oracle_decode(c)
+    check_against_oracle(dd, ref, im)
+    ctl = dd.ws[dd.lay["ctl"]:dd.lay["total"]].view(torch.int32).cpu().numpy()
+    assert np.all(ctl[2:] == 0) and ctl[0] == 0
+
+
+def test_workspace_of_another_shape_sets_the_error_word(orc):
+    """A workspace initialized for one shape and passed with another (large enough for both): the one-launch
+    step sees the shape word disagree, waits on no hand-off word and sets the error word to 2; a fresh init
+    for the right shape clears it and the step matches the oracle again."""
+    c = wl.decode_case(H=1024, I=768, topk=8, n_slots=12, active=6, seed=51)
+    d = dev()
+    size = max(m.fused_decode_workspace_size(1, 2048, 768, 8), m.fused_decode_workspace_size(1, 1024, 768, 8))
+    dd = DevDecode(c)
+    dd.ws = torch.empty(size, dtype=torch.uint8, device=d)
+    assert m.lib().moe_fused_decode_workspace_init(dd.ws.data_ptr(), size, 1, 2048, 768, 8,
+                                                   m._stream()) == m.MOE_OK
+    dd.run()
+    torch.cuda.synchronize()
+    assert int(dd.ws[dd.lay["ctl"]:dd.lay["ctl"] + 4].view(torch.int32)[0]) == 2
+    assert m.lib().moe_fused_decode_workspace_init(dd.ws.data_ptr(), size, 1, 1024, 768, 8,
+                                                   m._stream()) == m.MOE_OK
+    dd.poison()
+    dd.run()
+    torch.cuda.synchronize()
+    ref, im = oracle_decode(c)
+    check_against_oracle(dd, ref, im)
+    assert check_ctl(dd) == 1, "the step did not run as one launch"
 
 
 def test_ready_words_ahead_of_h_fall_back_to_coherent_loads(orc):
