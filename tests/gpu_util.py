@@ -51,46 +51,70 @@ def _t_dec(codes: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64)
 
 
-def gemm_abs_bound(a_q, a_s, w_q, w_s, experts_of_rows, a_rows):
-    """Per-element bound on |device - oracle| for an fp32 block-FP8 GEMM output.
+BLOCK_ROUNDINGS = 136   # per side: 127 additions inside a 128-wide K block, 2 scale roundings, and slack
 
-    Recursive summation of n terms in any order, each addition rounded or truncated to fp32
-    (unit 2^-23), is within n * 2^-23 * sum|terms| of the exact sum.  Each output sums K exact
-    products plus two scale multiplies and one accumulate per 128-wide block, so each side is within
-    (K + 4K/128 + 4) * 2^-23 * sum_k |a_k w_k s| of the exact result; the MFMA's internal K reduction
-    is covered whatever its order or rounding.  The two sides are within twice that of each other."""
+
+def bound_factor(K):
+    """Per-output bound on |device - oracle| of an fp32 block-scaled GEMM, in units of sum_k |a_k w_k s|.
+
+    Each side sums K exact products.  Inside one 128-wide K block that is at most 127 additions in any order
+    (the MFMA's internal reduction tree on the device, ascending k in the oracle); a sum of n terms whose
+    additions each round or truncate to fp32 (unit u = 2^-23) is within (n - 1) u sum|terms| of the exact
+    sum, whatever the order.  Per block come two roundings of the scale product and of p * s, and one
+    accumulate; split-K forms add at most 8 more accumulates.  So each side is within
+    (136 + 3 K/128) u sum|terms| of the exact result (first order), and the two sides within twice that."""
+    return 2.0 * (BLOCK_ROUNDINGS + 3 * K / 128) * 2.0 ** -23
+
+
+def _rows_by_expert(experts_of_rows):
+    ex = np.asarray(experts_of_rows)
+    return {int(e): np.nonzero(ex == e)[0] for e in np.unique(ex) if e >= 0}
+
+
+def gemm_abs_bound(a_q, a_s, w_q, w_s, experts_of_rows, a_rows):
+    """Per-element bound on |device - oracle| for an fp32 block-FP8 GEMM output: bound_factor(K) times
+    sum_k |a_k| |w_k| sA sW (dequantized magnitudes, float64)."""
     E, N, K = w_q.shape
     A = _t_dec(a_q).abs() * torch.from_numpy(np.repeat(a_s, 128, axis=1)[:, :K]).double()
     out = np.zeros((len(experts_of_rows), N))
-    for r, e in enumerate(experts_of_rows):
-        if e < 0:
-            continue
+    a_rows = np.asarray(a_rows)
+    for e, rows in _rows_by_expert(experts_of_rows).items():
         W = _t_dec(w_q[e]).abs() * torch.from_numpy(
             np.repeat(np.repeat(w_s[e], 128, axis=0), 128, axis=1)[:N, :K]).double()
-        out[r] = (W @ A[a_rows[r]]).numpy()
-    return 2.0 * out * (K + 4 * K / 128 + 4) * 2.0 ** -23
+        out[rows] = (A[torch.from_numpy(a_rows[rows])] @ W.T).numpy()
+    return out * bound_factor(K)
 
 
 E2M1_ABS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0] * 2)   # |value| of each E2M1 code
 
 
 def mxfp4_abs_bound(a_q, a_s, w4, w4_s, experts_of_rows, a_rows):
-    """gemm_abs_bound for MXFP4 weights: the same (K + 4K/128 + 4) * 2^-23 * sum|terms| per side, with
-    |w[e, n, k]| = |e2m1(nibble)| * 2^(w4_s[e, n, k/32] - 127)."""
+    """gemm_abs_bound for MXFP4 weights: the same per-block form, with
+    |w[e, n, k]| = |e2m1(nibble)| * 2^(w4_s[e, n, k/32] - 127) (the E8M0 scale is applied exactly)."""
     E, N, K2 = w4.shape
     K = 2 * K2
     A = _t_dec(a_q).abs() * torch.from_numpy(np.repeat(a_s, 128, axis=1)[:, :K]).double()
     out = np.zeros((len(experts_of_rows), N))
-    cache = {}
-    for r, e in enumerate(experts_of_rows):
-        if e < 0:
-            continue
-        if e not in cache:
-            codes = np.stack([w4[e] & 15, w4[e] >> 4], axis=2).reshape(N, K)
-            scale = np.exp2(np.repeat(w4_s[e].astype(np.float64), 32, axis=1) - 127.0)
-            cache = {e: torch.from_numpy(E2M1_ABS[codes] * scale)}
-        out[r] = (cache[e] @ A[a_rows[r]]).numpy()
-    return 2.0 * out * (K + 4 * K / 128 + 4) * 2.0 ** -23
+    a_rows = np.asarray(a_rows)
+    for e, rows in _rows_by_expert(experts_of_rows).items():
+        codes = np.stack([w4[e] & 15, w4[e] >> 4], axis=2).reshape(N, K)
+        W = torch.from_numpy(E2M1_ABS[codes] * np.exp2(np.repeat(w4_s[e].astype(np.float64), 32, axis=1) - 127.0))
+        out[rows] = (A[torch.from_numpy(a_rows[rows])] @ W.T).numpy()
+    return out * bound_factor(K)
+
+
+def assert_bf16_within_bound(got_bits, ref32, bound, what=""):
+    """Element-wise check of a bf16 output against the oracle's fp32 accumulator: the device's own fp32
+    value is within `bound` of it, and its rounding to bf16 moves it by at most half a bf16 step
+    (2^-8 of its magnitude); the oracle's bf16 output is bf16(ref32), so this also bounds the two outputs'
+    difference."""
+    got = bf16_bits_to_f64(got_bits)
+    ref = np.asarray(ref32, np.float64)
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    allowed = bound + 2.0 ** -8 * (np.abs(ref) + bound) + 1e-38
+    bad = np.abs(got - ref) > allowed
+    assert not bad.any(), "%s: %d bf16 elements beyond the bound (worst excess %.3e)" % (
+        what, bad.sum(), (np.abs(got - ref) - allowed)[bad].max())
 
 
 def assert_within_bound(got, ref, bound, what=""):
