@@ -183,13 +183,15 @@ def prefill_routes(T: int, E: int, topk: int, seed: int) -> PrefillRoutes:
     return PrefillRoutes(T, E, topk, ids, w, dst2src, route_rows.reshape(T, topk), offsets)
 
 
-def fp8_rows(rows: int, k: int, seed: int, device="cpu"):
+def fp8_rows(rows: int, k: int, seed: int, device="cpu", full_range: bool = False):
     """Activation rows as fp8 codes with 1x128 group scales, drawn directly (no quantizer):
-    codes uniform over the finite e4m3 codes with |value| <= 4 (4-bit mantissa grid), scales
-    log-uniform in [2^-8, 2^-4]."""
+    codes uniform over the finite e4m3 codes with |value| <= 4 (4-bit mantissa grid), or with
+    full_range over every finite code (|value| up to 448, subnormals included, as a quantized row's
+    codes span), scales log-uniform in [2^-8, 2^-4]."""
     g = _gen(seed, device)
-    # finite codes with |v| <= 4: exponent field 0..9 (2^(e-7) <= 4) -> codes 0x00..0x48 and their negatives
-    mag = torch.randint(0, 0x49, (rows, k), generator=g, device=device, dtype=torch.int32)
+    # finite codes with |v| <= 4: exponent field 0..9 (2^(e-7) <= 4) -> codes 0x00..0x48 and their negatives;
+    # full range: 0x00..0x7E (0x7F is NaN)
+    mag = torch.randint(0, 0x7F if full_range else 0x49, (rows, k), generator=g, device=device, dtype=torch.int32)
     sign = torch.randint(0, 2, (rows, k), generator=g, device=device, dtype=torch.int32) * 0x80
     q = (mag | sign).to(torch.uint8)
     gk = (k + 127) // 128
@@ -216,11 +218,12 @@ def powers_of_two_case(E: int, N: int, K: int, rows: int, seed: int):
 
 
 def mxfp4_exact_case(E: int, N: int, K: int, rows: int, seed: int):
-    """Exact operands for the MXFP4 GEMM (K <= 1024): activation codes of -4..4 with scales in {1/2, 1, 2},
-    every E2M1 weight code, E8M0 exponents 126..128.  Every partial sum is a multiple of 2^-3 below 2^17, so
-    fp32 holds each one exactly in any order.  Returns numpy arrays
+    """Exact operands for the MXFP4 GEMM (K <= 8192): activation codes of -4..4 with scales in {1/2, 1, 2},
+    every E2M1 weight code, E8M0 exponents 126..128.  Each product is a multiple of 2^-3 of magnitude at most
+    4*2*6*2 = 96, so every partial sum is a multiple of 2^-3 below 96*8192 < 2^20: 23 significant bits, which
+    fp32 holds exactly in any order.  Returns numpy arrays
     (a_q [rows,K], a_s [rows,K/128], w4 [E,N,K/2], w4_s [E,N,K/32])."""
-    assert K <= 1024
+    assert K <= 8192
     rng = np.random.default_rng(seed)
     pos = np.array([0x00, 0x38, 0x40, 0x44, 0x48], np.uint8)
     v = rng.integers(-4, 5, size=(rows, K))
