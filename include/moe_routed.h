@@ -283,8 +283,9 @@ int moe_topk_reduce(const void* y, int y_dt, int64_t y_stride,
  * from call to call: a workspace serves one shape (T, H, I, topk), and calls
  * that share it must not overlap in time (e.g. on two streams without an
  * event between them).  Its first 32-bit word is the error word: nonzero
- * after a call means the step's output is not valid and the workspace must
- * be initialized again -- 1: a hand-off wait gave up; 2: the workspace was
+ * after a call means the step's output is not valid (its affected output
+ * rows are NaN) and the workspace must be initialized again -- 1: a
+ * hand-off wait gave up; 2: the workspace was
  * initialized for another (T, H, I, topk) (init writes the shape into word 1
  * of the control block, and the one-launch step checks it before it waits on
  * any hand-off word).  The library never reads the word on the host; callers

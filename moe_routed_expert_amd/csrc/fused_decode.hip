@@ -725,12 +725,19 @@ __device__ __forceinline__ void down8_tile(const FusedDecodeArgs& a, int b) {
         }
         if (lane == 0) store_coherent(epochs + j, tag);
     }
-    if ((timed_out || !shape_ok) && lane == 0) store_coherent(a.ctl, shape_ok ? kDecodeErrWait : kDecodeErrShape);
+    __shared__ int failed;
+    if (threadIdx.x == 0) failed = 0;
+    __syncthreads();
+    if ((timed_out || !shape_ok) && lane == 0) {
+        store_coherent(a.ctl, shape_ok ? kDecodeErrWait : kDecodeErrShape);
+        failed = 1;
+    }
     __syncthreads();
     if (threadIdx.x < kDnRows) {
         float o = 0.0f;
         for (int j = 0; j < a.topk; j++) o += part[j][threadIdx.x];
-        a.out[t * a.H + n0 + threadIdx.x] = f32_to_bf16(o);
+        // rows whose inputs never arrived are NaN, so a failed step is visible in its output too
+        a.out[t * a.H + n0 + threadIdx.x] = failed ? (uint16_t)0x7FC0u : f32_to_bf16(o);
     }
 }
 
