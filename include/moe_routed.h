@@ -66,7 +66,8 @@ typedef enum {
     MOE_ERR_DTYPE = -3,     /* unsupported element type for this argument */
     MOE_ERR_WORKSPACE = -4, /* workspace too small */
     MOE_ERR_ALIGN = -5,     /* a pointer or stride breaks the required alignment */
-    MOE_ERR_HIP = -6        /* the HIP runtime rejected the launch */
+    MOE_ERR_HIP = -6,       /* the HIP runtime rejected the launch */
+    MOE_ERR_SCRATCH = -7    /* moe_fused_decode_noalloc: the step needs more than its fixed scratch */
 } moe_status;
 
 typedef enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_F16 = 2 } moe_dtype;
@@ -353,6 +354,34 @@ int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, in
                      const uint8_t* w13_q, const float* w13_s,
                      const uint8_t* w2_q, const float* w2_s,
                      void* workspace, size_t ws_bytes, uint16_t* out_bf16, void* stream);
+
+/*
+ * moe_fused_decode_noalloc  -- moe_fused_decode without a caller workspace
+ *   For callers that cannot allocate device memory at all: code under hipGraph
+ *   capture, tight serving loops, harnesses that forbid allocation.  Arguments
+ *   and results are those of moe_fused_decode minus the workspace; the step
+ *   runs the same kernels on a fixed device array inside the library
+ *   (4 MiB, 256-byte aligned; each GPU the library runs on holds its own copy
+ *   until the process ends).  The call allocates and frees nothing.
+ *   Limit: steps whose workspace (moe_fused_decode_workspace_size) exceeds
+ *   4 MiB return MOE_ERR_SCRATCH without launching; e.g. up to 16 tokens at
+ *   H = 4096, I = 1024, top-8.
+ *   State: the array keeps the last call's contents.  The first call on a
+ *   device, and every call whose (T, H, I, topk) differs from that device's
+ *   previous call, first clears the control block with a fill kernel on
+ *   `stream`; later calls of the same shape continue its call counters, as
+ *   with an initialized workspace.  All calls on one GPU share the array, so
+ *   calls that overlap in time on one GPU (two streams, two host threads
+ *   without ordering) race and give undefined results.  The device is the
+ *   current HIP device.
+ *   Errors: as moe_fused_decode, plus MOE_ERR_SCRATCH; if a hand-off wait
+ *   ever gives up, that step's affected output rows are NaN.
+ */
+int moe_fused_decode_noalloc(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk, int act,
+                             const int32_t* slot_ids, const float* weights, int64_t n_slots,
+                             const uint8_t* w13_q, const float* w13_s,
+                             const uint8_t* w2_q, const float* w2_s,
+                             uint16_t* out_bf16, void* stream);
 
 #ifdef __cplusplus
 }

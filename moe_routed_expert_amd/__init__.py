@@ -21,6 +21,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe_routed.so")
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
+MOE_ERR_SCRATCH = -7
 MOE_BF16, MOE_F32, MOE_F16 = 0, 1, 2
 MOE_ACT_IDENTITY, MOE_ACT_SILU_MUL, MOE_ACT_GELU_MUL, MOE_ACT_RELU_MUL, MOE_ACT_SIGMOID_MUL, MOE_ACT_MUL = 0, 1, 2, 3, 4, 5
 MOE_MODE_GROUPED, MOE_MODE_SLOT = 0, 1
@@ -30,7 +31,7 @@ EXPORTS = (
     "moe_pick_block_m", "moe_bf8_grouped_gemm", "moe_topk_reduce", "moe_fused_decode_workspace_size",
     "moe_fused_decode_workspace_layout", "moe_fused_decode_workspace_init", "moe_fused_decode",
     "moe_route_prep_workspace_size", "moe_route_prep", "moe_bf8_grouped_gemm_act_quant",
-    "moe_mxfp4_grouped_gemm", "moe_mxfp4_grouped_gemm_act_quant",
+    "moe_mxfp4_grouped_gemm", "moe_mxfp4_grouped_gemm_act_quant", "moe_fused_decode_noalloc",
 )
 
 _lib = None
@@ -69,6 +70,7 @@ def lib():
             "moe_fused_decode_workspace_layout": ([I64, I64, I64, I64, P], I32),
             "moe_fused_decode_workspace_init": ([P, SZ, I64, I64, I64, I64, P], I32),
             "moe_fused_decode": ([P, I64, I64, I64, I64, I32, P, P, I64, P, P, P, P, P, SZ, P, P], I32),
+            "moe_fused_decode_noalloc": ([P, I64, I64, I64, I64, I32, P, P, I64, P, P, P, P, P, P], I32),
             "moe_route_prep_workspace_size": ([I64, I64], SZ),
             "moe_route_prep": ([P, I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
             "moe_bf8_grouped_gemm_act_quant": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, P, I64,
@@ -243,6 +245,19 @@ def fused_decode(x, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, workspace, out,
     _check("moe_fused_decode", lib().moe_fused_decode(
         _ptr(x), T, H, I, topk, act, _ptr(slot_ids), _ptr(weights), S, _ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s),
         _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream)))
+
+
+def fused_decode_noalloc(x, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, out, act=1, stream=None):
+    """fused_decode on the library's fixed device scratch (no workspace, nothing allocated)."""
+    T, H = x.shape
+    topk = slot_ids.shape[1]
+    S = w13_q.shape[0]
+    I = w13_q.shape[1] // 2
+    for t in (x, slot_ids, weights, w13_q, w13_s, w2_q, w2_s, out):
+        assert t.is_contiguous()
+    _check("moe_fused_decode_noalloc", lib().moe_fused_decode_noalloc(
+        _ptr(x), T, H, I, topk, act, _ptr(slot_ids), _ptr(weights), S, _ptr(w13_q), _ptr(w13_s), _ptr(w2_q),
+        _ptr(w2_s), _ptr(out), _stream(stream)))
 
 
 def route_prep(logits, topk, stream=None):

@@ -3,6 +3,8 @@
 // the fused decode step with its workspace.
 #include <string.h>
 
+#include <mutex>
+
 #include "device.h"
 #include "host.h"
 #include "decode_args.h"
@@ -78,6 +80,20 @@ bool decode_shape_ok(int64_t T, int64_t H, int64_t I, int64_t topk) {
            T * topk <= 65535;
 }
 
+// Scratch of moe_fused_decode_noalloc: a fixed device array standing in for the caller's workspace.  Each
+// GPU the library runs on holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: host code uses the address hipGetSymbolAddress returns
+// for the current device.
+constexpr size_t kNoallocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+struct NoallocDevice {
+    void* ptr = nullptr;                       // device address of `scratch` on this device
+    int64_t shape[4] = {-1, -1, -1, -1};       // (T, H, I, topk) its control block was last initialized for
+};
+std::mutex g_noalloc_mu;
+NoallocDevice g_noalloc[64];
+
 }  // namespace
 }  // namespace moe
 
@@ -94,6 +110,7 @@ extern "C" const char* moe_status_string(int status) {
         case MOE_ERR_WORKSPACE: return "workspace too small";
         case MOE_ERR_ALIGN: return "a pointer or stride breaks the required 16-byte alignment";
         case MOE_ERR_HIP: return "the HIP runtime rejected a launch (see moe_last_hip_error)";
+        case MOE_ERR_SCRATCH: return "the step needs more than the library's fixed 4 MiB decode scratch";
         default: return "unknown status";
     }
 }
@@ -312,4 +329,45 @@ extern "C" int moe_fused_decode(const uint16_t* x_bf16, int64_t T, int64_t H, in
     // 4) routing-weighted reduce
     if (rc == MOE_OK) rc = topk_reduce_launch(st, c2, MOE_F32, H, slot_ids, nullptr, weights, T, topk, H, out_bf16, H);
     return rc;
+}
+
+extern "C" int moe_fused_decode_noalloc(const uint16_t* x_bf16, int64_t T, int64_t H, int64_t I, int64_t topk, int act,
+                                        const int32_t* slot_ids, const float* weights, int64_t n_slots,
+                                        const uint8_t* w13_q, const float* w13_s, const uint8_t* w2_q,
+                                        const float* w2_s, uint16_t* out_bf16, void* stream) {
+    if (!decode_shape_ok(T, H, I, topk) || n_slots < 0) return MOE_ERR_SHAPE;
+    if (act < MOE_ACT_SILU_MUL || act > MOE_ACT_MUL) return MOE_ERR_SHAPE;
+    if (T == 0) return MOE_OK;
+    const DecodeLayout L = decode_layout(T, H, I, topk);
+    if (L.off[6] > (int64_t)kNoallocScratchBytes) return MOE_ERR_SCRATCH;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        note_hip_error(e);
+        return MOE_ERR_HIP;
+    }
+    if (dev < 0 || dev >= 64) return MOE_ERR_HIP;
+    void* ws = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_noalloc_mu);
+        NoallocDevice& d = g_noalloc[dev];
+        if (!d.ptr) {                                  // once per device, with that device current
+            void* p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) {
+                note_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+                return MOE_ERR_HIP;
+            }
+            d.ptr = p;
+        }
+        ws = d.ptr;
+        if (d.shape[0] != T || d.shape[1] != H || d.shape[2] != I || d.shape[3] != topk) {
+            // another shape's control block: clear it (a fill kernel, no memset node) and record the shape
+            const int rc = moe_fused_decode_workspace_init(ws, kNoallocScratchBytes, T, H, I, topk, stream);
+            if (rc != MOE_OK) return rc;
+            d.shape[0] = T; d.shape[1] = H; d.shape[2] = I; d.shape[3] = topk;
+        }
+    }
+    return moe_fused_decode(x_bf16, T, H, I, topk, act, slot_ids, weights, n_slots, w13_q, w13_s, w2_q, w2_s, ws,
+                            kNoallocScratchBytes, out_bf16, stream);
 }

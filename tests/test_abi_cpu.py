@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version_and_status_strings():
     assert m.abi_version() == 1
     L = m.lib()
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert L.moe_status_string(st).decode() not in ("", "unknown status")
     assert L.moe_status_string(7).decode() == "unknown status"
 
@@ -267,3 +267,19 @@ def test_mxfp4_fused_gate_up_act_quant_checks():
     assert call(s_stride=0) == m.MOE_ERR_SHAPE
     assert call(w4_stride_e=128 * 128) == m.MOE_ERR_SHAPE   # 2I rows per expert
     assert call(w4s=P(0x1001)) == m.MOE_ERR_ALIGN
+
+
+def test_fused_decode_noalloc_checks():
+    """The no-workspace decode rejects shapes beyond its fixed 4 MiB scratch and bad arguments on the host,
+    before any HIP call."""
+    L = m.lib()
+    P = ctypes.c_void_p
+    f = L.moe_fused_decode_noalloc
+    args = lambda T, H, I, topk, act=1: (FAKE, T, H, I, topk, act, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert m.fused_decode_workspace_size(32, 4096, 1024, 8) > 4 << 20
+    assert f(*args(32, 4096, 1024, 8)) == m.MOE_ERR_SCRATCH
+    assert m.fused_decode_workspace_size(16, 4096, 1024, 8) <= 4 << 20
+    assert f(*args(1, 2048, 700, 8)) == m.MOE_ERR_SHAPE        # I % 128
+    assert f(*args(1, 2048, 768, 65)) == m.MOE_ERR_SHAPE       # topk > 64
+    assert f(*args(1, 2048, 768, 8, act=0)) == m.MOE_ERR_SHAPE # not a gated activation
+    assert f(*args(0, 2048, 768, 8)) == m.MOE_OK               # no tokens: nothing launched
