@@ -7,8 +7,11 @@ they run inside a model: a captured hipGraph of L=16 chained decode layers
 (layer l+1 takes layer l's output as its token row), each layer with its own
 64-slot expert pool, so the 16 pools (4.8 GB) cannot sit in the 256 MB
 Infinity Cache and every step streams its experts from HBM.  HIP events on
-the stream bracket each graph replay; a step is replay time / 16.  Inputs
-are resident in HBM before the timed region.
+the stream bracket each graph replay; a step is replay time / 16, and the
+headline is the median over max(5, ceil(steps/16)) replays (the pages' own
+method, the median of five ~100 ms windows, is reported beside it).  Inputs
+are resident in HBM before the timed region; after timing, the workspace's
+error word must be clear and the first layer's output must match the oracle.
 
 Also reported: 4/2/0 active routes and H=4096, I=1024 (time vs active
 routes), the fused gather (k=7168 with 8, 64, 512 and 8192 rows; k=896 with
@@ -19,7 +22,9 @@ roofline of the dominant kernel (the single fused decode kernel), and the
 CPU oracle timed on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--skip-prefill] [--skip-cpu]
-       python bench.py --only-headline | --only-prefill | --only-gather | --only-stream   (for counter passes)
+       python bench.py --only-headline [--active A] | --only-prefill | --only-gather | --only-stream
+                                                                         (for counter passes)
+       python bench.py --sweep-bm     (every M tile at the three prefill densities, checked, then timed)
 """
 from __future__ import annotations
 
@@ -123,8 +128,45 @@ def decode_pools(torch, wl, H, I, S, seed):
     return pools
 
 
+def decode_check(torch, m, wl, x0, route, pool, out, H, I, topk):
+    """The first layer's output of the timed graph against the oracle: the active slots' weights are copied to
+    the host (the rest of the pool is never read) and the oracle runs on that compacted bank.  Returns the
+    (rel L2, max abs / max|oracle|) pair; raises when the output breaks the pages' tolerance."""
+    import numpy as np
+    import oracle
+    slots = route[0].cpu().numpy().astype(np.int32)
+    w = route[1].cpu().numpy().astype(np.float32)
+    act = sorted(set(int(v) for v in slots.reshape(-1) if v >= 0))
+    remap = {v: i for i, v in enumerate(act)}
+    small = np.array([[remap[int(v)] if v >= 0 else -1 for v in row] for row in slots], np.int32)
+    idx = torch.tensor(act if act else [0], dtype=torch.long, device=pool[0].device)
+    bank = [t.index_select(0, idx).cpu().numpy() for t in pool]
+    xb = x0.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.bf16_decode(oracle.fused_decode(xb, small, w, *bank)).astype(np.float64)
+    got = oracle.bf16_decode(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    peak = np.abs(ref).max()
+    if peak == 0.0:
+        if not np.all(got == 0.0):
+            raise RuntimeError("decode output is not zero where the oracle's is")
+        return 0.0, 0.0
+    rel = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    mad = float(np.abs(got - ref).max() / peak)
+    if not (rel <= 5e-3 and mad <= 2e-2):
+        raise RuntimeError("decode output differs from the oracle: rel L2 %.3e, max abs %.3e of peak" % (rel, mad))
+    return rel, mad
+
+
+def decode_error_word(torch, m, ws, T, H, I, topk):
+    """The workspace's error word (0 = every hand-off of every call so far completed)."""
+    off = m.fused_decode_workspace_layout(T, H, I, topk)["ctl"]
+    return int(ws[off:off + 4].view(torch.int32).item())
+
+
 def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup):
-    """A graph of LAYERS chained decode steps; returns per-step times from HIP events."""
+    """A graph of LAYERS chained decode steps; per-step times from HIP events around each replay (the
+    headline statistic is their median), plus the pages' method: the median of five windows of about 100 ms
+    of back-to-back replays.  After timing, the workspace's error word must be clear and the first layer's
+    output must match the oracle."""
     dev = torch.device("cuda")
     x0 = wl.bf16_normal((1, H), seed=7, device=dev)
     outs = [torch.empty((1, H), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
@@ -157,16 +199,73 @@ def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     per_step = [u / LAYERS for u in t.us()]
+    # the pages' method: five windows of about 100 ms each, one event pair per window
+    per_window = max(1, int(100e3 / (statistics.median(per_step) * LAYERS)))
+    windows = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(per_window):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        windows.append(a.elapsed_time(b) * 1000.0 / (per_window * LAYERS))
+    torch.cuda.synchronize()
+    err = decode_error_word(torch, m, ws, 1, H, I, topk)
+    if err != 0:
+        raise RuntimeError("decode H=%d I=%d %d/8: the workspace error word is %d after timing" % (H, I, active, err))
+    rel, mad = decode_check(torch, m, wl, x0, routes[0], pools[0], outs[0], H, I, topk)
     nbytes = active * wl.nbytes_expert(H, I)
-    mean = statistics.fmean(per_step)
+    med = statistics.median(per_step)
     res = dict(H=H, I=I, slots=S, topk=topk, active=active, layers_per_graph=LAYERS, replays=reps,
-               us_per_step_mean=mean, us_per_step_median=statistics.median(per_step),
-               us_per_step_min=min(per_step), bytes_streamed=nbytes,
-               hbm_gbs=nbytes / (mean * 1e-6) / 1e9 if nbytes else 0.0,
-               wall_us_per_step=wall * 1e6 / (reps * LAYERS))
+               steps_timed=reps * LAYERS, us_per_step_median=med, us_per_step_mean=statistics.fmean(per_step),
+               us_per_step_min=min(per_step), us_per_step_max=max(per_step),
+               us_per_step_windows_median=statistics.median(windows), window_steps=per_window * LAYERS,
+               bytes_streamed=nbytes, hbm_gbs=nbytes / (med * 1e-6) / 1e9 if nbytes else 0.0,
+               wall_us_per_step=wall * 1e6 / (reps * LAYERS), error_word=err,
+               check_layer0=dict(rel_l2=rel, max_abs_frac=mad))
     res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
     del g
     return res
+
+
+def active_fit(rows):
+    """Least-squares fit t(a) = t0 + a * tau over the decode rows of one shape (a = active routes)."""
+    a = [r["active"] for r in rows]
+    t = [r["us_per_step_median"] for r in rows]
+    n = len(a)
+    ma, mt = sum(a) / n, sum(t) / n
+    saa = sum((x - ma) ** 2 for x in a)
+    tau = sum((x - ma) * (y - mt) for x, y in zip(a, t)) / saa
+    t0 = mt - tau * ma
+    ss_res = sum((y - (t0 + tau * x)) ** 2 for x, y in zip(a, t))
+    ss_tot = sum((y - mt) ** 2 for y in t)
+    return dict(H=rows[0]["H"], I=rows[0]["I"], actives=a, t0_us=t0, tau_us_per_route=tau,
+                r2=1.0 - ss_res / ss_tot if ss_tot else 1.0,
+                tau_gbs=(rows[0]["bytes_streamed"] / rows[0]["active"]) / (tau * 1e-6) / 1e9
+                if rows[0]["active"] and tau > 0 else None)
+
+
+def launch_floor(torch, reps=20):
+    """The empty-kernel floor beside the small gathers: 16 launches of a one-element fill (torch's own
+    kernel) in one graph, timed like the gathers (graph replay / 16)."""
+    dev = torch.device("cuda")
+    bufs = [torch.empty(1, dtype=torch.int32, device=dev) for _ in range(LAYERS)]
+    for b in bufs:
+        b.fill_(1)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=torch.cuda.Stream()):
+        for b in bufs:
+            b.fill_(1)
+    for _ in range(3):
+        gr.replay()
+    t = Timer(torch)
+    for _ in range(reps):
+        t.start()
+        gr.replay()
+        t.stop()
+    return dict(kernel="one-element fill, 16 per graph", us_per_launch=statistics.median(t.us()) / LAYERS)
 
 
 def gather_all(torch, m, wl):
@@ -486,51 +585,199 @@ def route_prep_bench(torch, m, wl, T, E, topk, reps):
     return dict(tokens=T, experts=E, topk=topk, us_per_call=us, bytes=nbytes, gbs=nbytes / (us * 1e-6) / 1e9)
 
 
-def cpu_baseline(wl, budget_s=12.0):
-    """The CPU oracle on the headline workload, on all of the host's cores (at most 16, the host share of
-    one GPU): one thread per core, each running whole decode steps back to back for about budget_s
-    seconds (the oracle's C calls release the GIL).  value = wall time / steps completed."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def run_threads(fn, n):
     import threading
+    th = [threading.Thread(target=fn, args=(i,)) for i in range(n)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+
+
+def cpu_baseline(wl, decode_s=8.0, single_s=2.0):
+    """The CPU oracle, unchanged, on bounded samples of the workloads (its C calls release the GIL, so Python
+    threads run it on several cores at once):
+      * headline (value): decode steps of the headline workload on all of the host's cores (at most 16, one
+        GPU's share of the host), one thread per core running whole steps back to back for decode_s seconds;
+        value = wall time / steps completed;
+      * the same step on one thread (median over single_s seconds of steps);
+      * the 8192-row gather (k = 7168) on one thread and split over all cores;
+      * the prefill GEMMs (gate/up and down) of the 6144-route workload for the rows of experts 0..31, on all
+        cores, the work cut into (expert, 256-column N block) jobs."""
     import numpy as np
     import torch
     import oracle
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
     c = wl.decode_case(H=2048, I=768, topk=8, n_slots=64, active=8, seed=1)
     xb = c.x.view(torch.int16).numpy().view(np.uint16)
     args = [t.numpy() for t in (c.w13_q, c.w13_s, c.w2_q, c.w2_s)]
     oracle.fused_decode(xb, c.slot_ids, c.weights, *args)
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    # one thread
+    single = []
+    t_end = time.perf_counter() + single_s
+    while time.perf_counter() < t_end or len(single) < 3:
+        t0 = time.perf_counter()
+        oracle.fused_decode(xb, c.slot_ids, c.weights, *args)
+        single.append(time.perf_counter() - t0)
+    # all cores
     counts = [0] * cores
     t0 = time.perf_counter()
-    deadline = t0 + budget_s
+    deadline = t0 + decode_s
 
     def worker(i):
         while time.perf_counter() < deadline:
             oracle.fused_decode(xb, c.slot_ids, c.weights, *args)
             counts[i] += 1
 
-    threads = [threading.Thread(target=worker, args=(i,)) for i in range(cores)]
-    for th in threads:
-        th.start()
-    for th in threads:
-        th.join()
+    run_threads(worker, cores)
     dt = time.perf_counter() - t0
     n = sum(counts)
+    # gather: 8192 rows of 7168 bytes + 56 scale words
+    src_q, src_s, mp = wl.gather_case(7168, 1024, 8, seed=50)
+    src_s = src_s.view(np.float32)
+    g1 = []
+    for _ in range(3):
+        t1 = time.perf_counter()
+        oracle.gather_rows_scales(src_q, src_s, mp)
+        g1.append(time.perf_counter() - t1)
+    parts = np.array_split(mp, cores)
+    t1 = time.perf_counter()
+    run_threads(lambda i: oracle.gather_rows_scales(src_q, src_s, parts[i]), cores)
+    g_all = time.perf_counter() - t1
+    gbytes = len(mp) * (7168 + 4 * 56) + len(set(mp.tolist())) * (7168 + 4 * 56)
+    # prefill sample: 6144 routes (T = 1024, E = 256, top-6), experts 0..31, gate/up then down
+    E_s, H, I, T = 32, 4096, 1024, 1024
+    rt = wl.prefill_routes(T, 256, 6, seed=9)
+    r_end = int(rt.expert_offsets[E_s])
+    w13_q, w13_s = (t.numpy() for t in wl.block_fp8_weights(E_s, 2 * I, H, 21, chunk_experts=32))
+    w2_q, w2_s = (t.numpy() for t in wl.block_fp8_weights(E_s, H, I, 22, chunk_experts=32))
+    a1_q, a1_s = (t.numpy()[:r_end] for t in wl.fp8_rows(T * 6, H, seed=23))
+    a2_q, a2_s = (t.numpy()[:r_end] for t in wl.fp8_rows(T * 6, I, seed=24))
+    jobs = []
+    for e in range(E_s):
+        r0, r1 = int(rt.expert_offsets[e]), int(rt.expert_offsets[e + 1])
+        if r1 == r0:
+            continue
+        one = np.array([0, r1 - r0], np.int32)
+        for n0 in range(0, 2 * I, 256):
+            jobs.append((a1_q[r0:r1], a1_s[r0:r1], w13_q[e:e + 1, n0:n0 + 256], w13_s[e:e + 1, n0 // 128:n0 // 128 + 2],
+                         one))
+        for n0 in range(0, H, 256):
+            jobs.append((a2_q[r0:r1], a2_s[r0:r1], w2_q[e:e + 1, n0:n0 + 256], w2_s[e:e + 1, n0 // 128:n0 // 128 + 2],
+                         one))
+    nxt = [0]
+    import threading
+    lock = threading.Lock()
+
+    def gemm_worker(i):
+        while True:
+            with lock:
+                j = nxt[0]
+                nxt[0] += 1
+            if j >= len(jobs):
+                return
+            a, sa, w, sw, o = jobs[j]
+            oracle.block_gemm(a, sa, w, sw, mode=oracle.MODE_GROUPED, expert_offsets=o, out_dtype=np.uint16)
+
+    t1 = time.perf_counter()
+    run_threads(gemm_worker, cores)
+    p_dt = time.perf_counter() - t1
+    p_flops = 2.0 * r_end * (2 * I * H + H * I)
     return dict(value=dt / n * 1e6, unit="us/step", cores=cores, kind="oracle",
                 sample="%d decode steps (bs=1, H=2048, I=768, 64 slots, 8/8 active) on %d threads of the C oracle, "
-                       "%.1f s wall" % (n, cores, dt))
+                       "%.1f s wall" % (n, cores, dt),
+                cpu_model=cpu_model(), hardware_concurrency=os.cpu_count(), threads_used=cores,
+                decode_single_thread_us_per_step=statistics.median(single) * 1e6,
+                decode_single_thread_steps=len(single),
+                gather_8192_rows=dict(k=7168, rows=len(mp), bytes=gbytes,
+                                      single_thread_us=statistics.median(g1) * 1e6,
+                                      all_cores_us=g_all * 1e6, threads=cores),
+                prefill_sample=dict(routes_total=T * 6, experts="0..31", rows=r_end, gemms="gate/up (N=2048, K=4096) "
+                                    "and down (N=4096, K=1024), bf16 out", jobs=len(jobs), threads=cores,
+                                    seconds=p_dt, tflops=p_flops / p_dt / 1e12))
+
+
+def bm_sweep(torch, m, wl, steps=10):
+    """Every M tile at the three prefill densities (E = 256, top-6, H = 4096, I = 1024), gate/up and down
+    (bf16 out).  As on the page, each configuration's output is checked before its time counts: every tile
+    must give the picker's output bit for bit (a tile size changes which rows share a workgroup, not the
+    order of any output's sums), and the picker's output must match the oracle on the rows of the first
+    and the last expert."""
+    import numpy as np
+    import oracle
+    dev = torch.device("cuda")
+    (w13_q, w13_s), (w2_q, w2_s) = prefill_weights(torch, wl, 256, 4096, 1024)
+    H, I, E = 4096, 1024, 256
+    res = []
+    for T in (256, 1024, 4096):
+        R = T * 6
+        rt = wl.prefill_routes(T, E, 6, seed=9)
+        offs = torch.from_numpy(rt.expert_offsets).to(dev)
+        a1_q, a1_s = wl.fp8_rows(R, H, seed=23, device=dev)
+        a2_q, a2_s = wl.fp8_rows(R, I, seed=24, device=dev)
+        pick = m.pick_block_m(R, E)
+        row = dict(routes=R, rows_per_expert=R / E, picked=pick, gemms={})
+        for name, a_q, a_s, w_q, w_s, N, K in (("gate_up", a1_q, a1_s, w13_q, w13_s, 2 * I, H),
+                                                ("down", a2_q, a2_s, w2_q, w2_s, H, I)):
+            base = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+            m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, base, mode=m.MOE_MODE_GROUPED, expert_offsets=offs, block_m=pick)
+            torch.cuda.synchronize()
+            for e in (0, E - 1):
+                r0, r1 = int(rt.expert_offsets[e]), int(rt.expert_offsets[e + 1])
+                ref = oracle.block_gemm(a_q[r0:r1].cpu().numpy(), a_s[r0:r1].cpu().numpy(), w_q[e:e + 1].cpu().numpy(),
+                                        w_s[e:e + 1].cpu().numpy(), mode=oracle.MODE_GROUPED,
+                                        expert_offsets=np.array([0, r1 - r0], np.int32), out_dtype=np.uint16)
+                got = oracle.bf16_decode(base[r0:r1].view(torch.int16).cpu().numpy().view(np.uint16)).astype(float)
+                r = oracle.bf16_decode(ref).astype(float)
+                rel = np.linalg.norm(got - r) / np.linalg.norm(r)
+                if not (rel <= 5e-3 and np.abs(got - r).max() <= 2e-2 * np.abs(r).max()):
+                    raise RuntimeError("bm sweep: %s at %d routes, expert %d: rel L2 %.3e" % (name, R, e, rel))
+            times = {}
+            for bm in (16, 32, 64, 128):
+                out = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
+                m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, out, mode=m.MOE_MODE_GROUPED, expert_offsets=offs, block_m=bm)
+                torch.cuda.synchronize()
+                if not torch.equal(out.view(torch.int16), base.view(torch.int16)):
+                    raise RuntimeError("bm sweep: %s at %d routes: BM=%d differs from BM=%d" % (name, R, bm, pick))
+                t = Timer(torch)
+                for _ in range(steps):
+                    t.start()
+                    m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, out, mode=m.MOE_MODE_GROUPED, expert_offsets=offs,
+                                       block_m=bm)
+                    t.stop()
+                times[bm] = statistics.median(t.us())
+                log("bm sweep %s %d routes BM=%d: %.1f us" % (name, R, bm, times[bm]))
+            best = min(times, key=times.get)
+            row["gemms"][name] = dict(us_median=times, best=best, picked_over_best=times[pick] / times[best])
+        res.append(row)
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=320, help="decode steps timed (multiple of 16)")
+    ap.add_argument("--steps", type=int, default=320,
+                    help="decode steps to time: ceil(steps/16) replays of the 16-layer graph, at least 5")
     ap.add_argument("--warmup", type=int, default=3, help="untimed graph replays")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--active", type=int, default=8, help="active routes of the --only-headline decode (0..8)")
     ap.add_argument("--only-prefill", action="store_true", help="copy calibration and the prefill GEMMs only")
     ap.add_argument("--only-gather", action="store_true", help="copy calibration and the gather configurations only")
     ap.add_argument("--only-stream", action="store_true", help="copy calibration, input quant, requant and reduce only")
+    ap.add_argument("--sweep-bm", action="store_true",
+                    help="every M tile at the three prefill densities, each checked before it is timed")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -540,9 +787,12 @@ def main():
     import workloads as wl
     m.lib()
     torch.cuda.init()
-    reps = max(1, args.steps // LAYERS)
-    steps = reps * LAYERS
+    reps = max(5, -(-args.steps // LAYERS))
     calib = copy_calibration(torch, m)
+    if args.sweep_bm:
+        print(json.dumps({"metric": "prefill grouped GEMM us per M tile (checked)", "copy_calibration": calib,
+                          "bm_sweep": bm_sweep(torch, m, wl)}))
+        return
     if args.only_prefill:
         print(json.dumps({"metric": "prefill fp8 TFLOP/s (grouped GEMMs only)", "copy_calibration": calib,
                           "prefill_densities": prefill_all(torch, m, wl)}))
@@ -558,36 +808,42 @@ def main():
 
     log("decode H=2048 I=768: building %d layer pools" % LAYERS)
     pools = decode_pools(torch, wl, 2048, 768, 64, seed=1)
-    log("decode H=2048 I=768 8/8 (headline)")
-    head = decode_bench(torch, m, wl, pools, 2048, 768, 64, 8, 8, reps, args.warmup)
+    head_active = args.active if args.only_headline else 8
+    log("decode H=2048 I=768 %d/8 (headline)" % head_active)
+    head = decode_bench(torch, m, wl, pools, 2048, 768, 64, 8, head_active, reps, args.warmup)
     extra = {"decode": [head]}
-    if not args.only_headline:
-        for active in (4, 2, 0):
-            log("decode H=2048 I=768 %d/8" % active)
-            extra["decode"].append(decode_bench(torch, m, wl, pools, 2048, 768, 64, 8, active, reps, args.warmup))
-        del pools
-        torch.cuda.empty_cache()
-        log("decode H=4096 I=1024: building %d layer pools" % LAYERS)
-        pools = decode_pools(torch, wl, 4096, 1024, 64, seed=2)
-        for active in (8, 4, 2, 0):
-            log("decode H=4096 I=1024 %d/8" % active)
-            extra["decode"].append(decode_bench(torch, m, wl, pools, 4096, 1024, 64, 8, active, reps, args.warmup))
-        del pools
-        torch.cuda.empty_cache()
-        log("gather")
-        extra["gather"] = gather_all(torch, m, wl)
-        log("input quant, requant and reduce at prefill sizes")
-        extra["stream_ops"] = stream_ops_bench(torch, m, wl)
-        log("route prep")
-        extra["route_prep"] = [route_prep_bench(torch, m, wl, T, 256, 6, 20) for T in (256, 4096)]
-        if not args.skip_prefill:
-            extra["prefill_densities"] = prefill_all(torch, m, wl)
-            extra["prefill"] = extra["prefill_densities"][-1]
+    if args.only_headline:
+        print(json.dumps({"metric": "decode us/step (headline configuration only)", "copy_calibration": calib,
+                          "decode": head}))
+        return
+    for active in (4, 2, 0):
+        log("decode H=2048 I=768 %d/8" % active)
+        extra["decode"].append(decode_bench(torch, m, wl, pools, 2048, 768, 64, 8, active, reps, args.warmup))
+    del pools
+    torch.cuda.empty_cache()
+    log("decode H=4096 I=1024: building %d layer pools" % LAYERS)
+    pools = decode_pools(torch, wl, 4096, 1024, 64, seed=2)
+    for active in (8, 4, 2, 0):
+        log("decode H=4096 I=1024 %d/8" % active)
+        extra["decode"].append(decode_bench(torch, m, wl, pools, 4096, 1024, 64, 8, active, reps, args.warmup))
+    del pools
+    torch.cuda.empty_cache()
+    extra["decode_fit"] = [active_fit([r for r in extra["decode"] if r["H"] == h]) for h in (2048, 4096)]
+    log("gather")
+    extra["gather"] = gather_all(torch, m, wl)
+    extra["launch_floor"] = launch_floor(torch)
+    log("input quant, requant and reduce at prefill sizes")
+    extra["stream_ops"] = stream_ops_bench(torch, m, wl)
+    log("route prep")
+    extra["route_prep"] = [route_prep_bench(torch, m, wl, T, 256, 6, 20) for T in (256, 4096)]
+    if not args.skip_prefill:
+        extra["prefill_densities"] = prefill_all(torch, m, wl)
+        extra["prefill"] = extra["prefill_densities"][-1]
     tr = measured_traffic()
     roof = dict(bound="hbm",
                 kernel="moe_fused_decode step = one decode_step_kernel launch (gate/up and down tiles in one "
                        "grid; H=2048, I=768, 8/8 active)",
-                bytes_per_launch=head["bytes_streamed"], us_per_launch=head["us_per_step_mean"],
+                bytes_per_launch=head["bytes_streamed"], us_per_launch=head["us_per_step_median"],
                 achieved=head["hbm_gbs"], peak=HBM_PEAK_GBS, unit="GB/s", frac=head["hbm_frac"],
                 traffic=tr["traffic_bytes_per_step"] if tr else None)
     extra["copy_calibration"] = calib
@@ -597,20 +853,23 @@ def main():
         cpu = cpu_baseline(wl)
     line = {
         "metric": "bs1 decode us/step & HBM GB/s (top-k 8); prefill fp8 TFLOP/s vs peak",
-        "value": round(head["us_per_step_mean"], 3),
+        "value": round(head["us_per_step_median"], 3),
         "unit": "us/step",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": head["steps_timed"],
+        "steps_requested": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["us_per_step_mean"] / 1000.0,
+        "ms_per_step": head["us_per_step_median"] / 1000.0,
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3",
         "data": "synthetic (seeded N(0,0.02) block-FP8 expert banks, N(0,1) bf16 activations)",
         "config": {"workload": "decode bs=1, H=2048, I=768, 64-slot pool per layer, top-k 8, 8/8 active; "
-                               "16 chained layers per graph, weights from HBM",
-                   "hbm_gbs": round(head["hbm_gbs"], 1), "hbm_frac": round(head["hbm_frac"], 4)},
+                               "16 chained layers per graph, weights from HBM; value = median over %d replays" % reps,
+                   "hbm_gbs": round(head["hbm_gbs"], 1), "hbm_frac": round(head["hbm_frac"], 4),
+                   "t0_us": round(extra["decode_fit"][0]["t0_us"], 3),
+                   "tau_us_per_route": round(extra["decode_fit"][0]["tau_us_per_route"], 3)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extra": extra,
@@ -619,4 +878,8 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    try:
+        main()
+    except RuntimeError as e:          # a failed output check or a set error word: no valid line
+        print("bench.py: %s" % e, file=sys.stderr)
+        sys.exit(3)
