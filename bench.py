@@ -7,11 +7,13 @@ they run inside a model: a captured hipGraph of L=16 chained decode layers
 (layer l+1 takes layer l's output as its token row), each layer with its own
 64-slot expert pool, so the 16 pools (4.8 GB) cannot sit in the 256 MB
 Infinity Cache and every step streams its experts from HBM.  HIP events on
-the stream bracket each graph replay; a step is replay time / 16, and the
-headline is the median over max(5, ceil(steps/16)) replays (the pages' own
-method, the median of five ~100 ms windows, is reported beside it).  Inputs
-are resident in HBM before the timed region; after timing, the workspace's
-error word must be clear and the first layer's output must match the oracle.
+the stream bracket five windows of back-to-back graph replays (the timed
+max(5, ceil(steps/16)) replays, at least 4 per window, split five ways); a
+step is window time / (replays x 16), and the headline is the median window,
+the pages' method (their five ~100 ms windows are reported beside it).
+Inputs are resident in HBM before the timed region; after timing, the
+workspace's error word must be clear and the first layer's output must match
+the oracle.
 
 Also reported: 4/2/0 active routes and H=4096, I=1024 (time vs active
 routes), the fused gather (k=7168 with 8, 64, 512 and 8192 rows; k=896 with
@@ -163,10 +165,11 @@ def decode_error_word(torch, m, ws, T, H, I, topk):
 
 
 def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup):
-    """A graph of LAYERS chained decode steps; per-step times from HIP events around each replay (the
-    headline statistic is their median), plus the pages' method: the median of five windows of about 100 ms
-    of back-to-back replays.  After timing, the workspace's error word must be clear and the first layer's
-    output must match the oracle."""
+    """A graph of LAYERS chained decode steps, timed as on the pages: the median of five windows of
+    back-to-back graph replays, one event pair per window.  The timed steps are split into the five
+    windows (max(4, ceil(reps/5)) replays each; value = the median window's time per step); the pages' exact form,
+    five windows of about 100 ms each, is reported beside it.  After timing, the workspace's error word must
+    be clear and the first layer's output must match the oracle."""
     dev = torch.device("cuda")
     x0 = wl.bf16_normal((1, H), seed=7, device=dev)
     outs = [torch.empty((1, H), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
@@ -190,39 +193,39 @@ def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup):
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
-    t = Timer(torch)
+
+    def windows(n_win, per_window):
+        out = []
+        for _ in range(n_win):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(per_window):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            out.append(a.elapsed_time(b) * 1000.0 / (per_window * LAYERS))
+        return out
+
+    per_win = max(4, -(-reps // 5))      # at least 4 back-to-back replays (64 steps) per window
     wall0 = time.perf_counter()
-    for _ in range(reps):
-        t.start()
-        g.replay()
-        t.stop()
-    torch.cuda.synchronize()
+    timed = windows(5, per_win)
     wall = time.perf_counter() - wall0
-    per_step = [u / LAYERS for u in t.us()]
-    # the pages' method: five windows of about 100 ms each, one event pair per window
-    per_window = max(1, int(100e3 / (statistics.median(per_step) * LAYERS)))
-    windows = []
-    for _ in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(per_window):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        windows.append(a.elapsed_time(b) * 1000.0 / (per_window * LAYERS))
-    torch.cuda.synchronize()
+    med = statistics.median(timed)
+    # the pages' method as printed: five windows of about 100 ms
+    per_100ms = max(1, int(100e3 / (med * LAYERS)))
+    pages = windows(5, per_100ms)
     err = decode_error_word(torch, m, ws, 1, H, I, topk)
     if err != 0:
         raise RuntimeError("decode H=%d I=%d %d/8: the workspace error word is %d after timing" % (H, I, active, err))
     rel, mad = decode_check(torch, m, wl, x0, routes[0], pools[0], outs[0], H, I, topk)
     nbytes = active * wl.nbytes_expert(H, I)
-    med = statistics.median(per_step)
-    res = dict(H=H, I=I, slots=S, topk=topk, active=active, layers_per_graph=LAYERS, replays=reps,
-               steps_timed=reps * LAYERS, us_per_step_median=med, us_per_step_mean=statistics.fmean(per_step),
-               us_per_step_min=min(per_step), us_per_step_max=max(per_step),
-               us_per_step_windows_median=statistics.median(windows), window_steps=per_window * LAYERS,
+    res = dict(H=H, I=I, slots=S, topk=topk, active=active, layers_per_graph=LAYERS, windows=5,
+               replays_per_window=per_win, steps_timed=5 * per_win * LAYERS,
+               us_per_step_median=med, us_per_step_windows=timed, us_per_step_min=min(timed),
+               us_per_step_max=max(timed), us_per_step_100ms_windows_median=statistics.median(pages),
+               steps_per_100ms_window=per_100ms * LAYERS,
                bytes_streamed=nbytes, hbm_gbs=nbytes / (med * 1e-6) / 1e9 if nbytes else 0.0,
-               wall_us_per_step=wall * 1e6 / (reps * LAYERS), error_word=err,
+               wall_us_per_step=wall * 1e6 / (5 * per_win * LAYERS), error_word=err,
                check_layer0=dict(rel_l2=rel, max_abs_frac=mad))
     res["hbm_frac"] = res["hbm_gbs"] / HBM_PEAK_GBS
     del g
@@ -767,7 +770,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320,
-                    help="decode steps to time: ceil(steps/16) replays of the 16-layer graph, at least 5")
+                    help="decode steps to time: max(5, ceil(steps/16)) replays of the 16-layer graph (at least "
+                         "4 per window) in five windows")
     ap.add_argument("--warmup", type=int, default=3, help="untimed graph replays")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
@@ -866,7 +870,8 @@ def main():
         "dtype": "fp8e4m3",
         "data": "synthetic (seeded N(0,0.02) block-FP8 expert banks, N(0,1) bf16 activations)",
         "config": {"workload": "decode bs=1, H=2048, I=768, 64-slot pool per layer, top-k 8, 8/8 active; "
-                               "16 chained layers per graph, weights from HBM; value = median over %d replays" % reps,
+                               "16 chained layers per graph, weights from HBM; value = median of 5 windows of %d replays"
+                               % head["replays_per_window"],
                    "hbm_gbs": round(head["hbm_gbs"], 1), "hbm_frac": round(head["hbm_frac"], 4),
                    "t0_us": round(extra["decode_fit"][0]["t0_us"], 3),
                    "tau_us_per_route": round(extra["decode_fit"][0]["tau_us_per_route"], 3)},
