@@ -440,6 +440,281 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     }
 }
 
+// ---------------------------------------------------------------------------
+// BM = 128, block-FP8 weights: the tiles of a workgroup as one continuous K-step pipeline.  One workgroup
+// fills a CU at this tile size, so nothing else on the CU hides a tile's start (the ring refilling from
+// empty) or its epilogue (stores, or the fused activation requant).  Here the lookahead loads of a tile's
+// last steps already fetch the next tile's first steps, and the next tile's scales, requested at the
+// start of the tile before, are written into the other half of a double-buffered scale table once that
+// tile's first group of K steps is under way; a tile's epilogue then runs while the next tile's first
+// weight and A steps are in flight, and the next tile starts without a wait.  Every tile takes
+// nsteps = ceil(K/128 / S) * S steps (the steps past K/128 only keep the ring in phase), so a step's
+// ring slot and A stage are its index within the S-step group, as in grouped_gemm_tile.
+
+// The wave-uniform position of one tile.
+struct TileId {
+    int expert, row0, row_end, n_tile;
+};
+
+template <int BM, int OUT_DT, bool FUSED>
+__device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int* cum_lds, const int* off_lds, int t,
+                                                     int hi, int m_tile, int n_tile) {
+    using C = GgCfg<BM>;
+    constexpr int TPW = C::TPW;
+    constexpr int CPW = 16 * TPW;
+    constexpr int MS = BM / 16;
+    constexpr int S = C::S;
+    constexpr int SA = C::S;
+    constexpr int NT = C::THREADS;
+    constexpr int A_CHUNKS = BM * 8;
+    constexpr int A_PER_THREAD = (A_CHUNKS + NT - 1) / NT;
+    constexpr int SA_ROW = BM + 4;
+    constexpr int SA_ROWS = BM / C::WAVES;
+    __shared__ __attribute__((aligned(32))) uint8_t a_lds[2][BM * 128];
+    __shared__ __attribute__((aligned(16))) float sa_lds[2][kGgMaxKb * SA_ROW];   // [tile parity][kb][row]
+    __shared__ float ws_lds[2][2][kGgMaxKb];                                       // [tile parity][block][kb]
+
+    const uint8_t* __restrict__ a_q = g.a_q;
+    const float* __restrict__ a_s = g.a_s;
+    const uint8_t* __restrict__ w_q = g.w_q;
+    const float* __restrict__ w_s = g.w_s;
+    const int64_t N = g.N, K = g.K, I = N / 2;
+    const int n_experts = g.n_experts, n_tiles_n = g.n_tiles_n, per_xcd = g.per_xcd;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int nkb = (int)(K / 128);
+    const int last = nkb - 1;
+    const int nsteps = (nkb + S - 1) / S * S;
+    const int q16 = (lane / 16) * 16;
+    const int kbl = lane < nkb ? lane : nkb - 1;
+
+    auto lookup = [&](int mt, int nt) {
+        int e_lo = 0, e_hi = n_experts - 1;
+        while (e_lo < e_hi) {
+            const int mid = (e_lo + e_hi + 1) / 2;
+            if (__builtin_amdgcn_readfirstlane(cum_lds[mid]) <= mt)
+                e_lo = mid;
+            else
+                e_hi = mid - 1;
+        }
+        TileId ti;
+        ti.expert = e_lo;
+        ti.row0 = __builtin_amdgcn_readfirstlane(off_lds[e_lo]) + (mt - __builtin_amdgcn_readfirstlane(cum_lds[e_lo])) * BM;
+        ti.row_end = __builtin_amdgcn_readfirstlane(off_lds[e_lo + 1]);
+        ti.n_tile = nt;
+        return ti;
+    };
+    auto advance = [&]() {
+        t += per_xcd;
+        m_tile += g.step_m;
+        n_tile += g.step_n;
+        if (n_tile >= n_tiles_n) {
+            n_tile -= n_tiles_n;
+            m_tile++;
+        }
+    };
+
+    // per-lane addressing of a tile (the layout of each piece is grouped_gemm_tile's)
+    struct Addr {
+        const uint8_t* wp0;
+        const uint8_t* wp1;
+        int64_t a_src[A_PER_THREAD];
+    };
+    auto wcol_of = [&](const TileId& ti) -> int64_t {
+        const int64_t n0 = (int64_t)ti.n_tile * C::BN;
+        const bool cols = FUSED || n0 + wv * CPW < N;
+        return FUSED ? (int64_t)ti.n_tile * 128 + 16 * wv : (cols ? n0 + wv * CPW : n0);
+    };
+    auto addr_of = [&](const TileId& ti) {
+        Addr ad;
+        const int64_t wcol = wcol_of(ti);
+        ad.wp0 = w_q + (int64_t)ti.expert * g.w_stride_e + (wcol + (lane & 15)) * g.w_stride_n + q16;
+        ad.wp1 = ad.wp0 + (FUSED ? I : 16) * g.w_stride_n;
+#pragma unroll
+        for (int j = 0; j < A_PER_THREAD; j++) {
+            const int c0 = tid + j * NT;
+            const int c = c0 < A_CHUNKS ? c0 : c0 % A_CHUNKS;
+            int row = ti.row0 + c / 8;
+            if (row >= ti.row_end) row = ti.row_end - 1;
+            ad.a_src[j] = (int64_t)row * g.a_stride + (c % 8) * 16;
+        }
+        return ad;
+    };
+    int a_dst[A_PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < A_PER_THREAD; j++) {
+        const int c0 = tid + j * NT;
+        const int c = c0 < A_CHUNKS ? c0 : c0 % A_CHUNKS;
+        const int rr = c / 8, ch = c % 8;
+        a_dst[j] = (rr / 16) * 2048 + ((rr % 16) + 16 * (ch % 4)) * 32 + (ch / 4) * 16;
+    }
+
+    // a tile's scales: requested into registers (lane = K block), written to one half of the tables
+    struct Scales {
+        float sa[SA_ROWS];
+        float ws;
+    };
+    auto scales_of = [&](const TileId& ti) {
+        Scales sv;
+#pragma unroll
+        for (int j = 0; j < SA_ROWS; j++) {
+            const int rr = wave + j * C::WAVES;
+            const int row = ti.row0 + rr < ti.row_end ? ti.row0 + rr : ti.row_end - 1;
+            sv.sa[j] = a_s[(int64_t)row * g.a_s_stride + kbl];
+        }
+        sv.ws = 0.0f;
+        if (wave < 2) {
+            const int64_t n0 = (int64_t)ti.n_tile * C::BN;
+            const int64_t nblk = (N - n0) >= 256 ? 2 : 1;
+            const int64_t b = FUSED ? (wave == 0 ? ti.n_tile : I / 128 + ti.n_tile) : n0 / 128 + (wave < nblk ? wave : 0);
+            sv.ws = w_s[(int64_t)ti.expert * g.w_s_stride_e + b * g.w_s_stride_n + kbl];
+        }
+        return sv;
+    };
+    auto commit_scales = [&](const Scales& sv, int tp) {
+        if (lane < nkb) {
+#pragma unroll
+            for (int j = 0; j < SA_ROWS; j++) sa_lds[tp][lane * SA_ROW + wave + j * C::WAVES] = sv.sa[j];
+            if (wave < 2) ws_lds[tp][wave][lane] = sv.ws;
+        }
+    };
+
+    v4i a_reg[SA][A_PER_THREAD];
+    v4i w_ring[S][2 * TPW];
+    auto load_a = [&](const Addr& ad, int kb, int stage) {
+#pragma unroll
+        for (int j = 0; j < A_PER_THREAD; j++)
+            a_reg[stage][j] = *reinterpret_cast<const v4i*>(a_q + ad.a_src[j] + (int64_t)kb * 128);
+    };
+    auto store_a = [&](int stage, int buf) {
+#pragma unroll
+        for (int j = 0; j < A_PER_THREAD; j++)
+            if (A_CHUNKS % NT == 0 || tid + j * NT < A_CHUNKS)
+                *reinterpret_cast<v4i*>(&a_lds[buf][a_dst[j]]) = a_reg[stage][j];
+    };
+    auto load_w = [&](const Addr& ad, int kb, v4i* w) {
+        const int64_t o = (int64_t)kb * 128;
+        w[0] = *reinterpret_cast<const v4i*>(ad.wp0 + o);
+        w[1] = *reinterpret_cast<const v4i*>(ad.wp0 + o + 64);
+        if constexpr (TPW == 2) {
+            w[2] = *reinterpret_cast<const v4i*>(ad.wp1 + o);
+            w[3] = *reinterpret_cast<const v4i*>(ad.wp1 + o + 64);
+        }
+    };
+
+    if (t >= hi) return;
+    TileId cur = lookup(m_tile, n_tile);
+    advance();
+    bool has_next = t < hi;
+    TileId nxt = has_next ? lookup(m_tile, n_tile) : cur;
+    Addr ca = addr_of(cur);
+    Addr na = addr_of(nxt);
+    int tp = 0;                                      // half of the scale tables the current tile reads
+    // prologue of the first tile: its scales, A and W steps 0..S-2, A step 0 into LDS
+    {
+        const Scales s0 = scales_of(cur);
+#pragma unroll
+        for (int s = 0; s < S - 1; s++) {
+            load_a(ca, s < last ? s : last, s % SA);
+            load_w(ca, s < last ? s : last, w_ring[s]);
+        }
+        commit_scales(s0, 0);
+    }
+    store_a(0, 0);
+    __syncthreads();
+    int par = 0;                                     // A buffer of the current step
+    for (;;) {
+        const Scales sn = scales_of(nxt);            // the next tile's scales, written after the first group
+        v4f acc[MS][TPW];
+#pragma unroll
+        for (int m = 0; m < MS; m++)
+#pragma unroll
+            for (int c = 0; c < TPW; c++) acc[m][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        const int64_t n0 = (int64_t)cur.n_tile * C::BN;
+        const bool cols = FUSED || n0 + wv * CPW < N;
+        const int wsb = FUSED ? 0 : (int)((wcol_of(cur) - n0) / 128);
+        const int tile_rows = __builtin_amdgcn_readfirstlane(cur.row_end - cur.row0);
+        const float* sa_t = sa_lds[tp];
+        for (int kb0 = 0; kb0 < nsteps; kb0 += S) {
+#pragma unroll
+            for (int s = 0; s < S; s++) {
+                const int kb = kb0 + s;
+                // the lookahead step: this tile's (its last step again past K/128), or, once it runs past
+                // this tile's steps, the next tile's first steps (all loads unconditional: the pointers
+                // are selected)
+                const int la = kb + S - 1;
+                const bool nx = la >= nsteps;
+                const int ls = nx ? (la - nsteps < last ? la - nsteps : last) : (la < last ? la : last);
+                Addr sel;
+                sel.wp0 = nx ? na.wp0 : ca.wp0;
+                sel.wp1 = nx ? na.wp1 : ca.wp1;
+#pragma unroll
+                for (int j = 0; j < A_PER_THREAD; j++) sel.a_src[j] = nx ? na.a_src[j] : ca.a_src[j];
+                load_a(sel, ls, (s + S - 1) % SA);
+                load_w(sel, ls, w_ring[(s + S - 1) % S]);
+                if (kb < nkb) {
+                    float sw[TPW];
+#pragma unroll
+                    for (int c = 0; c < TPW; c++) sw[c] = ws_lds[tp][FUSED ? c : wsb][kb];
+                    v8i b[TPW];
+#pragma unroll
+                    for (int c = 0; c < TPW; c++)
+                        b[c] = __builtin_shufflevector(w_ring[s][2 * c], w_ring[s][2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int m = 0; m < MS; m++) {
+                        if (MS > 4 && m * 16 >= tile_rows) continue;
+                        const v8i a = *reinterpret_cast<const v8i*>(&a_lds[par][m * 2048 + lane * 32]);
+                        const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                        const float sa = sa_t[kb * SA_ROW + m * 16 + (lane & 15)];
+#pragma unroll
+                        for (int c = 0; c < TPW; c++) acc[m][c] += mfma16x16x128_e4m3(b[c], a, zero) * (sa * sw[c]);
+                    }
+                }
+                store_a((s + 1) % SA, par ^ 1);     // A step kb+1 (the next tile's step 0 after the last step)
+                __syncthreads();
+                par ^= 1;
+            }
+            // after the first group (its loads issued, so the wait below covers only old requests): the
+            // next tile's scales into the other half of the tables, read first after the tile boundary
+            if (kb0 == 0 && has_next) commit_scales(sn, tp ^ 1);
+        }
+        // the tile's epilogue, with the next tile's first S-1 steps in flight
+        if constexpr (FUSED) {
+            act_quant_epilogue<BM>(g, acc, cur.row0, cur.row_end, cur.n_tile, lane, wave);
+        } else {
+            void* __restrict__ out = g.out;
+            const int64_t out_stride = g.out_stride;
+            const bool vec4 = (out_stride % 4 == 0) &&
+                              (reinterpret_cast<uintptr_t>(out) % (OUT_DT == kF32 ? 16 : 8) == 0);
+#pragma unroll
+            for (int m = 0; m < MS; m++) {
+                const int row = cur.row0 + m * 16 + (lane & 15);
+                if (cols && row < cur.row_end) {
+                    const int64_t o = (int64_t)row * out_stride + n0 + wave * CPW + 4 * (lane / 16);
+#pragma unroll
+                    for (int c = 0; c < TPW; c++) {
+                        if (vec4) {
+                            store4_from_f32<OUT_DT>(out, o + 16 * c, acc[m][c]);
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; i++) store_from_f32<OUT_DT>(out, o + 16 * c + i, acc[m][c][i]);
+                        }
+                    }
+                }
+            }
+        }
+        if (!has_next) return;
+        cur = nxt;
+        ca = na;
+        tp ^= 1;
+        advance();
+        has_next = t < hi;
+        nxt = has_next ? lookup(m_tile, n_tile) : cur;
+        na = addr_of(nxt);
+    }
+}
+
 template <int BM, int OUT_DT, bool FUSED, bool W4>
 __global__ void __launch_bounds__(GgCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(GgCfg<BM>::WAVES_PER_EU, 8)))
 grouped_gemm_kernel(GgArgs g) {
@@ -486,6 +761,9 @@ grouped_gemm_kernel(GgArgs g) {
     int t = lo + slot;
     // (M tile, N tile) of t, advanced by (step_m, step_n) = divmod(per_xcd, n_tiles_n) per tile
     int m_tile = t / n_tiles_n, n_tile = t - m_tile * n_tiles_n;
+    if constexpr (BM == 128 && !W4) {
+        grouped_gemm_walk128<BM, OUT_DT, FUSED>(g, cum_lds, off_lds, t, hi, m_tile, n_tile);
+    } else {
     for (; t < hi; t += per_xcd) {
         // last expert whose first tile <= m_tile; the table values are made wave-uniform so the tile's
         // addresses stay scalar
@@ -508,6 +786,7 @@ grouped_gemm_kernel(GgArgs g) {
             n_tile -= n_tiles_n;
             m_tile++;
         }
+    }
     }
 }
 
