@@ -164,7 +164,7 @@ def decode_error_word(torch, m, ws, T, H, I, topk):
     return int(ws[off:off + 4].view(torch.int32).item())
 
 
-def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup):
+def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup, pages_windows=True):
     """A graph of LAYERS chained decode steps, timed as on the pages: the median of five windows of
     back-to-back graph replays, one event pair per window.  The timed steps are split into the five
     windows (max(4, ceil(reps/5)) replays each; value = the median window's time per step); the pages' exact form,
@@ -211,9 +211,9 @@ def decode_bench(torch, m, wl, pools, H, I, S, topk, active, reps, warmup):
     timed = windows(5, per_win)
     wall = time.perf_counter() - wall0
     med = statistics.median(timed)
-    # the pages' method as printed: five windows of about 100 ms
-    per_100ms = max(1, int(100e3 / (med * LAYERS)))
-    pages = windows(5, per_100ms)
+    # the pages' method as printed: five windows of about 100 ms (left out of counter passes)
+    per_100ms = max(1, int(100e3 / (med * LAYERS))) if pages_windows else 0
+    pages = windows(5, per_100ms) if pages_windows else [float("nan")]
     err = decode_error_word(torch, m, ws, 1, H, I, topk)
     if err != 0:
         raise RuntimeError("decode H=%d I=%d %d/8: the workspace error word is %d after timing" % (H, I, active, err))
@@ -775,7 +775,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3, help="untimed graph replays")
     ap.add_argument("--skip-prefill", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
-    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="the headline decode configuration only, without the 100 ms windows (for counter passes)")
     ap.add_argument("--active", type=int, default=8, help="active routes of the --only-headline decode (0..8)")
     ap.add_argument("--only-prefill", action="store_true", help="copy calibration and the prefill GEMMs only")
     ap.add_argument("--only-gather", action="store_true", help="copy calibration and the gather configurations only")
@@ -814,7 +815,8 @@ def main():
     pools = decode_pools(torch, wl, 2048, 768, 64, seed=1)
     head_active = args.active if args.only_headline else 8
     log("decode H=2048 I=768 %d/8 (headline)" % head_active)
-    head = decode_bench(torch, m, wl, pools, 2048, 768, 64, 8, head_active, reps, args.warmup)
+    head = decode_bench(torch, m, wl, pools, 2048, 768, 64, 8, head_active, reps, args.warmup,
+                        pages_windows=not args.only_headline)
     extra = {"decode": [head]}
     if args.only_headline:
         print(json.dumps({"metric": "decode us/step (headline configuration only)", "copy_calibration": calib,
