@@ -441,13 +441,15 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
 }
 
 // ---------------------------------------------------------------------------
-// BM = 128, block-FP8 weights: the tiles of a workgroup as one continuous K-step pipeline.  One workgroup
-// fills a CU at this tile size, so nothing else on the CU hides a tile's start (the ring refilling from
-// empty) or its epilogue (stores, or the fused activation requant).  Here the lookahead loads of a tile's
-// last steps already fetch the next tile's first steps, and the next tile's scales, requested at the
-// start of the tile before, are written into the other half of a double-buffered scale table once that
-// tile's first group of K steps is under way; a tile's epilogue then runs while the next tile's first
-// weight and A steps are in flight, and the next tile starts without a wait.  Every tile takes
+// BM = 128: the tiles of a workgroup as one continuous K-step pipeline.  One workgroup fills a CU at this
+// tile size, so nothing else on the CU hides a tile's start (the ring refilling from empty) or its
+// epilogue (stores, or the fused activation requant).  Here the lookahead loads of a tile's last steps
+// already fetch the next tile's first steps, and the next tile's A (and block-FP8 weight) scales,
+// requested at the start of the tile before, are written into the other half of a double-buffered scale
+// table once that tile's first group of K steps is under way.  MXFP4: each wave's E8M0 chunk of the next
+// tile is requested before the epilogue and written to LDS after it (requested in the last group
+// instead, its 16 registers stay live through the whole K loop and the long-K launches ran 3-5% slower).
+// A tile's epilogue then runs while the next tile's first weight and A steps are in flight.  Every tile takes
 // nsteps = ceil(K/128 / S) * S steps (the steps past K/128 only keep the ring in phase), so a step's
 // ring slot and A stage are its index within the S-step group, as in grouped_gemm_tile.
 
@@ -456,7 +458,7 @@ struct TileId {
     int expert, row0, row_end, n_tile;
 };
 
-template <int BM, int OUT_DT, bool FUSED>
+template <int BM, int OUT_DT, bool FUSED, bool W4>
 __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int* cum_lds, const int* off_lds, int t,
                                                      int hi, int m_tile, int n_tile) {
     using C = GgCfg<BM>;
@@ -472,7 +474,9 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
     constexpr int SA_ROWS = BM / C::WAVES;
     __shared__ __attribute__((aligned(32))) uint8_t a_lds[2][BM * 128];
     __shared__ __attribute__((aligned(16))) float sa_lds[2][kGgMaxKb * SA_ROW];   // [tile parity][kb][row]
-    __shared__ float ws_lds[2][2][kGgMaxKb];                                       // [tile parity][block][kb]
+    __shared__ float ws_lds[2][2][W4 ? 1 : kGgMaxKb];                              // [tile parity][block][kb]
+    // MXFP4: each wave's E8M0 bytes of its 32 weight rows, 32 K steps at a time (as grouped_gemm_tile)
+    __shared__ __attribute__((aligned(16))) uint8_t sc_lds[W4 ? C::WAVES * 32 * kScRow : 4];
 
     const uint8_t* __restrict__ a_q = g.a_q;
     const float* __restrict__ a_s = g.a_s;
@@ -488,6 +492,8 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
     const int nsteps = (nkb + S - 1) / S * S;
     const int q16 = (lane / 16) * 16;
     const int kbl = lane < nkb ? lane : nkb - 1;
+    const int sshift = 8 * (lane / 16);
+    uint8_t* const sc_wave = sc_lds + wave * 32 * kScRow;
 
     auto lookup = [&](int mt, int nt) {
         int e_lo = 0, e_hi = n_experts - 1;
@@ -564,7 +570,7 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
             sv.sa[j] = a_s[(int64_t)row * g.a_s_stride + kbl];
         }
         sv.ws = 0.0f;
-        if (wave < 2) {
+        if (!W4 && wave < 2) {
             const int64_t n0 = (int64_t)ti.n_tile * C::BN;
             const int64_t nblk = (N - n0) >= 256 ? 2 : 1;
             const int64_t b = FUSED ? (wave == 0 ? ti.n_tile : I / 128 + ti.n_tile) : n0 / 128 + (wave < nblk ? wave : 0);
@@ -576,7 +582,38 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
         if (lane < nkb) {
 #pragma unroll
             for (int j = 0; j < SA_ROWS; j++) sa_lds[tp][lane * SA_ROW + wave + j * C::WAVES] = sv.sa[j];
-            if (wave < 2) ws_lds[tp][wave][lane] = sv.ws;
+            if (!W4 && wave < 2) ws_lds[tp][wave][lane] = sv.ws;
+        }
+    };
+    // MXFP4: this wave's E8M0 chunk of a tile from K step kb0 (32 steps of its 32 rows; lanes 0-31 one row,
+    // 32-63 the next), as 16 dwords per lane
+    struct Chunk {
+        uint32_t w[W4 ? 16 : 1];
+    };
+    auto chunk_of = [&](const TileId& ti, int kb0) {
+        Chunk ck;
+        if constexpr (W4) {
+            const uint8_t* base = g.w4s + (int64_t)ti.expert * g.w4s_stride_e + wcol_of(ti) * g.w4s_stride_n;
+            const int64_t sub = (FUSED ? I : 16) * g.w4s_stride_n;
+            int l = lane;
+            asm volatile("" : "+v"(l));
+            const bool in = (l & 31) < nkb - kb0;
+            const uint32_t lo = (uint32_t)((l >> 5) * g.w4s_stride_n + 4 * (l & 31));
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                const uint8_t* u = base + (i / 8) * sub + (2 * (i % 8)) * g.w4s_stride_n + 4 * (int64_t)kb0;
+                ck.w[i] = in ? *reinterpret_cast<const uint32_t*>(u + lo) : 0u;
+            }
+        }
+        return ck;
+    };
+    auto commit_chunk = [&](const Chunk& ck) {
+        if constexpr (W4) {
+            wave_lds_fence();
+#pragma unroll
+            for (int i = 0; i < 16; i++)
+                *reinterpret_cast<uint32_t*>(sc_wave + (2 * i + (lane >> 5)) * kScRow + 4 * (lane & 31)) = ck.w[i];
+            wave_lds_fence();
         }
     };
 
@@ -594,6 +631,12 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
                 *reinterpret_cast<v4i*>(&a_lds[buf][a_dst[j]]) = a_reg[stage][j];
     };
     auto load_w = [&](const Addr& ad, int kb, v4i* w) {
+        if constexpr (W4) {
+            const int64_t o = (int64_t)kb * 64;
+            w[0] = *reinterpret_cast<const v4i*>(ad.wp0 + o);
+            w[1] = *reinterpret_cast<const v4i*>(ad.wp1 + o);
+            return;
+        }
         const int64_t o = (int64_t)kb * 128;
         w[0] = *reinterpret_cast<const v4i*>(ad.wp0 + o);
         w[1] = *reinterpret_cast<const v4i*>(ad.wp0 + o + 64);
@@ -613,12 +656,14 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
     int tp = 0;                                      // half of the scale tables the current tile reads
     // prologue of the first tile: its scales, A and W steps 0..S-2, A step 0 into LDS
     {
+        const Chunk c0 = chunk_of(cur, 0);
         const Scales s0 = scales_of(cur);
 #pragma unroll
         for (int s = 0; s < S - 1; s++) {
             load_a(ca, s < last ? s : last, s % SA);
             load_w(ca, s < last ? s : last, w_ring[s]);
         }
+        commit_chunk(c0);
         commit_scales(s0, 0);
     }
     store_a(0, 0);
@@ -636,7 +681,15 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
         const int wsb = FUSED ? 0 : (int)((wcol_of(cur) - n0) / 128);
         const int tile_rows = __builtin_amdgcn_readfirstlane(cur.row_end - cur.row0);
         const float* sa_t = sa_lds[tp];
+        int sc_kb = 0;                               // MXFP4: first K step of the chunk in sc_lds
+        constexpr int kScSteps = 32 / S * S;
         for (int kb0 = 0; kb0 < nsteps; kb0 += S) {
+            if constexpr (W4) {
+                if (kb0 - sc_kb == kScSteps && kb0 < nkb) {   // next chunk of this tile (K > 32 steps)
+                    sc_kb = kb0;
+                    commit_chunk(chunk_of(cur, kb0));
+                }
+            }
 #pragma unroll
             for (int s = 0; s < S; s++) {
                 const int kb = kb0 + s;
@@ -654,9 +707,16 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
                 load_a(sel, ls, (s + S - 1) % SA);
                 load_w(sel, ls, w_ring[(s + S - 1) % S]);
                 if (kb < nkb) {
+                    uint32_t e8[TPW];                     // MXFP4: the E8M0 byte of the step, per sub-tile
+                    if constexpr (W4) {
+#pragma unroll
+                        for (int c = 0; c < TPW; c++)
+                            e8[c] = (*reinterpret_cast<const uint32_t*>(sc_wave + (16 * c + (lane & 15)) * kScRow +
+                                                                        4 * (kb - sc_kb)) >> sshift) & 0xFFu;
+                    }
                     float sw[TPW];
 #pragma unroll
-                    for (int c = 0; c < TPW; c++) sw[c] = ws_lds[tp][FUSED ? c : wsb][kb];
+                    for (int c = 0; c < TPW; c++) sw[c] = W4 ? 1.0f : ws_lds[tp][FUSED ? c : wsb][kb];
                     v8i b[TPW];
 #pragma unroll
                     for (int c = 0; c < TPW; c++)
@@ -668,7 +728,12 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
                         const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                         const float sa = sa_t[kb * SA_ROW + m * 16 + (lane & 15)];
 #pragma unroll
-                        for (int c = 0; c < TPW; c++) acc[m][c] += mfma16x16x128_e4m3(b[c], a, zero) * (sa * sw[c]);
+                        for (int c = 0; c < TPW; c++) {
+                            if constexpr (W4)
+                                acc[m][c] += mfma16x16x128_fp4_e4m3(w_ring[s][c], e8[c], a, zero) * sa;
+                            else
+                                acc[m][c] += mfma16x16x128_e4m3(b[c], a, zero) * (sa * sw[c]);
+                        }
                     }
                 }
                 store_a((s + 1) % SA, par ^ 1);     // A step kb+1 (the next tile's step 0 after the last step)
@@ -679,7 +744,9 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
             // next tile's scales into the other half of the tables, read first after the tile boundary
             if (kb0 == 0 && has_next) commit_scales(sn, tp ^ 1);
         }
-        // the tile's epilogue, with the next tile's first S-1 steps in flight
+        // the tile's epilogue, with the next tile's first S-1 steps in flight (MXFP4: and its first E8M0
+        // chunk; nxt is the current tile again after the last one)
+        const Chunk cn = chunk_of(nxt, 0);
         if constexpr (FUSED) {
             act_quant_epilogue<BM>(g, acc, cur.row0, cur.row_end, cur.n_tile, lane, wave);
         } else {
@@ -705,6 +772,7 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
             }
         }
         if (!has_next) return;
+        commit_chunk(cn);                            // this wave's reads of the chunk ended with its last step
         cur = nxt;
         ca = na;
         tp ^= 1;
@@ -715,7 +783,7 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
     }
 }
 
-template <int BM, int OUT_DT, bool FUSED, bool W4>
+template <int BM, int OUT_DT, bool FUSED, bool W4, bool WALK>
 __global__ void __launch_bounds__(GgCfg<BM>::THREADS) __attribute__((amdgpu_waves_per_eu(GgCfg<BM>::WAVES_PER_EU, 8)))
 grouped_gemm_kernel(GgArgs g) {
     const int32_t* __restrict__ offsets = g.offsets;
@@ -761,8 +829,8 @@ grouped_gemm_kernel(GgArgs g) {
     int t = lo + slot;
     // (M tile, N tile) of t, advanced by (step_m, step_n) = divmod(per_xcd, n_tiles_n) per tile
     int m_tile = t / n_tiles_n, n_tile = t - m_tile * n_tiles_n;
-    if constexpr (BM == 128 && !W4) {
-        grouped_gemm_walk128<BM, OUT_DT, FUSED>(g, cum_lds, off_lds, t, hi, m_tile, n_tile);
+    if constexpr (WALK) {
+        grouped_gemm_walk128<BM, OUT_DT, FUSED, W4>(g, cum_lds, off_lds, t, hi, m_tile, n_tile);
     } else {
     for (; t < hi; t += per_xcd) {
         // last expert whose first tile <= m_tile; the table values are made wave-uniform so the tile's
@@ -791,7 +859,7 @@ grouped_gemm_kernel(GgArgs g) {
 }
 
 // Workgroups of one configuration the device holds at once (cached per device and variant).
-template <int BM, int OUT_DT, bool FUSED, bool W4>
+template <int BM, int OUT_DT, bool FUSED, bool W4, bool WALK>
 static int gg_resident_blocks() {
     using C = GgCfg<BM>;
     static std::atomic<int> cached[64];   // concurrent first calls may both fill it, with the same value
@@ -800,7 +868,7 @@ static int gg_resident_blocks() {
     int c = cached[dev].load(std::memory_order_relaxed);
     if (c == 0) {
         int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, OUT_DT, FUSED, W4>, C::THREADS,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, grouped_gemm_kernel<BM, OUT_DT, FUSED, W4, WALK>, C::THREADS,
                                                          0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -811,22 +879,40 @@ static int gg_resident_blocks() {
 }
 
 // Fills the tile walk of g (N tiles of BN columns, or I/128 act groups when fused) and launches.
-template <int BM, int OUT_DT, bool FUSED, bool W4>
-static int launch_grouped(hipStream_t st, GgArgs g) {
+template <int BM, int OUT_DT, bool FUSED, bool W4, bool WALK>
+static int launch_grouped_walk(hipStream_t st, GgArgs g) {
     using C = GgCfg<BM>;
     if (g.N % 128 != 0 || (FUSED && g.N % 256 != 0)) return MOE_ERR_SHAPE;
     const int64_t n_tiles_n = FUSED ? g.N / 256 : ceil_div(g.N, C::BN);
     if (g.m_rows > 0x7FFFFFFF || n_tiles_n * (ceil_div(g.m_rows, BM) + g.n_experts) > 0x7FFFFFFF - (1 << 20))
         return MOE_ERR_SHAPE;
-    const int wgs = gg_resident_blocks<BM, OUT_DT, FUSED, W4>();
+    const int wgs = gg_resident_blocks<BM, OUT_DT, FUSED, W4, WALK>();
     if (wgs < kXcds) return MOE_ERR_HIP;
     g.n_tiles_n = (int)n_tiles_n;
     g.per_xcd = wgs / kXcds;
     g.step_m = g.per_xcd / g.n_tiles_n;
     g.step_n = g.per_xcd % g.n_tiles_n;
-    hipLaunchKernelGGL((grouped_gemm_kernel<BM, OUT_DT, FUSED, W4>), dim3((unsigned)(g.per_xcd * kXcds)),
+    hipLaunchKernelGGL((grouped_gemm_kernel<BM, OUT_DT, FUSED, W4, WALK>), dim3((unsigned)(g.per_xcd * kXcds)),
                        dim3(C::THREADS), 0, st, g);
     return launch_status();
+}
+
+// BM = 128 runs a workgroup's tiles as one pipeline (grouped_gemm_walk128).  With MXFP4 weights only up
+// to kW4WalkMaxKb K steps per tile: at the 24576-route prefill (E = 256, I = 1024) it took the down GEMM
+// (8 steps) from 290 to 260-265 us at H = 4096 and from 155 to 141 us at H = 2048, and the H = 2048
+// gate/up GEMM (16 steps) 1-3 % faster, but the H = 4096 gate/up GEMM (32 steps) ran 1-5 % slower than
+// with tiles one at a time.
+constexpr int kW4WalkMaxKb = 16;
+
+template <int BM, int OUT_DT, bool FUSED, bool W4>
+static int launch_grouped(hipStream_t st, const GgArgs& g) {
+    if constexpr (BM == 128 && !W4)
+        return launch_grouped_walk<BM, OUT_DT, FUSED, W4, true>(st, g);
+    else if constexpr (BM == 128)
+        return g.K / 128 <= kW4WalkMaxKb ? launch_grouped_walk<BM, OUT_DT, FUSED, W4, true>(st, g)
+                                         : launch_grouped_walk<BM, OUT_DT, FUSED, W4, false>(st, g);
+    else
+        return launch_grouped_walk<BM, OUT_DT, FUSED, W4, false>(st, g);
 }
 
 template <int BM, bool W4>

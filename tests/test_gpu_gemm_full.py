@@ -5,9 +5,11 @@
 * The prefill workload (E = 256, top-6, H = 4096, I = 1024) at 1536, 6144 and 24576 routes in the launch
   the picker chooses ("perf(dsfp4): pick the grouped-prefill tile from route density on sm_89",
   Measurements): the gate/up GEMM (bf16 out), the fused gate/up + SiLU requant and the down GEMM (bf16 out),
-  block-FP8, and MXFP4 at 6144 routes.  Every column of the rows of four experts is compared with the
+  block-FP8, and MXFP4 at 6144 and 24576 routes.  Every column of the rows of four experts is compared with the
   oracle: expert 0, expert E-1, and the experts whose rows start the third and the sixth of the eight
   per-XCD ranges of the persistent tile walk.
+* At 24576 routes, the BM = 128 launch (a workgroup's tiles as one pipeline) against the BM = 64 launch
+  (tiles one at a time), bit for bit, block-FP8 and MXFP4.
 """
 import concurrent.futures as cf
 
@@ -219,8 +221,8 @@ def test_prefill_full_size_fp8_vs_oracle(orc, T):
     assert not torch.isnan(as_).any()
 
 
-def test_prefill_full_size_mxfp4_vs_oracle(orc):
-    T = 1024
+@pytest.mark.parametrize("T", [1024, 4096])
+def test_prefill_full_size_mxfp4_vs_oracle(orc, T):
     R = T * TOPK
     bm = m.pick_block_m(R, E_FULL)
     print("prefill mxfp4 full size: %d routes, BM=%d" % (R, bm), flush=True)
@@ -268,3 +270,49 @@ def test_prefill_full_size_mxfp4_vs_oracle(orc):
                 assert_bf16_within_bound(got, ref, bound, what=what)
     assert not torch.isnan(c1.float()).any() and not torch.isnan(c2.float()).any()
     assert not torch.isnan(as_).any()
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_block_m_128_tile_walk_equals_single_tiles(fmt):
+    """At 24576 routes each BM = 128 workgroup runs many tiles back to back as one K-step pipeline (the next
+    tile's first steps and scales in flight during a tile's last steps and epilogue; with MXFP4 weights
+    only for the down GEMM, whose tiles have 8 K steps).  Each output element takes the same K order at
+    every tile size, so the gate/up GEMM (f32 out), its fused SiLU requant and the down GEMM (bf16 out)
+    must equal the BM = 64 launch, whose tiles run one at a time, bit for bit."""
+    T = 4096
+    R = T * TOPK
+    assert m.pick_block_m(R, E_FULL) == 128
+    print("BM=128 walk vs BM=64 tiles, %s, %d routes" % (fmt, R), flush=True)
+    d = dev()
+    if fmt == "fp8":
+        w13, w13_s = wl.block_fp8_weights(E_FULL, 2 * I, H, 41, device=d, chunk_experts=32)
+        w2, w2_s = wl.block_fp8_weights(E_FULL, H, I, 42, device=d, chunk_experts=32)
+        gemm = lambda a, s_, w, ws, od, out, bm: m.bf8_grouped_gemm(a, s_, w, ws, out, mode=m.MOE_MODE_GROUPED,
+                                                                     expert_offsets=od, block_m=bm)
+        fused = lambda a, s_, w, ws, od, q, s, bm: m.bf8_grouped_gemm_act_quant(a, s_, w, ws, od, q, s, block_m=bm)
+    else:
+        w13, w13_s = wl.mxfp4_weights(E_FULL, 2 * I, H, seed=43, device=d)
+        w2, w2_s = wl.mxfp4_weights(E_FULL, H, I, seed=44, device=d)
+        gemm = lambda a, s_, w, ws, od, out, bm: m.mxfp4_grouped_gemm(a, s_, w, ws, od, out, block_m=bm)
+        fused = lambda a, s_, w, ws, od, q, s, bm: m.mxfp4_grouped_gemm_act_quant(a, s_, w, ws, od, q, s,
+                                                                                  block_m=bm)
+    rt = wl.prefill_routes(T, E_FULL, TOPK, seed=45)
+    od = to_dev(rt.expert_offsets)
+    a1_q, a1_s = wl.fp8_rows(R, H, seed=46, device=d, full_range=True)
+    a2_q, a2_s = wl.fp8_rows(R, I, seed=47, device=d, full_range=True)
+    res = {}
+    for bm in (128, 64):
+        c1 = torch.full((R, 2 * I), float("nan"), dtype=torch.float32, device=d)
+        q = torch.full((R, I), 0xAB, dtype=torch.uint8, device=d)
+        s = torch.full((R, I // 128), float("nan"), dtype=torch.float32, device=d)
+        c2 = torch.full((R, H), float("nan"), dtype=torch.bfloat16, device=d)
+        gemm(a1_q, a1_s, w13, w13_s, od, c1, bm)
+        fused(a1_q, a1_s, w13, w13_s, od, q, s, bm)
+        gemm(a2_q, a2_s, w2, w2_s, od, c2, bm)
+        res[bm] = (c1.view(torch.int32), q, s.view(torch.int32), c2.view(torch.int16))
+    torch.cuda.synchronize()
+    assert not torch.isnan(res[128][0].view(torch.float32)).any()
+    for name, x, y in zip(("gate/up", "codes", "scales", "down"), res[128], res[64]):
+        bad = (x != y).nonzero()
+        assert bad.numel() == 0, "%s %s: %d elements differ, first at %s" % (fmt, name, bad.shape[0],
+                                                                              bad[0].tolist())
