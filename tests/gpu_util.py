@@ -52,18 +52,22 @@ def _t_dec(codes: np.ndarray) -> torch.Tensor:
 
 
 BLOCK_ROUNDINGS = 136   # per side: 127 additions inside a 128-wide K block, 2 scale roundings, and slack
+MFMA_BLOCK_SUM = 2.0 ** -11   # the device's sum of one K block's 128 products, as a fraction of their sum |p|
 
 
 def bound_factor(K):
     """Per-output bound on |device - oracle| of an fp32 block-scaled GEMM, in units of sum_k |a_k w_k s|.
 
-    Each side sums K exact products.  Inside one 128-wide K block that is at most 127 additions in any order
-    (the MFMA's internal reduction tree on the device, ascending k in the oracle); a sum of n terms whose
-    additions each round or truncate to fp32 (unit u = 2^-23) is within (n - 1) u sum|terms| of the exact
-    sum, whatever the order.  Per block come two roundings of the scale product and of p * s, and one
-    accumulate; split-K forms add at most 8 more accumulates.  So each side is within
-    (136 + 3 K/128) u sum|terms| of the exact result (first order), and the two sides within twice that."""
-    return 2.0 * (BLOCK_ROUNDINGS + 3 * K / 128) * 2.0 ** -23
+    Each side sums K exact products, 128 at a time.  The oracle adds a block's products in ascending k in
+    fp32, within 127 u sum|p| of their exact sum (u = 2^-23: any order, rounding or truncating).  The
+    device's fp8 MFMA does not add them in fp32: like other fp8 matrix units it keeps only about 13-14
+    significant bits of the block sum (its products are aligned to the largest one and truncated, which
+    biases all-positive sums downward).  Measured on MI355X over 2M block sums against the exact sum, its
+    error reached 2^-12.5 of the block's sum|p| with all products positive and 2^-13.2 with random signs;
+    the bound takes 2^-11 for it.  Per block, each side also rounds the scale product and p * s and
+    accumulates once in fp32; split-K forms add at most 8 accumulates.  So the two sides are within
+    (2^-11 + 2 (136 + 3 K/128) u) sum|a w s| of each other."""
+    return MFMA_BLOCK_SUM + 2.0 * (BLOCK_ROUNDINGS + 3 * K / 128) * 2.0 ** -23
 
 
 def _rows_by_expert(experts_of_rows):
