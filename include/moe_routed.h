@@ -82,6 +82,9 @@ typedef enum {
     MOE_ACT_MUL = 5           /* g * u */
 } moe_act;
 typedef enum { MOE_MODE_GROUPED = 0, MOE_MODE_SLOT = 1 } moe_gemm_mode;
+/* Passed as the weight row stride (w_stride_n, w4_stride_n) of the grouped-mode GEMMs: the weights are
+ * in the packed order that moe_pack_weights writes, and the expert stride keeps its meaning. */
+#define MOE_W_PACKED (-1)
 
 /* Version of this header the library was built from (MOE_ABI_VERSION). */
 int moe_abi_version(void);
@@ -150,7 +153,9 @@ int moe_pick_block_m(int64_t routes, int64_t experts);
  * moe_bf8_grouped_gemm  -- block-FP8 GEMM for the gate/up and the down projections
  *   ("bf8" = block-FP8 with e4m3 operands.)
  *   out[r, n] = sum_kb ( sum_{k in kb} A[ar, k] * W[e, n, k] ) * a_s[ar, kb] * w_s[e, n/128, kb]
- *   with fp8 products exact and fp32 accumulation; one 128-wide K block per scale pair.
+ *   with fp8 products exact; the 128 products of a K block are summed by the fp8 MFMA, which keeps
+ *   about 13-14 significant bits of that sum (error below 2^-12 of the block's sum |products|), and
+ *   the scaled block sums are accumulated in fp32.
  *   a_q  [*][a_stride] fp8,   a_s [*][a_s_stride] fp32 (K/128 used)
  *   w_q  [n_experts] x [N][K] fp8: element (e,n,k) at e*w_stride_e + n*w_stride_n + k
  *   w_s  fp32: block (e,nb,kb) at e*w_s_stride_e + nb*w_s_stride_n + kb
@@ -172,6 +177,8 @@ int moe_pick_block_m(int64_t routes, int64_t experts);
  *   N % 128 == 0, 1 <= n_experts <= 1024 and K <= 8192 (a tile keeps all its
  *   K-block scales in LDS); MOE_ERR_SHAPE otherwise.  n_experts == 0 with NULL
  *   w_q/w_s is allowed in slot mode (an empty bank: every slot must be < 0).
+ *   Grouped mode also takes a packed bank (moe_pack_weights with step_bytes
+ *   128): w_stride_n = MOE_W_PACKED, w_stride_e >= N*K when n_experts > 1.
  */
 int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
                          const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
@@ -197,6 +204,7 @@ int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s,
  *   by moe_act_quant with the same act on it, bit for bit.
  *   Requirements: I % 128 == 0, K % 128 == 0, K <= 8192, 1 <= n_experts <=
  *   1024, alignment as moe_bf8_grouped_gemm; m_rows == 0 launches nothing.
+ *   w_stride_n = MOE_W_PACKED takes a packed bank as moe_bf8_grouped_gemm.
  */
 int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
                                    const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
@@ -213,7 +221,8 @@ int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const f
  *   two per byte with K element 2i in the low nibble, and one E8M0 scale byte
  *   (2^(e-127)) per 32 consecutive K elements.
  *   out[r, n] = sum_kb ( sum_{k in kb} A[r, k] * W[e, n, k] * 2^(w4_s[e, n, k/32] - 127) ) * a_s[r, kb]
- *   with products exact and fp32 accumulation (kb = 128-wide K blocks).
+ *   with products exact, each 128-wide K block (kb) summed by the MFMA as in moe_bf8_grouped_gemm
+ *   and the scaled block sums accumulated in fp32.
  *   a_q, a_s: fp8 activations with 1x128 fp32 scales, as moe_bf8_grouped_gemm.
  *   w4   [n_experts] x [N][K/2] bytes: the byte of (e, n, k) is at
  *        e*w4_stride_e + n*w4_stride_n + k/2 (strides in BYTES).
@@ -226,6 +235,8 @@ int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const f
  *   its strides 4-byte aligned (MOE_ERR_ALIGN).  A scale byte of 255 (NaN in
  *   the format) gives results this library does not define, and so do scaled
  *   products below the fp32 normal range.  m_rows == 0 launches nothing.
+ *   w4_stride_n = MOE_W_PACKED takes a packed bank (moe_pack_weights with
+ *   step_bytes 64), w4_stride_e >= N*K/2 when n_experts > 1; w4_s unchanged.
  */
 int moe_mxfp4_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
                            const uint8_t* w4, int64_t w4_stride_e, int64_t w4_stride_n,
@@ -250,6 +261,31 @@ int moe_mxfp4_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stride, const
                                      int64_t n_experts, int64_t I, int64_t K, const int32_t* expert_offsets,
                                      int64_t m_rows, int32_t block_m, int act, uint8_t* out_q, int64_t q_stride,
                                      float* out_s, int64_t s_stride, void* stream);
+
+/*
+ * moe_pack_weights  -- an expert bank in the grouped GEMMs' operand order
+ *   Not a step of the pages' method: a one-time copy of static weights into an
+ *   order in which every 1 KiB load of the grouped GEMMs reads contiguous bytes
+ *   (row-major weights are read as 64 bytes of each of 16 rows 4 KiB or more
+ *   apart, which streams about 15 % slower on MI355X).
+ *   w     [n_experts] x [N][row_bytes] bytes: byte (e, n, c) at e*w_stride_e + n*w_stride_n + c
+ *         (block-FP8: row_bytes = K; MXFP4: row_bytes = K/2 nibble pairs).
+ *   step_bytes: bytes of one 128-wide K block of a row: 128 (block-FP8) or 64 (MXFP4).
+ *   out   packed bank, expert e at e*out_stride_e.  Within an expert, for each 16-row
+ *         group g = n/16 and K step s = c/step_bytes, a block of 16*step_bytes bytes at
+ *         (g*(row_bytes/step_bytes) + s)*16*step_bytes holds 16-byte pieces p = 0 ..
+ *         step_bytes-1: piece p is row 16g + (p%16), bytes s*step_bytes + 64*(p/64) +
+ *         16*((p%64)/16) .. +15.  The scale arrays keep their own layout.
+ *   The grouped-mode GEMMs read such a bank when given w_stride_n = MOE_W_PACKED
+ *   and the bank's expert stride; their results are those of the row-major bank,
+ *   bit for bit.  Slot mode and the fused decode take row-major banks only.
+ *   Requirements: N % 16 == 0, step_bytes 64 or 128, row_bytes % step_bytes == 0,
+ *   w_stride_n >= row_bytes, w_stride_e >= N*w_stride_n and out_stride_e >=
+ *   N*row_bytes when n_experts > 1 (MOE_ERR_SHAPE); w, out and every stride
+ *   16-byte aligned (MOE_ERR_ALIGN).  w and out must not overlap.
+ */
+int moe_pack_weights(const uint8_t* w, int64_t w_stride_e, int64_t w_stride_n, int64_t n_experts, int64_t N,
+                     int64_t row_bytes, int64_t step_bytes, uint8_t* out, int64_t out_stride_e, void* stream);
 
 /*
  * moe_topk_reduce  -- routing-weighted sum over each token's top-k routes
