@@ -25,13 +25,14 @@ MOE_ERR_SCRATCH = -7
 MOE_BF16, MOE_F32, MOE_F16 = 0, 1, 2
 MOE_ACT_IDENTITY, MOE_ACT_SILU_MUL, MOE_ACT_GELU_MUL, MOE_ACT_RELU_MUL, MOE_ACT_SIGMOID_MUL, MOE_ACT_MUL = 0, 1, 2, 3, 4, 5
 MOE_MODE_GROUPED, MOE_MODE_SLOT = 0, 1
+MOE_W_PACKED = -1
 
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_gather_rows_scales", "moe_act_quant",
     "moe_pick_block_m", "moe_bf8_grouped_gemm", "moe_topk_reduce", "moe_fused_decode_workspace_size",
     "moe_fused_decode_workspace_layout", "moe_fused_decode_workspace_init", "moe_fused_decode",
     "moe_route_prep_workspace_size", "moe_route_prep", "moe_bf8_grouped_gemm_act_quant",
-    "moe_mxfp4_grouped_gemm", "moe_mxfp4_grouped_gemm_act_quant", "moe_fused_decode_noalloc",
+    "moe_mxfp4_grouped_gemm", "moe_mxfp4_grouped_gemm_act_quant", "moe_fused_decode_noalloc", "moe_pack_weights",
 )
 
 _lib = None
@@ -79,6 +80,7 @@ def lib():
                                         I32, P, I32, I64, P], I32),
             "moe_mxfp4_grouped_gemm_act_quant": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, P,
                                                   I64, I32, I32, P, I64, P, I64, P], I32),
+            "moe_pack_weights": ([P, I64, I64, I64, I64, I64, I64, P, I64, P], I32),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -142,22 +144,45 @@ def act_quant(x, out_q, out_s, act=MOE_ACT_IDENTITY, n=None, stream=None):
         _rowstride(out_s), _stream(stream)))
 
 
+def pack_weights(w, step_bytes, out=None, stream=None):
+    """The packed order of an expert bank (moe_pack_weights): w [E, N, row_bytes] bytes with unit last stride,
+    step_bytes 128 for block-FP8 codes (row_bytes = K) or 64 for MXFP4 (row_bytes = K/2).  Returns out (a new
+    contiguous [E, N, row_bytes] byte tensor when None), to be passed to the grouped GEMMs with w_packed=True."""
+    E, N, RB = w.shape
+    assert w.dtype == torch.uint8 and w.stride(2) == 1
+    if out is None:
+        out = torch.empty((E, N, RB), dtype=torch.uint8, device=w.device)
+    assert out.dtype == torch.uint8 and tuple(out.shape) == (E, N, RB) and out.stride(2) == 1 and out.stride(1) == RB
+    _check("moe_pack_weights", lib().moe_pack_weights(
+        _ptr(w), w.stride(0), w.stride(1), E, N, RB, step_bytes, _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def _w_strides(w, packed):
+    """(expert stride, row stride) of a weight bank argument: MOE_W_PACKED as the row stride of a packed one."""
+    if packed:
+        assert w.stride(2) == 1 and w.stride(1) == w.shape[2], "a packed bank is contiguous per expert"
+        return w.stride(0), MOE_W_PACKED
+    return w.stride(0), w.stride(1)
+
+
 def bf8_grouped_gemm(a_q, a_s, w_q, w_s, out, *, mode, expert_offsets=None, slot_ids=None, m_rows=None,
-                     a_row_div=1, block_m=0, stream=None):
-    """Block-FP8 GEMM; w_q [E, N, K] (unit K stride), w_s [E, ceil(N/128), K/128]."""
+                     a_row_div=1, block_m=0, w_packed=False, stream=None):
+    """Block-FP8 GEMM; w_q [E, N, K] (unit K stride; the packed order of pack_weights when w_packed),
+    w_s [E, ceil(N/128), K/128]."""
     E, N, K = w_q.shape
     if m_rows is None:
         m_rows = out.shape[0]
     assert w_q.stride(2) == 1 and w_s.stride(2) == 1
     _check("moe_bf8_grouped_gemm", lib().moe_bf8_grouped_gemm(
         _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
-        _ptr(w_q), w_q.stride(0), w_q.stride(1), _ptr(w_s), w_s.stride(0), w_s.stride(1),
+        _ptr(w_q), *_w_strides(w_q, w_packed), _ptr(w_s), w_s.stride(0), w_s.stride(1),
         E, N, K, mode, _ptr(expert_offsets), _ptr(slot_ids), m_rows, a_row_div, block_m,
         _ptr(out), _dt(out), _rowstride(out), _stream(stream)))
 
 
 def bf8_grouped_gemm_act_quant(a_q, a_s, w13_q, w13_s, expert_offsets, out_q, out_s, m_rows=None, block_m=0,
-                               act=1, stream=None):
+                               act=1, w_packed=False, stream=None):
     """Prefill gate/up GEMM with act(gate)*up (moe_act 1..5, default SwiGLU) and the 1x128 fp8 requant in
     its epilogue.
     w13_q [E, 2I, K] (gate rows, then up rows), w13_s [E, 2I/128, K/128]; out_q [rows, I] u8, out_s [rows, I/128]."""
@@ -167,7 +192,7 @@ def bf8_grouped_gemm_act_quant(a_q, a_s, w13_q, w13_s, expert_offsets, out_q, ou
     assert w13_q.stride(2) == 1 and w13_s.stride(2) == 1
     _check("moe_bf8_grouped_gemm_act_quant", lib().moe_bf8_grouped_gemm_act_quant(
         _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
-        _ptr(w13_q), w13_q.stride(0), w13_q.stride(1), _ptr(w13_s), w13_s.stride(0), w13_s.stride(1),
+        _ptr(w13_q), *_w_strides(w13_q, w_packed), _ptr(w13_s), w13_s.stride(0), w13_s.stride(1),
         E, N // 2, K, _ptr(expert_offsets), m_rows, block_m, act, _ptr(out_q), _rowstride(out_q),
         _ptr(out_s), _rowstride(out_s), _stream(stream)))
 
@@ -179,7 +204,8 @@ def _mxfp4_weights(w4, w4_s):
     return E, N, 2 * K2
 
 
-def mxfp4_grouped_gemm(a_q, a_s, w4, w4_s, expert_offsets, out, m_rows=None, block_m=0, stream=None):
+def mxfp4_grouped_gemm(a_q, a_s, w4, w4_s, expert_offsets, out, m_rows=None, block_m=0, w_packed=False,
+                       stream=None):
     """Grouped GEMM with MXFP4 weights: w4 [E, N, K/2] bytes (two E2M1 codes, even k in the low nibble),
     w4_s [E, N, K/32] E8M0 bytes; a_q/a_s/out as bf8_grouped_gemm in grouped mode."""
     E, N, K = _mxfp4_weights(w4, w4_s)
@@ -187,19 +213,19 @@ def mxfp4_grouped_gemm(a_q, a_s, w4, w4_s, expert_offsets, out, m_rows=None, blo
         m_rows = out.shape[0]
     _check("moe_mxfp4_grouped_gemm", lib().moe_mxfp4_grouped_gemm(
         _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
-        _ptr(w4), w4.stride(0), w4.stride(1), _ptr(w4_s), w4_s.stride(0), w4_s.stride(1),
+        _ptr(w4), *_w_strides(w4, w_packed), _ptr(w4_s), w4_s.stride(0), w4_s.stride(1),
         E, N, K, _ptr(expert_offsets), m_rows, block_m, _ptr(out), _dt(out), _rowstride(out), _stream(stream)))
 
 
 def mxfp4_grouped_gemm_act_quant(a_q, a_s, w4, w4_s, expert_offsets, out_q, out_s, m_rows=None, block_m=0,
-                                 act=1, stream=None):
+                                 act=1, w_packed=False, stream=None):
     """bf8_grouped_gemm_act_quant with MXFP4 gate/up weights w4 [E, 2I, K/2], w4_s [E, 2I, K/32]."""
     E, N, K = _mxfp4_weights(w4, w4_s)
     if m_rows is None:
         m_rows = out_q.shape[0]
     _check("moe_mxfp4_grouped_gemm_act_quant", lib().moe_mxfp4_grouped_gemm_act_quant(
         _ptr(a_q), _rowstride(a_q), _ptr(a_s), _rowstride(a_s),
-        _ptr(w4), w4.stride(0), w4.stride(1), _ptr(w4_s), w4_s.stride(0), w4_s.stride(1),
+        _ptr(w4), *_w_strides(w4, w_packed), _ptr(w4_s), w4_s.stride(0), w4_s.stride(1),
         E, N // 2, K, _ptr(expert_offsets), m_rows, block_m, act, _ptr(out_q), _rowstride(out_q),
         _ptr(out_s), _rowstride(out_s), _stream(stream)))
 

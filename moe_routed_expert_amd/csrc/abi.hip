@@ -75,6 +75,20 @@ DecodeLayout decode_layout(int64_t T, int64_t H, int64_t I, int64_t topk) {
     return L;
 }
 
+// The weight bank of a grouped-mode GEMM: row-major with row stride w_stride_n >= row_bytes, or packed
+// (w_stride_n == MOE_W_PACKED, moe_pack_weights) with expert stride >= N * row_bytes.
+int weight_bank_ok(const uint8_t* w, int64_t w_stride_e, int64_t w_stride_n, int64_t n_experts, int64_t N,
+                   int64_t row_bytes) {
+    if (w_stride_n == MOE_W_PACKED) {
+        if (n_experts > 1 && w_stride_e < N * row_bytes) return MOE_ERR_SHAPE;
+        if (!aligned16(w) || w_stride_e % 16) return MOE_ERR_ALIGN;
+        return MOE_OK;
+    }
+    if (w_stride_n < row_bytes || (n_experts > 1 && w_stride_e < N * w_stride_n)) return MOE_ERR_SHAPE;
+    if (!aligned16(w) || w_stride_n % 16 || w_stride_e % 16) return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
 bool decode_shape_ok(int64_t T, int64_t H, int64_t I, int64_t topk) {
     return T >= 0 && H > 0 && I > 0 && topk >= 1 && topk <= 64 && H % 128 == 0 && I % 128 == 0 &&
            T * topk <= 65535;
@@ -144,10 +158,12 @@ extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const 
     const bool empty_bank = n_experts == 0;
     if (!empty_bank) {
         if (!w_q || !w_s || !a_q || !a_s) return MOE_ERR_NULL;
-        if (w_stride_n < K || a_stride < K || a_s_stride < kb || w_s_stride_n < kb) return MOE_ERR_SHAPE;
-        if (n_experts > 1 && (w_stride_e < N * w_stride_n || w_s_stride_e < nb * w_s_stride_n)) return MOE_ERR_SHAPE;
-        if (!aligned16(w_q) || !aligned16(a_q) || w_stride_n % 16 || w_stride_e % 16 || a_stride % 16)
-            return MOE_ERR_ALIGN;
+        if (a_stride < K || a_s_stride < kb || w_s_stride_n < kb) return MOE_ERR_SHAPE;
+        if (n_experts > 1 && w_s_stride_e < nb * w_s_stride_n) return MOE_ERR_SHAPE;
+        if (mode == MOE_MODE_SLOT && w_stride_n == MOE_W_PACKED) return MOE_ERR_SHAPE;
+        const int rc = weight_bank_ok(w_q, w_stride_e, w_stride_n, n_experts, N, K);
+        if (rc != MOE_OK) return rc;
+        if (!aligned16(a_q) || a_stride % 16) return MOE_ERR_ALIGN;
     }
     auto st = as_stream(stream);
     if (mode == MOE_MODE_SLOT) {
@@ -181,10 +197,12 @@ extern "C" int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stri
     if (m_rows == 0) return MOE_OK;
     if (!a_q || !a_s || !w_q || !w_s || !expert_offsets || !out_q || !out_s) return MOE_ERR_NULL;
     const int64_t kb = K / 128, nb = 2 * I / 128;
-    if (a_stride < K || a_s_stride < kb || w_stride_n < K || w_s_stride_n < kb || q_stride < I || s_stride < I / 128)
+    if (a_stride < K || a_s_stride < kb || w_s_stride_n < kb || q_stride < I || s_stride < I / 128)
         return MOE_ERR_SHAPE;
-    if (n_experts > 1 && (w_stride_e < 2 * I * w_stride_n || w_s_stride_e < nb * w_s_stride_n)) return MOE_ERR_SHAPE;
-    if (!aligned16(w_q) || !aligned16(a_q) || w_stride_n % 16 || w_stride_e % 16 || a_stride % 16) return MOE_ERR_ALIGN;
+    if (n_experts > 1 && w_s_stride_e < nb * w_s_stride_n) return MOE_ERR_SHAPE;
+    const int rc = weight_bank_ok(w_q, w_stride_e, w_stride_n, n_experts, 2 * I, K);
+    if (rc != MOE_OK) return rc;
+    if (!aligned16(a_q) || a_stride % 16) return MOE_ERR_ALIGN;
     const int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
     return grouped_gemm_act_quant_launch(as_stream(stream), bm, act, a_q, a_stride, a_s, a_s_stride, w_q,
                                          w_stride_e, w_stride_n, w_s, w_s_stride_e, w_s_stride_n, n_experts, I, K,
@@ -199,10 +217,11 @@ int mxfp4_args_ok(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_
                   int64_t w4s_stride_e, int64_t w4s_stride_n, int64_t n_experts, int64_t N, int64_t K,
                   const int32_t* expert_offsets) {
     if (!a_q || !a_s || !w4 || !w4s || !expert_offsets) return MOE_ERR_NULL;
-    if (a_stride < K || a_s_stride < K / 128 || w4_stride_n < K / 2 || w4s_stride_n < K / 32) return MOE_ERR_SHAPE;
-    if (n_experts > 1 && (w4_stride_e < N * w4_stride_n || w4s_stride_e < N * w4s_stride_n)) return MOE_ERR_SHAPE;
-    if (!aligned16(a_q) || a_stride % 16 || !aligned16(w4) || w4_stride_n % 16 || w4_stride_e % 16)
-        return MOE_ERR_ALIGN;
+    if (a_stride < K || a_s_stride < K / 128 || w4s_stride_n < K / 32) return MOE_ERR_SHAPE;
+    if (n_experts > 1 && w4s_stride_e < N * w4s_stride_n) return MOE_ERR_SHAPE;
+    const int rc = weight_bank_ok(w4, w4_stride_e, w4_stride_n, n_experts, N, K / 2);
+    if (rc != MOE_OK) return rc;
+    if (!aligned16(a_q) || a_stride % 16) return MOE_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(w4s) % 4 || w4s_stride_n % 4 || w4s_stride_e % 4) return MOE_ERR_ALIGN;
     return MOE_OK;
 }

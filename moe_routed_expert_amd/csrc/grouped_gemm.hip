@@ -107,7 +107,31 @@ struct GgArgs {
     // MXFP4 weights (W4 variant): w_q holds [e][n][K/2] bytes (strides in bytes), w4s [e][n][K/32] E8M0
     const uint8_t* w4s;
     int64_t w4s_stride_e, w4s_stride_n;
+    // weight addressing (set by set_weight_layout): row-major [e][n][k] with row stride w_stride_n, or
+    // packed (moe_pack_weights: per expert, per 16-row group, per K step, one block in operand order)
+    bool w_packed;
+    int64_t w_group;                          // bytes from one 16-row group to the next
+    int64_t w_kstep;                          // bytes from one K step to the next within a group
+    int64_t w_khalf;                          // block-FP8: bytes from a lane's first 16-byte piece to its second
 };
+
+// Fills the weight addressing of g for w_stride_n (MOE_W_PACKED: the packed order) and row_bytes = K
+// (block-FP8) or K/2 (MXFP4).  A K step is 128 bytes of a row (block-FP8) or 64 (MXFP4).
+inline void set_weight_layout(GgArgs& g, bool w4) {
+    const int64_t row_bytes = w4 ? g.K / 2 : g.K, step = w4 ? 64 : 128;
+    g.w_packed = g.w_stride_n == MOE_W_PACKED;
+    g.w_group = g.w_packed ? 16 * row_bytes : 16 * g.w_stride_n;
+    g.w_kstep = g.w_packed ? 16 * step : step;
+    g.w_khalf = g.w_packed ? 1024 : 64;
+}
+
+// Byte offset, from w_q, of this lane's first weight piece of the 16-row group that starts at row r16
+// (a multiple of 16) of expert e.  Row-major: row r16 + lane%16, bytes 16*(lane/16) of each K step (and
+// 64 more for the second piece).  Packed: the pieces of a step are stored in lane order.
+__device__ __forceinline__ int64_t w_lane_offset(const GgArgs& g, int expert, int64_t r16, int lane) {
+    return (int64_t)expert * g.w_stride_e + (r16 / 16) * g.w_group +
+           (g.w_packed ? 16 * (int64_t)lane : (lane & 15) * g.w_stride_n + (lane / 16) * 16);
+}
 
 // Exclusive scan of one int per thread over a block of WAVES waves.
 template <int WAVES>
@@ -183,8 +207,8 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     const float* __restrict__ a_s = g.a_s;
     const uint8_t* __restrict__ w_q = g.w_q;
     const float* __restrict__ w_s = g.w_s;
-    const int64_t a_stride = g.a_stride, a_s_stride = g.a_s_stride, w_stride_e = g.w_stride_e;
-    const int64_t w_stride_n = g.w_stride_n, w_s_stride_e = g.w_s_stride_e, w_s_stride_n = g.w_s_stride_n;
+    const int64_t a_stride = g.a_stride, a_s_stride = g.a_s_stride;
+    const int64_t w_s_stride_e = g.w_s_stride_e, w_s_stride_n = g.w_s_stride_n;
     const int64_t N = g.N, K = g.K;
     using C = GgCfg<BM>;
     constexpr int TPW = C::TPW;
@@ -219,8 +243,9 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     // [0, 16), sub-tile 1 the matching up rows I + ..., with scale blocks n_tile and I/128 + n_tile.
     const int64_t I = N / 2;
     const int64_t wcol = FUSED ? (int64_t)n_tile * 128 + 16 * wv : (cols ? n0 + wv * CPW : n0);
-    const uint8_t* wp0 = w_q + (int64_t)expert * w_stride_e + (wcol + (lane & 15)) * w_stride_n + q16;
-    const uint8_t* wp1 = wp0 + (FUSED ? I : 16) * w_stride_n;
+    const uint8_t* wp0 = w_q + w_lane_offset(g, expert, wcol, lane);
+    const uint8_t* wp1 = wp0 + (FUSED ? I / 16 : 1) * g.w_group;
+    const int64_t kstep = g.w_kstep, khalf = g.w_khalf;
     // MXFP4 scales.  A chunk is 128 blocks (32 K steps) of the wave's 32 rows: lanes 0-31 read one row's
     // 128 bytes as 32 dwords and lanes 32-63 the next row, 16 loads per lane, all requested before the
     // first LDS store.  In a step the lane's K block is 4 kb + lane/16; it reads the row's dword of the
@@ -310,18 +335,17 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     };
     v4i w_ring[S][2 * TPW];
     auto load_w = [&](int kb, v4i* w) {
+        const int64_t o = (int64_t)kb * kstep;
         if constexpr (W4) {
-            const int64_t o = (int64_t)kb * 64;
             w[0] = *reinterpret_cast<const v4i*>(wp0 + o);
             w[1] = *reinterpret_cast<const v4i*>(wp1 + o);
             return;
         }
-        const int64_t o = (int64_t)kb * 128;
         w[0] = *reinterpret_cast<const v4i*>(wp0 + o);
-        w[1] = *reinterpret_cast<const v4i*>(wp0 + o + 64);
+        w[1] = *reinterpret_cast<const v4i*>(wp0 + o + khalf);
         if constexpr (TPW == 2) {
             w[2] = *reinterpret_cast<const v4i*>(wp1 + o);
-            w[3] = *reinterpret_cast<const v4i*>(wp1 + o + 64);
+            w[3] = *reinterpret_cast<const v4i*>(wp1 + o + khalf);
         }
     };
 
@@ -535,8 +559,8 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
     auto addr_of = [&](const TileId& ti) {
         Addr ad;
         const int64_t wcol = wcol_of(ti);
-        ad.wp0 = w_q + (int64_t)ti.expert * g.w_stride_e + (wcol + (lane & 15)) * g.w_stride_n + q16;
-        ad.wp1 = ad.wp0 + (FUSED ? I : 16) * g.w_stride_n;
+        ad.wp0 = w_q + w_lane_offset(g, ti.expert, wcol, lane);
+        ad.wp1 = ad.wp0 + (FUSED ? I / 16 : 1) * g.w_group;
 #pragma unroll
         for (int j = 0; j < A_PER_THREAD; j++) {
             const int c0 = tid + j * NT;
@@ -630,19 +654,19 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
             if (A_CHUNKS % NT == 0 || tid + j * NT < A_CHUNKS)
                 *reinterpret_cast<v4i*>(&a_lds[buf][a_dst[j]]) = a_reg[stage][j];
     };
+    const int64_t kstep = g.w_kstep, khalf = g.w_khalf;
     auto load_w = [&](const Addr& ad, int kb, v4i* w) {
+        const int64_t o = (int64_t)kb * kstep;
         if constexpr (W4) {
-            const int64_t o = (int64_t)kb * 64;
             w[0] = *reinterpret_cast<const v4i*>(ad.wp0 + o);
             w[1] = *reinterpret_cast<const v4i*>(ad.wp1 + o);
             return;
         }
-        const int64_t o = (int64_t)kb * 128;
         w[0] = *reinterpret_cast<const v4i*>(ad.wp0 + o);
-        w[1] = *reinterpret_cast<const v4i*>(ad.wp0 + o + 64);
+        w[1] = *reinterpret_cast<const v4i*>(ad.wp0 + o + khalf);
         if constexpr (TPW == 2) {
             w[2] = *reinterpret_cast<const v4i*>(ad.wp1 + o);
-            w[3] = *reinterpret_cast<const v4i*>(ad.wp1 + o + 64);
+            w[3] = *reinterpret_cast<const v4i*>(ad.wp1 + o + khalf);
         }
     };
 
@@ -951,6 +975,7 @@ int grouped_gemm_launch(hipStream_t st, int block_m, const uint8_t* a_q, int64_t
     g.w_s = w_s; g.w_s_stride_e = w_s_stride_e; g.w_s_stride_n = w_s_stride_n;
     g.n_experts = (int)E; g.N = N; g.K = K; g.offsets = offsets; g.m_rows = (int)m_rows;
     g.out = out; g.out_stride = out_stride;
+    set_weight_layout(g, false);
     return grouped_launch_bm(st, block_m, out_dt, false, g);
 }
 
@@ -969,6 +994,7 @@ int mxfp4_grouped_gemm_launch(hipStream_t st, int block_m, int act, const uint8_
     g.n_experts = (int)E; g.N = N; g.K = K; g.offsets = offsets; g.m_rows = (int)m_rows;
     g.out = out; g.out_stride = out_stride;
     g.q = q; g.q_stride = q_stride; g.s = s; g.s_stride = s_stride; g.act = act;
+    set_weight_layout(g, true);
     return grouped_launch_bm(st, block_m, out_dt, act > 0, g);
 }
 
@@ -983,6 +1009,7 @@ int grouped_gemm_act_quant_launch(hipStream_t st, int block_m, int act, const ui
     g.w_s = w_s; g.w_s_stride_e = w_s_stride_e; g.w_s_stride_n = w_s_stride_n;
     g.n_experts = (int)E; g.N = 2 * I; g.K = K; g.offsets = offsets; g.m_rows = (int)m_rows;
     g.q = q; g.q_stride = q_stride; g.s = s; g.s_stride = s_stride; g.act = act;
+    set_weight_layout(g, false);
     return grouped_launch_bm(st, block_m, MOE_F32, true, g);
 }
 

@@ -283,3 +283,44 @@ def test_fused_decode_noalloc_checks():
     assert f(*args(1, 2048, 768, 65)) == m.MOE_ERR_SHAPE       # topk > 64
     assert f(*args(1, 2048, 768, 8, act=0)) == m.MOE_ERR_SHAPE # not a gated activation
     assert f(*args(0, 2048, 768, 8)) == m.MOE_OK               # no tokens: nothing launched
+
+
+def test_pack_weights_and_packed_bank_checks():
+    """moe_pack_weights validates before any launch; the grouped GEMMs take MOE_W_PACKED as a row stride
+    in grouped mode only, with a packed bank's expert stride (N * row_bytes)."""
+    L = m.lib()
+
+    def pack(**kw):
+        a = dict(w=FAKE, w_stride_e=256 * 256, w_stride_n=256, n_experts=4, N=256, row_bytes=256, step_bytes=128,
+                 out=P(0x10000000), out_stride_e=256 * 256, stream=None)
+        a.update(kw)
+        return L.moe_pack_weights(*a.values())
+
+    assert pack(step_bytes=96) == m.MOE_ERR_SHAPE
+    assert pack(N=24) == m.MOE_ERR_SHAPE                      # 16-row groups
+    assert pack(row_bytes=192) == m.MOE_ERR_SHAPE             # whole K steps
+    assert pack(n_experts=-1) == m.MOE_ERR_SHAPE
+    assert pack(n_experts=0, w=None, out=None) == m.MOE_OK   # nothing to copy, no launch
+    assert pack(w=None) == m.MOE_ERR_NULL
+    assert pack(out=None) == m.MOE_ERR_NULL
+    assert pack(w_stride_n=128) == m.MOE_ERR_SHAPE            # row stride < row bytes
+    assert pack(w_stride_e=128 * 256) == m.MOE_ERR_SHAPE      # source experts overlap
+    assert pack(out_stride_e=128 * 256) == m.MOE_ERR_SHAPE    # packed experts overlap
+    assert pack(w=P(0x1008)) == m.MOE_ERR_ALIGN
+    assert pack(out=P(0x10000008)) == m.MOE_ERR_ALIGN
+    assert pack(w_stride_n=264, w_stride_e=264 * 256) == m.MOE_ERR_ALIGN
+    assert pack(out=P(0x1000 + 4096)) == m.MOE_ERR_SHAPE      # the two ranges meet
+    # packed banks in the GEMMs
+    assert gemm(mode=1, w_stride_n=m.MOE_W_PACKED) == m.MOE_ERR_SHAPE    # slot mode: row-major only
+    assert gemm(mode=0, w_stride_n=m.MOE_W_PACKED, w_stride_e=255 * 256) == m.MOE_ERR_SHAPE   # < N*K
+    assert gemm(mode=0, w_stride_n=m.MOE_W_PACKED, w_stride_e=256 * 256 + 8) == m.MOE_ERR_ALIGN
+    assert gemm(mode=0, w_stride_n=-2) == m.MOE_ERR_SHAPE    # other negative strides stay invalid
+    fused = dict(a_q=FAKE, a_stride=256, a_s=FAKE, a_s_stride=2, w_q=FAKE, w_stride_e=256 * 256,
+                 w_stride_n=m.MOE_W_PACKED, w_s=FAKE, w_s_stride_e=4, w_s_stride_n=2, n_experts=4, I=128, K=256,
+                 offsets=FAKE, m_rows=8, block_m=0, act=1, q=FAKE, q_stride=128, s=FAKE, s_stride=1, stream=None)
+    a = dict(fused, w_stride_e=200 * 256)
+    assert L.moe_bf8_grouped_gemm_act_quant(*a.values()) == m.MOE_ERR_SHAPE
+    mx = dict(a_q=FAKE, a_stride=256, a_s=FAKE, a_s_stride=2, w4=FAKE, w4_stride_e=255 * 128,
+              w4_stride_n=m.MOE_W_PACKED, w4s=FAKE, w4s_stride_e=256 * 8, w4s_stride_n=8, n_experts=4, N=256, K=256,
+              offsets=FAKE, m_rows=8, block_m=0, out=FAKE, out_dt=m.MOE_BF16, out_stride=256, stream=None)
+    assert L.moe_mxfp4_grouped_gemm(*mx.values()) == m.MOE_ERR_SHAPE    # < N*K/2
