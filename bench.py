@@ -19,7 +19,8 @@ Also reported: 4/2/0 active routes and H=4096, I=1024 (time vs active
 routes), the fused gather (k=7168 with 8, 64, 512 and 8192 rows; k=896 with
 512 rows) timed the same way, the grouped prefill GEMMs at 1536, 6144 and
 24576 routes (E=256, top-6, H=4096, I=1024) in TFLOP/s against the fp8 dense
-peak and against the HBM roofline, the
+peak and against the HBM roofline, from row-major banks and from the same banks
+in the GEMMs' packed order (moe_pack_weights, a one-time copy), the
 roofline of the dominant kernel (the single fused decode kernel), and the
 CPU oracle timed on a bounded sample of the headline workload.
 
@@ -320,7 +321,15 @@ def prefill_weights(torch, wl, E, H, I):
     return w13, w2
 
 
-def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
+def packed_banks(m, weights, step):
+    """The same banks in the GEMMs' packed order (moe_pack_weights), scales shared."""
+    (w13, w13_s), (w2, w2_s) = weights
+    return (m.pack_weights(w13, step), w13_s), (m.pack_weights(w2, step), w2_s)
+
+
+def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
+    """The block-FP8 gate/up and down GEMMs and the fused gate/up requant; `packed`: banks in the packed
+    order (moe_pack_weights)."""
     dev = torch.device("cuda")
     rt = wl.prefill_routes(T, E, topk, seed=9)
     R = T * topk
@@ -337,11 +346,11 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
             "gate_up": (a1_q, a1_s, w13_q, w13_s, c1, 2 * I, H),
             "down": (a2_q, a2_s, w2_q, w2_s, c2, H, I)}.items():
         for _ in range(3):
-            m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c, mode=m.MOE_MODE_GROUPED, expert_offsets=offs)
+            m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c, mode=m.MOE_MODE_GROUPED, expert_offsets=offs, w_packed=packed)
         t = Timer(torch)
         for _ in range(steps):          # 2-3 GB of weights per call: cold by construction
             t.start()
-            m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c, mode=m.MOE_MODE_GROUPED, expert_offsets=offs)
+            m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c, mode=m.MOE_MODE_GROUPED, expert_offsets=offs, w_packed=packed)
             t.stop()
         us = statistics.median(t.us())
         flops = 2.0 * R * N * K
@@ -357,11 +366,11 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     aq = torch.empty((R, I), dtype=torch.uint8, device=dev)
     as_ = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
     for _ in range(3):
-        m.bf8_grouped_gemm_act_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_)
+        m.bf8_grouped_gemm_act_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_, w_packed=packed)
     t = Timer(torch)
     for _ in range(steps):
         t.start()
-        m.bf8_grouped_gemm_act_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_)
+        m.bf8_grouped_gemm_act_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_, w_packed=packed)
         t.stop()
     us_f = statistics.median(t.us())
     t = Timer(torch)
@@ -376,7 +385,7 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
 
 
-def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
+def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
     """The grouped GEMMs with MXFP4 expert weights (E2M1 codes, an E8M0 scale per 32 K) on the same routes:
     gate/up with the SiLU-mul requant fused, gate/up to bf16, and down to bf16."""
     dev = torch.device("cuda")
@@ -392,10 +401,12 @@ def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
     as_ = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
     touched = int((rt.expert_offsets[1:] > rt.expert_offsets[:-1]).sum())
     calls = {
-        "gate_up_act_quant": (lambda: m.mxfp4_grouped_gemm_act_quant(a1_q, a1_s, w13, w13_s, offs, aq, as_),
+        "gate_up_act_quant": (lambda: m.mxfp4_grouped_gemm_act_quant(a1_q, a1_s, w13, w13_s, offs, aq, as_,
+                                                                     w_packed=packed),
                               2 * I, H, R * (I + 4 * I // 128)),
-        "gate_up": (lambda: m.mxfp4_grouped_gemm(a1_q, a1_s, w13, w13_s, offs, c1), 2 * I, H, R * 2 * I * 2),
-        "down": (lambda: m.mxfp4_grouped_gemm(a2_q, a2_s, w2, w2_s, offs, c2), H, I, R * H * 2),
+        "gate_up": (lambda: m.mxfp4_grouped_gemm(a1_q, a1_s, w13, w13_s, offs, c1, w_packed=packed), 2 * I, H,
+                    R * 2 * I * 2),
+        "down": (lambda: m.mxfp4_grouped_gemm(a2_q, a2_s, w2, w2_s, offs, c2, w_packed=packed), H, I, R * H * 2),
     }
     out = {}
     for name, (fn, N, K, out_bytes) in calls.items():
@@ -419,7 +430,7 @@ def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
                 weights="MXFP4 (E2M1 + E8M0 per 32 K)", **out)
 
 
-def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
+def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
     """One whole prefill layer on the device from router logits: routing prep, input quant, gather,
     fused gate/up + SiLU-mul requant, down GEMM, top-k reduce (timed per layer with events)."""
     dev = torch.device("cuda")
@@ -451,9 +462,10 @@ def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights):
         assert rc == 0, rc
         m.act_quant(x, xq, xs)
         m.gather_rows_scales(xq, xs, d2s, gq, gs)
-        m.bf8_grouped_gemm_act_quant(gq, gs, w13_q, w13_s, offs, aq, as_, block_m=m.pick_block_m(R, E))
+        m.bf8_grouped_gemm_act_quant(gq, gs, w13_q, w13_s, offs, aq, as_, block_m=m.pick_block_m(R, E),
+                                     w_packed=packed)
         m.bf8_grouped_gemm(aq, as_, w2_q, w2_s, c2, mode=m.MOE_MODE_GROUPED, expert_offsets=offs,
-                           block_m=m.pick_block_m(R, E))
+                           block_m=m.pick_block_m(R, E), w_packed=packed)
         m.topk_reduce(c2, ids, w, out, route_rows=rr)
 
     for _ in range(2):
@@ -473,20 +485,27 @@ def prefill_all(torch, m, wl):
     """The grouped GEMMs at 1536, 6144 and 24576 routes (E=256, top-6, H=4096, I=1024), with block-FP8 and
     with MXFP4 expert weights."""
     weights = prefill_weights(torch, wl, 256, 4096, 1024)
+    packed = packed_banks(m, weights, 128)
     res = []
     for T in (256, 1024, 4096):
         log("prefill %d routes" % (T * 6))
         res.append(prefill_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights))
         res[-1]["layer"] = prefill_layer_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights)
-    del weights
+        res[-1]["packed"] = prefill_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, packed, packed=True)
+        res[-1]["packed"]["layer"] = prefill_layer_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, packed,
+                                                         packed=True)
+    del weights, packed
     torch.cuda.empty_cache()
     dev = torch.device("cuda")
     weights = (wl.mxfp4_weights(256, 2048, 4096, seed=31, device=dev), wl.mxfp4_weights(256, 4096, 1024, seed=32,
                                                                                         device=dev))
+    packed = packed_banks(m, weights, 64)
     for i, T in enumerate((256, 1024, 4096)):
         log("prefill mxfp4 %d routes" % (T * 6))
         res[i]["mxfp4"] = prefill_mxfp4_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, weights)
-    del weights
+        res[i]["mxfp4"]["packed"] = prefill_mxfp4_bench(torch, m, wl, T, 256, 6, 4096, 1024, 10, packed,
+                                                        packed=True)
+    del weights, packed
     torch.cuda.empty_cache()
     return res
 
