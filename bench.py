@@ -340,7 +340,7 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
     c1 = torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev)
     c2 = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
     touched = int((rt.expert_offsets[1:] > rt.expert_offsets[:-1]).sum())
-    bm = m.pick_block_m(R, E)
+    bm = m.grouped_block_m(R, E, H, packed=packed)
     out = {}
     for name, (a_q, a_s, w_q, w_s, c, N, K) in {
             "gate_up": (a1_q, a1_s, w13_q, w13_s, c1, 2 * I, H),
@@ -382,7 +382,9 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
     flops = 2.0 * R * 2 * I * H
     out["gate_up_act_quant"] = dict(us_median=us_f, tflops=flops / (us_f * 1e-6) / 1e12,
                                      unfused_us=out["gate_up"]["us_median"] + us_a, act_quant_us=us_a)
-    return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm, **out)
+    return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm,
+                block_m_fused=m.grouped_block_m(R, E, H, packed=packed, fused=True),
+                block_m_down=m.grouped_block_m(R, E, I, packed=packed), **out)
 
 
 def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
@@ -426,7 +428,10 @@ def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=F
         out[name] = dict(us_median=us, tflops=tflops, fp8_peak_frac=tflops / FP8_PEAK_TFLOPS,
                          roofline_frac=tflops / attainable, arithmetic_intensity=ai, bytes=nbytes,
                          hbm_gbs=nbytes / (us * 1e-6) / 1e9)
-    return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=m.pick_block_m(R, E),
+    return dict(routes=R, experts=E, topk=topk, H=H, I=I,
+                block_m=m.grouped_block_m(R, E, H, mxfp4=True, packed=packed),
+                block_m_fused=m.grouped_block_m(R, E, H, mxfp4=True, packed=packed, fused=True),
+                block_m_down=m.grouped_block_m(R, E, I, mxfp4=True, packed=packed),
                 weights="MXFP4 (E2M1 + E8M0 per 32 K)", **out)
 
 
@@ -462,10 +467,8 @@ def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=F
         assert rc == 0, rc
         m.act_quant(x, xq, xs)
         m.gather_rows_scales(xq, xs, d2s, gq, gs)
-        m.bf8_grouped_gemm_act_quant(gq, gs, w13_q, w13_s, offs, aq, as_, block_m=m.pick_block_m(R, E),
-                                     w_packed=packed)
-        m.bf8_grouped_gemm(aq, as_, w2_q, w2_s, c2, mode=m.MOE_MODE_GROUPED, expert_offsets=offs,
-                           block_m=m.pick_block_m(R, E), w_packed=packed)
+        m.bf8_grouped_gemm_act_quant(gq, gs, w13_q, w13_s, offs, aq, as_, w_packed=packed)
+        m.bf8_grouped_gemm(aq, as_, w2_q, w2_s, c2, mode=m.MOE_MODE_GROUPED, expert_offsets=offs, w_packed=packed)
         m.topk_reduce(c2, ids, w, out, route_rows=rr)
 
     for _ in range(2):
@@ -729,59 +732,115 @@ def cpu_baseline(wl, decode_s=8.0, single_s=2.0):
                                     seconds=p_dt, tflops=p_flops / p_dt / 1e12))
 
 
-def bm_sweep(torch, m, wl, steps=10):
-    """Every M tile at the three prefill densities (E = 256, top-6, H = 4096, I = 1024), gate/up and down
-    (bf16 out).  As on the page, each configuration's output is checked before its time counts: every tile
-    must give the picker's output bit for bit (a tile size changes which rows share a workgroup, not the
-    order of any output's sums), and the picker's output must match the oracle on the rows of the first
-    and the last expert."""
+def bm_sweep(torch, m, wl, rounds=6):
+    """Every M tile at six route densities (48 to 24576 routes over E = 256, top-6, H = 4096, I = 1024): the
+    block-FP8 and MXFP4 gate/up (bf16 out), fused gate/up requant and down (bf16 out) GEMMs, each from a
+    row-major and from a packed bank.  As on the page, each configuration's output is checked before its
+    time counts: every tile and both layouts must give the output of the 16-row tile on the row-major bank
+    bit for bit (a tile size or a layout changes which rows share a workgroup or where a weight byte sits,
+    not the order of any output's sums), and for the plain GEMMs that output must match the oracle on the
+    rows of the first and the last expert that has rows.  Times: the tiles take turns call by call with a
+    sync between calls, `rounds` rounds, the first dropped; the median of the rest."""
     import numpy as np
     import oracle
     dev = torch.device("cuda")
-    (w13_q, w13_s), (w2_q, w2_s) = prefill_weights(torch, wl, 256, 4096, 1024)
     H, I, E = 4096, 1024, 256
+    banks = {}
     res = []
-    for T in (256, 1024, 4096):
-        R = T * 6
-        rt = wl.prefill_routes(T, E, 6, seed=9)
-        offs = torch.from_numpy(rt.expert_offsets).to(dev)
-        a1_q, a1_s = wl.fp8_rows(R, H, seed=23, device=dev)
-        a2_q, a2_s = wl.fp8_rows(R, I, seed=24, device=dev)
-        pick = m.pick_block_m(R, E)
-        row = dict(routes=R, rows_per_expert=R / E, picked=pick, gemms={})
-        for name, a_q, a_s, w_q, w_s, N, K in (("gate_up", a1_q, a1_s, w13_q, w13_s, 2 * I, H),
-                                                ("down", a2_q, a2_s, w2_q, w2_s, H, I)):
-            base = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
-            m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, base, mode=m.MOE_MODE_GROUPED, expert_offsets=offs, block_m=pick)
-            torch.cuda.synchronize()
-            for e in (0, E - 1):
-                r0, r1 = int(rt.expert_offsets[e]), int(rt.expert_offsets[e + 1])
-                ref = oracle.block_gemm(a_q[r0:r1].cpu().numpy(), a_s[r0:r1].cpu().numpy(), w_q[e:e + 1].cpu().numpy(),
-                                        w_s[e:e + 1].cpu().numpy(), mode=oracle.MODE_GROUPED,
-                                        expert_offsets=np.array([0, r1 - r0], np.int32), out_dtype=np.uint16)
-                got = oracle.bf16_decode(base[r0:r1].view(torch.int16).cpu().numpy().view(np.uint16)).astype(float)
-                r = oracle.bf16_decode(ref).astype(float)
-                rel = np.linalg.norm(got - r) / np.linalg.norm(r)
-                if not (rel <= 5e-3 and np.abs(got - r).max() <= 2e-2 * np.abs(r).max()):
-                    raise RuntimeError("bm sweep: %s at %d routes, expert %d: rel L2 %.3e" % (name, R, e, rel))
-            times = {}
-            for bm in (16, 32, 64, 128):
-                out = torch.empty((R, N), dtype=torch.bfloat16, device=dev)
-                m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, out, mode=m.MOE_MODE_GROUPED, expert_offsets=offs, block_m=bm)
+    for fmt in ("fp8", "mxfp4"):
+        if fmt == "fp8":
+            (w13, w13_s), (w2, w2_s) = prefill_weights(torch, wl, E, H, I)
+            step = 128
+        else:
+            (w13, w13_s), (w2, w2_s) = (wl.mxfp4_weights(E, 2 * I, H, seed=31, device=dev),
+                                        wl.mxfp4_weights(E, H, I, seed=32, device=dev))
+            step = 64
+        p13, p2 = m.pack_weights(w13, step), m.pack_weights(w2, step)
+        for T in (8, 32, 128, 256, 1024, 4096):
+            R = T * 6
+            rt = wl.prefill_routes(T, E, 6, seed=9)
+            offs = torch.from_numpy(rt.expert_offsets).to(dev)
+            a1_q, a1_s = wl.fp8_rows(R, H, seed=23, device=dev)
+            a2_q, a2_s = wl.fp8_rows(R, I, seed=24, device=dev)
+            nonempty = [e for e in range(E) if rt.expert_offsets[e + 1] > rt.expert_offsets[e]]
+            row = dict(weights=fmt, routes=R, rows_per_expert=R / E, density_rule=m.pick_block_m(R, E), gemms={})
+            for name in ("gate_up", "gate_up_act_quant", "down"):
+                down = name == "down"
+                a_q, a_s = (a2_q, a2_s) if down else (a1_q, a1_s)
+                w_s = w2_s if down else w13_s
+                N, K = (H, I) if down else (2 * I, H)
+                fused = name == "gate_up_act_quant"
+
+                def alloc():
+                    if fused:
+                        return (torch.empty((R, I), dtype=torch.uint8, device=dev),
+                                torch.empty((R, I // 128), dtype=torch.float32, device=dev))
+                    return (torch.empty((R, N), dtype=torch.bfloat16, device=dev),)
+
+                def call(bm, packed, out):
+                    w = (p2 if down else p13) if packed else (w2 if down else w13)
+                    if fmt == "fp8" and fused:
+                        m.bf8_grouped_gemm_act_quant(a_q, a_s, w, w_s, offs, out[0], out[1], block_m=bm, w_packed=packed)
+                    elif fmt == "fp8":
+                        m.bf8_grouped_gemm(a_q, a_s, w, w_s, out[0], mode=m.MOE_MODE_GROUPED, expert_offsets=offs,
+                                           block_m=bm, w_packed=packed)
+                    elif fused:
+                        m.mxfp4_grouped_gemm_act_quant(a_q, a_s, w, w_s, offs, out[0], out[1], block_m=bm,
+                                                       w_packed=packed)
+                    else:
+                        m.mxfp4_grouped_gemm(a_q, a_s, w, w_s, offs, out[0], block_m=bm, w_packed=packed)
+
+                base = alloc()
+                call(16, False, base)
                 torch.cuda.synchronize()
-                if not torch.equal(out.view(torch.int16), base.view(torch.int16)):
-                    raise RuntimeError("bm sweep: %s at %d routes: BM=%d differs from BM=%d" % (name, R, bm, pick))
-                t = Timer(torch)
-                for _ in range(steps):
-                    t.start()
-                    m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, out, mode=m.MOE_MODE_GROUPED, expert_offsets=offs,
-                                       block_m=bm)
-                    t.stop()
-                times[bm] = statistics.median(t.us())
-                log("bm sweep %s %d routes BM=%d: %.1f us" % (name, R, bm, times[bm]))
-            best = min(times, key=times.get)
-            row["gemms"][name] = dict(us_median=times, best=best, picked_over_best=times[pick] / times[best])
-        res.append(row)
+                if not fused:
+                    for e in (nonempty[0], nonempty[-1]):
+                        r0, r1 = int(rt.expert_offsets[e]), int(rt.expert_offsets[e + 1])
+                        one = np.array([0, r1 - r0], np.int32)
+                        wq = (w2 if down else w13)[e:e + 1].cpu().numpy()
+                        ws = w_s[e:e + 1].cpu().numpy()
+                        aq, as_ = a_q[r0:r1].cpu().numpy(), a_s[r0:r1].cpu().numpy()
+                        if fmt == "fp8":
+                            ref = oracle.block_gemm(aq, as_, wq, ws, mode=oracle.MODE_GROUPED, expert_offsets=one,
+                                                    out_dtype=np.uint16)
+                        else:
+                            ref = oracle.mxfp4_gemm(aq, as_, wq, ws, mode=oracle.MODE_GROUPED, expert_offsets=one,
+                                                    out_dtype=np.uint16)
+                        got = oracle.bf16_decode(base[0][r0:r1].view(torch.int16).cpu().numpy().view(np.uint16))
+                        got, r = got.astype(float), oracle.bf16_decode(ref).astype(float)
+                        rel = np.linalg.norm(got - r) / np.linalg.norm(r)
+                        if not (rel <= 5e-3 and np.abs(got - r).max() <= 2e-2 * np.abs(r).max()):
+                            raise RuntimeError("bm sweep: %s %s at %d routes, expert %d: rel L2 %.3e" % (
+                                fmt, name, R, e, rel))
+                for packed in (False, True):
+                    outs = {bm: alloc() for bm in (16, 32, 64, 128)}
+                    for bm in (16, 32, 64, 128):
+                        call(bm, packed, outs[bm])
+                        torch.cuda.synchronize()
+                        for x, y in zip(outs[bm], base):
+                            if not torch.equal(x.view(torch.uint8), y.view(torch.uint8)):
+                                raise RuntimeError("bm sweep: %s %s at %d routes: BM=%d%s differs from BM=16" % (
+                                    fmt, name, R, bm, " packed" if packed else ""))
+                    ts = {bm: [] for bm in (16, 32, 64, 128)}
+                    for rnd in range(rounds):
+                        for bm in (16, 32, 64, 128):
+                            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                            a.record()
+                            call(bm, packed, outs[bm])
+                            b.record()
+                            torch.cuda.synchronize()
+                            if rnd:
+                                ts[bm].append(a.elapsed_time(b) * 1000.0)
+                    times = {bm: statistics.median(v) for bm, v in ts.items()}
+                    best = min(times, key=times.get)
+                    lib = m.grouped_block_m(R, E, K, mxfp4=fmt == "mxfp4", packed=packed, fused=fused)
+                    row["gemms"][name + ("_packed" if packed else "")] = dict(
+                        us_median=times, best=best, library=lib, library_over_best=times[lib] / times[best])
+                    log("bm sweep %s %s %d routes%s: %s" % (fmt, name, R, " packed" if packed else "",
+                                                            " ".join("%d:%.1f" % kv for kv in times.items())))
+            res.append(row)
+        del w13, w2, p13, p2
+        torch.cuda.empty_cache()
     return res
 
 

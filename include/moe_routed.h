@@ -150,6 +150,22 @@ int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, in
 int moe_pick_block_m(int64_t routes, int64_t experts);
 
 /*
+ * moe_grouped_block_m  [tile]
+ *   The M tile the grouped-mode GEMMs take when called with block_m = 0, for
+ *   `routes` rows over `experts` experts, K, the weight format (mxfp4 = 0:
+ *   block-FP8, 1: MXFP4), the bank layout (packed = 1: MOE_W_PACKED) and the
+ *   form (fused = 1: the gate/up + requant entry points).  It refines
+ *   moe_pick_block_m with an MI355X sweep of every tile at 48 to 24576 routes
+ *   over 256 experts; with r = ceil(routes/experts):
+ *     block-FP8 row-major: 128 (plain), moe_pick_block_m (fused);
+ *     block-FP8 packed:    r <= 8: 16; r <= 64: 128 if K <= 2048, else 64; 128;
+ *     MXFP4:               r <= 8: 16; r <= 64: 32 (packed) or 64; 128, or 64
+ *                          for packed banks with K > 2048.
+ *   Pure function; 16 when routes or experts is <= 0.
+ */
+int moe_grouped_block_m(int64_t routes, int64_t experts, int64_t K, int mxfp4, int packed, int fused);
+
+/*
  * moe_bf8_grouped_gemm  -- block-FP8 GEMM for the gate/up and the down projections
  *   ("bf8" = block-FP8 with e4m3 operands.)
  *   out[r, n] = sum_kb ( sum_{k in kb} A[ar, k] * W[e, n, k] ) * a_s[ar, kb] * w_s[e, n/128, kb]
@@ -165,7 +181,8 @@ int moe_pick_block_m(int64_t routes, int64_t experts);
  *        expert_offsets is a DEVICE int32 array of n_experts+1 entries with
  *        expert_offsets[0] = 0 and expert_offsets[n_experts] <= m_rows (rows
  *        beyond it are left untouched).  block_m = 0 picks the M tile with
- *        moe_pick_block_m(m_rows, n_experts); 16, 32, 64 or 128 forces it.
+ *        moe_grouped_block_m (moe_pick_block_m's density rule, refined per
+ *        weight format and bank layout); 16, 32, 64 or 128 forces it.
  *        The kernel is persistent (one workgroup per resident slot); tiles
  *        come from the device offsets, clamped to [0, m_rows].
  *   mode MOE_MODE_SLOT (decode, [inactive]): row r uses slot slot_ids[r]

@@ -33,6 +33,7 @@ EXPORTS = (
     "moe_fused_decode_workspace_layout", "moe_fused_decode_workspace_init", "moe_fused_decode",
     "moe_route_prep_workspace_size", "moe_route_prep", "moe_bf8_grouped_gemm_act_quant",
     "moe_mxfp4_grouped_gemm", "moe_mxfp4_grouped_gemm_act_quant", "moe_fused_decode_noalloc", "moe_pack_weights",
+    "moe_grouped_block_m",
 )
 
 _lib = None
@@ -64,6 +65,7 @@ def lib():
             "moe_gather_rows_scales": ([P, I64, P, I64, I64, I64, I64, P, I64, P, I64, P, I64, P], I32),
             "moe_act_quant": ([P, I32, I64, I64, I64, I32, P, I64, P, I64, P], I32),
             "moe_pick_block_m": ([I64, I64], I32),
+            "moe_grouped_block_m": ([I64, I64, I64, I32, I32, I32], I32),
             "moe_bf8_grouped_gemm": ([P, I64, P, I64, P, I64, I64, P, I64, I64, I64, I64, I64, I32, P, P, I64, I64,
                                       ctypes.c_int32, P, I32, I64, P], I32),
             "moe_topk_reduce": ([P, I32, I64, P, P, P, I64, I64, I64, P, I64, P], I32),
@@ -124,6 +126,12 @@ def abi_version() -> int:
 
 def pick_block_m(routes: int, experts: int) -> int:
     return lib().moe_pick_block_m(routes, experts)
+
+
+def grouped_block_m(routes: int, experts: int, K: int, mxfp4: bool = False, packed: bool = False,
+                    fused: bool = False) -> int:
+    """The M tile the grouped GEMMs take for block_m = 0 (moe_grouped_block_m)."""
+    return lib().moe_grouped_block_m(routes, experts, K, int(mxfp4), int(packed), int(fused))
 
 
 def gather_rows_scales(src_q, src_s, dst2src, dst_q, dst_s, k=None, g=None, stream=None):

@@ -140,6 +140,31 @@ extern "C" int moe_pick_block_m(int64_t routes, int64_t experts) {
     return r <= 8 ? 16 : (r <= 64 ? 64 : 128);
 }
 
+extern "C" int moe_grouped_block_m(int64_t routes, int64_t experts, int64_t K, int mxfp4, int packed, int fused) {
+    // The tile the grouped GEMMs take for block_m = 0, from an interleaved sweep of every tile at 48 to
+    // 24576 routes over 256 experts (H = 4096, I = 1024), both weight formats and bank layouts, plain and
+    // fused.  The 128-row tiles run a workgroup's tiles as one pipeline when a tile has at most 16 K steps
+    // (block-FP8: always), so they win wherever that pipeline outweighs their single workgroup per CU.
+    //   block-FP8, row-major, plain: 128 at every density (3-15 % ahead of the density rule's tile);
+    //   block-FP8, row-major, fused: the density rule (the pipeline's epilogue costs more at few rows);
+    //   block-FP8, packed: 16 up to 8 rows per expert, then 128 for K <= 2048 (down: 6 % ahead) or 64,
+    //   then 128;
+    //   MXFP4: 16 up to 8 rows per expert, then 32 (packed) or 64 (row-major) up to 64, then 128, or 64
+    //   for packed banks with K > 2048 (the 128-row tiles run those one at a time: 4-12 % slower).
+    if (routes <= 0 || experts <= 0) return 16;
+    const int64_t r = ceil_div(routes, experts);
+    const bool short_k = K / 128 <= 16;
+    if (!mxfp4) {
+        if (!packed) return fused ? moe_pick_block_m(routes, experts) : 128;
+        if (r <= 8) return 16;
+        if (r <= 64) return short_k ? 128 : 64;
+        return 128;
+    }
+    if (r <= 8) return 16;
+    if (r <= 64) return packed ? 32 : 64;
+    return packed && !short_k ? 64 : 128;
+}
+
 extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const float* a_s, int64_t a_s_stride,
                                     const uint8_t* w_q, int64_t w_stride_e, int64_t w_stride_n,
                                     const float* w_s, int64_t w_s_stride_e, int64_t w_s_stride_n,
@@ -176,7 +201,7 @@ extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const 
     if (empty_bank) return MOE_ERR_SHAPE;
     if (!expert_offsets) return MOE_ERR_NULL;
     if (N % 128 != 0) return MOE_ERR_SHAPE;
-    int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
+    int bm = block_m == 0 ? moe_grouped_block_m(m_rows, n_experts, K, 0, w_stride_n == MOE_W_PACKED, 0) : block_m;
     if (bm != 16 && bm != 32 && bm != 64 && bm != 128) return MOE_ERR_SHAPE;
     return grouped_gemm_launch(st, bm, a_q, a_stride, a_s, a_s_stride, w_q, w_stride_e, w_stride_n, w_s,
                                w_s_stride_e, w_s_stride_n, n_experts, N, K, expert_offsets, m_rows, out, out_dt,
@@ -203,7 +228,7 @@ extern "C" int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stri
     const int rc = weight_bank_ok(w_q, w_stride_e, w_stride_n, n_experts, 2 * I, K);
     if (rc != MOE_OK) return rc;
     if (!aligned16(a_q) || a_stride % 16) return MOE_ERR_ALIGN;
-    const int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
+    const int bm = block_m == 0 ? moe_grouped_block_m(m_rows, n_experts, K, 0, w_stride_n == MOE_W_PACKED, 1) : block_m;
     return grouped_gemm_act_quant_launch(as_stream(stream), bm, act, a_q, a_stride, a_s, a_s_stride, w_q,
                                          w_stride_e, w_stride_n, w_s, w_s_stride_e, w_s_stride_n, n_experts, I, K,
                                          expert_offsets, m_rows, out_q, q_stride, out_s, s_stride);
@@ -244,7 +269,7 @@ extern "C" int moe_mxfp4_grouped_gemm(const uint8_t* a_q, int64_t a_stride, cons
     const int rc = mxfp4_args_ok(a_q, a_stride, a_s, a_s_stride, w4, w4_stride_e, w4_stride_n, w4_s, w4s_stride_e,
                                  w4s_stride_n, n_experts, N, K, expert_offsets);
     if (rc != MOE_OK) return rc;
-    const int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
+    const int bm = block_m == 0 ? moe_grouped_block_m(m_rows, n_experts, K, 1, w4_stride_n == MOE_W_PACKED, 0) : block_m;
     return mxfp4_grouped_gemm_launch(as_stream(stream), bm, 0, a_q, a_stride, a_s, a_s_stride, w4, w4_stride_e,
                                      w4_stride_n, w4_s, w4s_stride_e, w4s_stride_n, n_experts, N, K, expert_offsets,
                                      m_rows, out, out_dt, out_stride, nullptr, 0, nullptr, 0);
@@ -267,7 +292,7 @@ extern "C" int moe_mxfp4_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_st
     const int rc = mxfp4_args_ok(a_q, a_stride, a_s, a_s_stride, w4, w4_stride_e, w4_stride_n, w4_s, w4s_stride_e,
                                  w4s_stride_n, n_experts, 2 * I, K, expert_offsets);
     if (rc != MOE_OK) return rc;
-    const int bm = block_m == 0 ? moe_pick_block_m(m_rows, n_experts) : block_m;
+    const int bm = block_m == 0 ? moe_grouped_block_m(m_rows, n_experts, K, 1, w4_stride_n == MOE_W_PACKED, 1) : block_m;
     return mxfp4_grouped_gemm_launch(as_stream(stream), bm, act, a_q, a_stride, a_s, a_s_stride, w4, w4_stride_e,
                                      w4_stride_n, w4_s, w4s_stride_e, w4s_stride_n, n_experts, 2 * I, K,
                                      expert_offsets, m_rows, nullptr, MOE_F32, 0, out_q, q_stride, out_s, s_stride);

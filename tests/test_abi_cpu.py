@@ -324,3 +324,18 @@ def test_pack_weights_and_packed_bank_checks():
               w4_stride_n=m.MOE_W_PACKED, w4s=FAKE, w4s_stride_e=256 * 8, w4s_stride_n=8, n_experts=4, N=256, K=256,
               offsets=FAKE, m_rows=8, block_m=0, out=FAKE, out_dt=m.MOE_BF16, out_stride=256, stream=None)
     assert L.moe_mxfp4_grouped_gemm(*mx.values()) == m.MOE_ERR_SHAPE    # < N*K/2
+
+
+def test_grouped_block_m_refines_the_density_rule():
+    """moe_grouped_block_m: the tile the grouped GEMMs take for block_m = 0 (a pure function)."""
+    for r in (1, 6, 24, 96, 1000):
+        R = 256 * r
+        assert m.grouped_block_m(R, 256, 4096) == 128                                      # fp8 row-major
+        assert m.grouped_block_m(R, 256, 4096, fused=True) == m.pick_block_m(R, 256)      # fp8 row-major fused
+    assert [m.grouped_block_m(256 * r, 256, 4096, packed=True) for r in (8, 9, 64, 65)] == [16, 64, 64, 128]
+    assert [m.grouped_block_m(256 * r, 256, 1024, packed=True) for r in (8, 9, 64, 65)] == [16, 128, 128, 128]
+    assert [m.grouped_block_m(256 * r, 256, 4096, mxfp4=True) for r in (1, 8, 9, 64, 65)] == [16, 16, 64, 64, 128]
+    assert [m.grouped_block_m(256 * r, 256, 4096, mxfp4=True, packed=True) for r in (8, 9, 64, 65)] == [16, 32, 32, 64]
+    assert m.grouped_block_m(256 * 96, 256, 2048, mxfp4=True, packed=True) == 128    # <= 16 K steps
+    assert m.grouped_block_m(256 * 96, 256, 1024, mxfp4=True, fused=True) == 128
+    assert m.grouped_block_m(0, 256, 4096) == 16 and m.grouped_block_m(10, 0, 4096, mxfp4=True) == 16

@@ -170,8 +170,10 @@ def oracle_rows(fn, jobs):
 @pytest.mark.parametrize("T", [256, 1024, 4096])
 def test_prefill_full_size_fp8_vs_oracle(orc, T):
     R = T * TOPK
-    bm = m.pick_block_m(R, E_FULL)
-    print("prefill fp8 full size: %d routes, BM=%d" % (R, bm), flush=True)
+    # the tiles the launches take (block_m = 0): gate/up and the fused form at K = H, down at K = I
+    bms = {"gate/up": m.grouped_block_m(R, E_FULL, H), "fused": m.grouped_block_m(R, E_FULL, H, fused=True),
+           "down": m.grouped_block_m(R, E_FULL, I)}
+    print("prefill fp8 full size: %d routes, BM %s" % (R, bms), flush=True)
     d = dev()
     w13_q, w13_s = wl.block_fp8_weights(E_FULL, 2 * I, H, 21, device=d, chunk_experts=32)
     w2_q, w2_s = wl.block_fp8_weights(E_FULL, H, I, 22, device=d, chunk_experts=32)
@@ -189,7 +191,7 @@ def test_prefill_full_size_fp8_vs_oracle(orc, T):
     m.bf8_grouped_gemm(a2_q, a2_s, w2_q, w2_s, c2, mode=m.MOE_MODE_GROUPED, expert_offsets=od)
     torch.cuda.synchronize()
     for name, n_tiles_n in (("gate/up", 2 * I // 256), ("fused", I // 128), ("down", H // 256)):
-        experts = sampled_experts(offs, bm, n_tiles_n)
+        experts = sampled_experts(offs, bms[name], n_tiles_n)
         print("  %s: experts %s" % (name, experts), flush=True)
         jobs = []
         for e in experts:
@@ -224,8 +226,10 @@ def test_prefill_full_size_fp8_vs_oracle(orc, T):
 @pytest.mark.parametrize("T", [1024, 4096])
 def test_prefill_full_size_mxfp4_vs_oracle(orc, T):
     R = T * TOPK
-    bm = m.pick_block_m(R, E_FULL)
-    print("prefill mxfp4 full size: %d routes, BM=%d" % (R, bm), flush=True)
+    bms = {"gate/up": m.grouped_block_m(R, E_FULL, H, mxfp4=True),
+           "fused": m.grouped_block_m(R, E_FULL, H, mxfp4=True, fused=True),
+           "down": m.grouped_block_m(R, E_FULL, I, mxfp4=True)}
+    print("prefill mxfp4 full size: %d routes, BM %s" % (R, bms), flush=True)
     d = dev()
     w13, w13_s = wl.mxfp4_weights(E_FULL, 2 * I, H, seed=31, device=d)
     w2, w2_s = wl.mxfp4_weights(E_FULL, H, I, seed=32, device=d)
@@ -243,7 +247,7 @@ def test_prefill_full_size_mxfp4_vs_oracle(orc, T):
     m.mxfp4_grouped_gemm(a2_q, a2_s, w2, w2_s, od, c2)
     torch.cuda.synchronize()
     for name, n_tiles_n in (("gate/up", 2 * I // 256), ("fused", I // 128), ("down", H // 256)):
-        experts = sampled_experts(offs, bm, n_tiles_n)
+        experts = sampled_experts(offs, bms[name], n_tiles_n)
         print("  %s: experts %s" % (name, experts), flush=True)
         jobs = []
         for e in experts:
