@@ -8,90 +8,155 @@
 // to zero codes and zero scales ("perf(moe): skip inactive block-fp8 decode
 // routes", opening section).
 //
-// MI355X design: one wavefront per (row, 512 columns), from a 2D grid (column
+// MI355X design: one wavefront per (row, 1024 columns), from a 2D grid (column
 // groups x rows, rows taken in strides beyond 65535) so no index needs an
-// integer division.  The kernel is bound by its vector ALU work (about 150
-// instructions per wavefront), not by HBM: waves that take 2, 4 or 8 rows with
-// all their loads in flight at once ran slower, not faster.  Each lane owns 8
-// consecutive columns, 16 lanes form one 128-column group, and the group amax
-// is four DPP row moves inside the wave, so no LDS and no barrier is needed.
-// The 8 codes of a lane leave as one 8-byte store.  The scale is amax/448 with
+// integer division.  The kernel is bound by its vector ALU work, not by HBM
+// (instruction counters: 0.7 of its time issuing VALU at 8 columns per lane),
+// so each lane owns 16 consecutive columns: the per-group scale, reciprocal
+// and amax and the addressing (a wave-uniform row base plus a 32-bit lane
+// offset) are then shared by twice the codes.  Waves that took 2, 4 or 8 rows
+// with all their loads in flight at once ran slower, not faster.  8 lanes form
+// one 128-column group, and the group amax is three DPP moves inside the wave,
+// so no LDS and no barrier is needed.  The 16 codes of a lane leave as one
+// 16-byte store.  The scale is amax/448 with
 // the correctly rounded fp32 division and each code is that of v/s rounded to
 // nearest even (clamped to +-448), matching the definition bit for bit in
 // IDENTITY mode; the quotient is v * (1/s) except near a code boundary, where
-// it is the exact division (e4m3_quot), so one division per lane replaces eight.
+// it is the exact division (e4m3_quot), so one division per lane replaces sixteen.
 #include "device.h"
 #include "host.h"
 
 namespace moe {
 namespace {
 
-constexpr int kColsPerLane = 8;
-constexpr int kColsPerWave = kWave * kColsPerLane;   // 512 = 4 groups
+constexpr int kColsPerLane = 16;
+constexpr int kColsPerWave = kWave * kColsPerLane;   // 1024 = 8 groups
 
-constexpr int kRowsPerWave = 1;                      // rows per wavefront (loads of all issued together)
 
-// One lane's 16-byte input words for its 8 columns of one row (two words for f32), and those of the
-// matching up columns when the activation is gated.
+// One lane's 16-byte input words for its 16 columns of one row (four words for f32), and those of
+// the matching up columns when the activation is gated.
 template <int DT>
 struct RawCols {
-    uint4 g[DT == kF32 ? 2 : 1];
-    uint4 u[DT == kF32 ? 2 : 1];
+    static constexpr int W = DT == kF32 ? 4 : 2;
+    uint4 g[W];
+    uint4 u[W];
 };
 
+// rowp: the row's first input byte (wave-uniform); off: this lane's byte offset of column c0
 template <int DT, bool GATED>
-__device__ __forceinline__ RawCols<DT> load_cols(const void* __restrict__ in, int64_t base, int64_t n, int64_t c0) {
+__device__ __forceinline__ RawCols<DT> load_cols(const char* __restrict__ rowp, uint32_t off, int64_t up_bytes) {
     RawCols<DT> r;
-    const int64_t ge = DT == kF32 ? 4 : 2;      // element size
-    const uint4* pg = reinterpret_cast<const uint4*>((const char*)in + (base + c0) * ge);
-    r.g[0] = pg[0];
-    if constexpr (DT == kF32) r.g[1] = pg[1];
+    const uint4* pg = reinterpret_cast<const uint4*>(rowp + off);
+#pragma unroll
+    for (int i = 0; i < RawCols<DT>::W; i++) r.g[i] = pg[i];
     if constexpr (GATED) {
-        const uint4* pu = reinterpret_cast<const uint4*>((const char*)in + (base + n + c0) * ge);
-        r.u[0] = pu[0];
-        if constexpr (DT == kF32) r.u[1] = pu[1];
+        const uint4* pu = reinterpret_cast<const uint4*>(rowp + up_bytes + off);
+#pragma unroll
+        for (int i = 0; i < RawCols<DT>::W; i++) r.u[i] = pu[i];
     }
     return r;
 }
 
 template <int DT>
-__device__ __forceinline__ void unpack_cols(const uint4 (&w)[DT == kF32 ? 2 : 1], float (&v)[8]) {
-    if constexpr (DT == kF32) {
-        const uint32_t x[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+__device__ __forceinline__ void unpack_cols(const uint4 (&w)[RawCols<DT>::W], float (&v)[kColsPerLane]) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) v[i] = __uint_as_float(x[i]);
-    } else {
-        const uint32_t x[4] = {w[0].x, w[0].y, w[0].z, w[0].w};
+    for (int k = 0; k < RawCols<DT>::W; k++) {
+        const uint32_t x[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+        if constexpr (DT == kF32) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            v[2 * i] = DT == kBF16 ? bf16_to_f32((uint16_t)(x[i] & 0xFFFF)) : f16_to_f32((uint16_t)(x[i] & 0xFFFF));
-            v[2 * i + 1] = DT == kBF16 ? bf16_to_f32((uint16_t)(x[i] >> 16)) : f16_to_f32((uint16_t)(x[i] >> 16));
+            for (int i = 0; i < 4; i++) v[4 * k + i] = __uint_as_float(x[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                v[8 * k + 2 * i] = DT == kBF16 ? bf16_to_f32((uint16_t)(x[i] & 0xFFFF)) : f16_to_f32((uint16_t)(x[i] & 0xFFFF));
+                v[8 * k + 2 * i + 1] = DT == kBF16 ? bf16_to_f32((uint16_t)(x[i] >> 16)) : f16_to_f32((uint16_t)(x[i] >> 16));
+            }
         }
     }
 }
 
-// One wavefront's 512 columns [c0 - 8*lane, +512) of one row; this lane owns columns [c0, c0 + 8).
-template <int DT, bool GATED, bool VEC>
-__device__ __forceinline__ void act_quant_row(const void* __restrict__ in, int64_t base, int64_t row, int64_t n, int act,
-                                              int64_t c0, int lane, const RawCols<DT>& raw, uint8_t* __restrict__ out_q,
-                                              int64_t q_stride, float* __restrict__ out_s, int64_t s_stride) {
-    const int64_t ncols = n;   // width of v
-    float v[kColsPerLane];
-    const bool full = c0 + kColsPerLane <= ncols;
-    if (VEC && full) {
+// The 16 codes (as four words) and the group scale of this lane's columns v; the 8 lanes of a
+// 128-column group share the scale.
+__device__ __forceinline__ void quant_cols(const float (&v)[kColsPerLane], uint32_t (&w)[4], float& s) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kColsPerLane; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    amax = group8_max(amax);                   // 8 lanes = one 128-column group
+    s = amax / 448.0f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) w[k] = 0u;
+    if (s != 0.0f) {
+        // the quotients as v * (1/s), with one bit per column that needs the exact division (e4m3_quot's
+        // test); the rare columns that do are redone together afterwards, so the common path has no
+        // branch per column
+        const float r = 1.0f / s;
+        float q[kColsPerLane];
+        uint32_t exact = 0u;
+#pragma unroll
+        for (int i = 0; i < kColsPerLane; i++) {
+            q[i] = v[i] * r;
+            exact |= (uint32_t)e4m3_quot_needs_division(q[i]) << i;
+        }
+        if (exact != 0u) {
+#pragma unroll
+            for (int i = 0; i < kColsPerLane; i++)
+                if (exact & (1u << i)) q[i] = v[i] / s;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) w[k] = enc4_e4m3(q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]);
+    }
+}
+
+// A segment of 1024 columns that lies inside the row, with 16-byte aligned loads: no per-column bounds;
+// the row bases are wave-uniform and each lane adds its own 32-bit offset.
+template <int DT, bool GATED>
+__device__ __forceinline__ void act_quant_segment(const void* __restrict__ in, int64_t in_stride, int64_t rows,
+                                                  int64_t n, int act, int64_t seg, int lane,
+                                                  uint8_t* __restrict__ out_q, int64_t q_stride,
+                                                  float* __restrict__ out_s, int64_t s_stride) {
+    constexpr int64_t esz = DT == kF32 ? 4 : 2;
+    const uint32_t lane_off = (uint32_t)(lane * kColsPerLane * esz);
+    const uint32_t q_off = (uint32_t)(lane * kColsPerLane);
+    for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+        const char* rowp = (const char*)in + (row * in_stride + seg * kColsPerWave) * esz;
+        const RawCols<DT> raw = load_cols<DT, GATED>(rowp, lane_off, n * esz);
+        float v[kColsPerLane];
         unpack_cols<DT>(raw.g, v);
         if constexpr (GATED) {
-            float u[8];
+            float u[kColsPerLane];
             unpack_cols<DT>(raw.u, u);
 #pragma unroll
-            for (int i = 0; i < 8; i++) v[i] = gated_act(act, v[i], u[i]);
+            for (int i = 0; i < kColsPerLane; i++) v[i] = gated_act(act, v[i], u[i]);
         }
-    } else {
+        uint32_t w[4];
+        float s;
+        quant_cols(v, w, s);
+        uint8_t* q = out_q + row * q_stride + seg * kColsPerWave + q_off;
+        if ((reinterpret_cast<uintptr_t>(q) & 15u) == 0) {
+            *reinterpret_cast<uint4*>(q) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kColsPerLane; i++) q[i] = (uint8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xFF);
+        }
+        if ((lane & 7) == 0) out_s[row * s_stride + seg * (kColsPerWave / 128) + (lane >> 3)] = s;
+    }
+}
+
+// Any segment: per-column bounds and element loads (the last, partial segment of a row, or inputs whose
+// rows or up offset are not 16-byte aligned).  This lane owns columns [c0, c0 + 16).
+template <int DT, bool GATED>
+__device__ __forceinline__ void act_quant_segment_any(const void* __restrict__ in, int64_t in_stride, int64_t rows,
+                                                      int64_t n, int act, int64_t c0, int lane,
+                                                      uint8_t* __restrict__ out_q, int64_t q_stride,
+                                                      float* __restrict__ out_s, int64_t s_stride) {
+    for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
+        const int64_t base = row * in_stride;
+        float v[kColsPerLane];
 #pragma unroll
         for (int i = 0; i < kColsPerLane; i++) {
             const int64_t c = c0 + i;
             float x = 0.0f;
-            if (c < ncols) {
+            if (c < n) {
                 x = load_as_f32<DT>(in, base + c);
                 if constexpr (GATED) {
                     float u = load_as_f32<DT>(in, base + n + c);
@@ -100,27 +165,14 @@ __device__ __forceinline__ void act_quant_row(const void* __restrict__ in, int64
             }
             v[i] = x;
         }
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kColsPerLane; i++) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
-    amax = row16_max(amax);                    // 16 lanes = one 128-column group
-    const float s = amax / 448.0f;
-    uint32_t lo = 0, hi = 0;
-    if (s != 0.0f) {
-        const float r = 1.0f / s;
-        lo = enc4_e4m3(e4m3_quot(v[0], s, r), e4m3_quot(v[1], s, r), e4m3_quot(v[2], s, r), e4m3_quot(v[3], s, r));
-        hi = enc4_e4m3(e4m3_quot(v[4], s, r), e4m3_quot(v[5], s, r), e4m3_quot(v[6], s, r), e4m3_quot(v[7], s, r));
-    }
-    if (c0 < ncols) {
-        uint8_t* q = out_q + row * q_stride + c0;
-        if (full && (reinterpret_cast<uintptr_t>(q) & 7u) == 0) {
-            *reinterpret_cast<uint2*>(q) = make_uint2(lo, hi);
-        } else {
-            for (int i = 0; i < kColsPerLane && c0 + i < ncols; i++)
-                q[i] = (uint8_t)(((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFF);
+        uint32_t w[4];
+        float s;
+        quant_cols(v, w, s);
+        if (c0 < n) {
+            uint8_t* q = out_q + row * q_stride + c0;
+            for (int i = 0; i < kColsPerLane && c0 + i < n; i++) q[i] = (uint8_t)((w[i >> 2] >> (8 * (i & 3))) & 0xFF);
+            if ((lane & 7) == 0) out_s[row * s_stride + c0 / 128] = s;
         }
-        if ((lane & 15) == 0) out_s[row * s_stride + c0 / 128] = s;
     }
 }
 
@@ -129,28 +181,15 @@ __global__ void __launch_bounds__(256)
 act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, int64_t n, int act,
                  uint8_t* __restrict__ out_q, int64_t q_stride, float* __restrict__ out_s, int64_t s_stride) {
     const int lane = threadIdx.x & (kWave - 1);
-    // grid: x = groups of blockDim.x/64 segments of 512 columns, y = groups of kRowsPerWave rows (taken
-    // in strides beyond the grid), so no index needs an integer division
-    const int64_t seg = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const int64_t c0 = seg * kColsPerWave + (int64_t)lane * kColsPerLane;
+    // grid: x = groups of blockDim.x/64 segments of 1024 columns, y = rows (taken in strides beyond the
+    // grid), so no index needs an integer division; the segment is wave-uniform
+    const int64_t seg = (int64_t)blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (seg * kColsPerWave >= n) return;
-    const bool full = c0 + kColsPerLane <= n;
-    for (int64_t r0 = (int64_t)blockIdx.y * kRowsPerWave; r0 < rows; r0 += (int64_t)gridDim.y * kRowsPerWave) {
-        RawCols<DT> raw[kRowsPerWave];
-        if (VEC && full) {
-            // every row's loads go out before the first is used (rows past the end re-read the last)
-#pragma unroll
-            for (int u = 0; u < kRowsPerWave; u++) {
-                const int64_t row = r0 + u < rows ? r0 + u : rows - 1;
-                raw[u] = load_cols<DT, GATED>(in, row * in_stride, n, c0);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kRowsPerWave; u++)
-            if (r0 + u < rows)
-                act_quant_row<DT, GATED, VEC>(in, (r0 + u) * in_stride, r0 + u, n, act, c0, lane, raw[u], out_q, q_stride,
-                                              out_s, s_stride);
-    }
+    if (VEC && (seg + 1) * kColsPerWave <= n)
+        act_quant_segment<DT, GATED>(in, in_stride, rows, n, act, seg, lane, out_q, q_stride, out_s, s_stride);
+    else
+        act_quant_segment_any<DT, GATED>(in, in_stride, rows, n, act, seg * kColsPerWave + (int64_t)lane * kColsPerLane,
+                                         lane, out_q, q_stride, out_s, s_stride);
 }
 
 template <int DT, bool GATED>
@@ -179,12 +218,12 @@ extern "C" int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64
     const int64_t width = act != MOE_ACT_IDENTITY ? 2 * n : n;
     if (in_stride < width || q_stride < n || s_stride < ceil_div(n, 128)) return MOE_ERR_SHAPE;
     const int64_t esz = in_dt == MOE_F32 ? 4 : 2;
-    // vector loads need every lane's 8 elements 16-byte aligned: base, stride and the up offset
+    // vector loads need every lane's 16 elements 16-byte aligned: base, stride and the up offset
     const bool vec = aligned16(in) && (in_stride * esz) % 16 == 0 && (n * esz) % 16 == 0;
-    const int64_t segs = ceil_div(n, kColsPerWave);                   // 512-column segments per row
+    const int64_t segs = ceil_div(n, kColsPerWave);                   // 1024-column segments per row
     const int64_t wpb = segs < 4 ? segs : 4;                            // waves per workgroup
     const int64_t col_blocks = ceil_div(segs, wpb);
-    const int64_t row_blocks = ceil_div(rows, kRowsPerWave);
+    const int64_t row_blocks = rows;
     if (col_blocks > 0x7FFFFFFF) return MOE_ERR_SHAPE;
     dim3 grid((unsigned)col_blocks, (unsigned)(row_blocks < 65535 ? row_blocks : 65535)), block((unsigned)(wpb * kWave));
     auto st = as_stream(stream);

@@ -39,12 +39,15 @@ __device__ __forceinline__ uint32_t enc2_e4m3(float a, float b) {
 // low 20 bits 0x80000 (normal range) and lie 2^20 ulp apart.  So v * r names the same code as
 // RN(v / s) unless its low bits lie within 16 of a midpoint's, or it is below the e4m3 normal range
 // (2^-6, where the code grid is finer), or not finite; those take the exact division.
-__device__ __forceinline__ float e4m3_quot(float v, float s, float r) {
-    const float q = v * r;
+__device__ __forceinline__ bool e4m3_quot_needs_division(float q) {
     const uint32_t b = __float_as_uint(q) & 0x7FFFFFFFu;
     const bool edge = (b & 0xFFFFFu) - 0x7FFF0u <= 0x20u;
-    if (b != 0u && (edge || b < 0x3C800000u || b >= 0x7F800000u)) return v / s;
-    return q;
+    return b != 0u && (edge || b < 0x3C800000u || b >= 0x7F800000u);
+}
+
+__device__ __forceinline__ float e4m3_quot(float v, float s, float r) {
+    const float q = v * r;
+    return e4m3_quot_needs_division(q) ? v / s : q;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
