@@ -125,6 +125,16 @@ inline void set_weight_layout(GgArgs& g, bool w4) {
     g.w_khalf = g.w_packed ? 1024 : 64;
 }
 
+// LDS byte offset, within a 16-row A sub-tile (2 KiB), of piece h of MFMA lane `lane`: h = 0 holds the
+// row's K bytes 16q .. 16q+15 and h = 1 bytes 64+16q .. +15 (q = lane/16), the order the weight pieces
+// take.  The 128 pieces are 16-byte slots 64h + lane with the low three bits XORed by 4h + q, so the 8
+// lanes an LDS cycle serves read 8 different slots of a 128-byte span, and so do the 8 chunks of one A
+// row (chunk 4h + q) that 8 consecutive threads write (without the XOR, reads were 2-way and writes
+// 8-way conflicts).
+__device__ __forceinline__ int a_piece_offset(int lane, int h) {
+    return 16 * ((64 * h + lane) ^ (4 * h + ((lane >> 4) & 3)));
+}
+
 // Byte offset, from w_q, of this lane's first weight piece of the 16-row group that starts at row r16
 // (a multiple of 16) of expert e.  Row-major: row r16 + lane%16, bytes 16*(lane/16) of each K step (and
 // 64 more for the second piece).  Packed: the pieces of a step are stored in lane order.
@@ -303,6 +313,7 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     // Threads beyond the tile's chunks load a valid chunk too (never stored).
     int64_t a_src[A_PER_THREAD];
     int a_dst[A_PER_THREAD];
+    const int a_p0 = a_piece_offset(lane, 0), a_p1 = a_piece_offset(lane, 1);   // this lane's MFMA pieces
 #pragma unroll
     for (int j = 0; j < A_PER_THREAD; j++) {
         const int c0 = tid + j * NT;
@@ -311,8 +322,8 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
         int row = row0 + rr;
         if (row >= row_end) row = row_end - 1;     // padding rows: any valid row, outputs dropped
         a_src[j] = (int64_t)row * a_stride + ch * 16;
-        // fragment order: sub-tile rr/16, lane (rr%16) + 16*(ch%4), half ch/4
-        a_dst[j] = (rr / 16) * 2048 + ((rr % 16) + 16 * (ch % 4)) * 32 + (ch / 4) * 16;
+        // fragment order: sub-tile rr/16, lane (rr%16) + 16*(ch%4), piece ch/4
+        a_dst[j] = (rr / 16) * 2048 + a_piece_offset((rr % 16) + 16 * (ch % 4), ch / 4);
     }
 
     // A K steps pass through SA register stages (step kb in stage kb % SA) on their way to LDS, W K
@@ -420,7 +431,9 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
                     if (MS > 4 && m * 16 >= tile_rows) continue;
                     // W is the MFMA's row operand and A its column operand, so a lane's four results
                     // share one A row (lane % 16) and take a single scale
-                    const v8i a = *reinterpret_cast<const v8i*>(&a_lds[buf][m * 2048 + lane * 32]);
+                    const v8i a = __builtin_shufflevector(*reinterpret_cast<const v4i*>(&a_lds[buf][m * 2048 + a_p0]),
+                                                          *reinterpret_cast<const v4i*>(&a_lds[buf][m * 2048 + a_p1]),
+                                                          0, 1, 2, 3, 4, 5, 6, 7);
                     const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                     const float sa = sa_lds[kb * SA_ROW + m * 16 + (lane & 15)];
 #pragma unroll
@@ -577,8 +590,9 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
         const int c0 = tid + j * NT;
         const int c = c0 < A_CHUNKS ? c0 : c0 % A_CHUNKS;
         const int rr = c / 8, ch = c % 8;
-        a_dst[j] = (rr / 16) * 2048 + ((rr % 16) + 16 * (ch % 4)) * 32 + (ch / 4) * 16;
+        a_dst[j] = (rr / 16) * 2048 + a_piece_offset((rr % 16) + 16 * (ch % 4), ch / 4);
     }
+    const int a_p0 = a_piece_offset(lane, 0), a_p1 = a_piece_offset(lane, 1);   // this lane's MFMA pieces
 
     // a tile's scales: requested into registers (lane = K block), written to one half of the tables
     struct Scales {
@@ -748,7 +762,9 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
 #pragma unroll
                     for (int m = 0; m < MS; m++) {
                         if (MS > 4 && m * 16 >= tile_rows) continue;
-                        const v8i a = *reinterpret_cast<const v8i*>(&a_lds[par][m * 2048 + lane * 32]);
+                        const v8i a = __builtin_shufflevector(
+                            *reinterpret_cast<const v4i*>(&a_lds[par][m * 2048 + a_p0]),
+                            *reinterpret_cast<const v4i*>(&a_lds[par][m * 2048 + a_p1]), 0, 1, 2, 3, 4, 5, 6, 7);
                         const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
                         const float sa = sa_t[kb * SA_ROW + m * 16 + (lane & 15)];
 #pragma unroll
