@@ -320,6 +320,25 @@ def test_fused_decode_narrow_two_launch_down_tiles(orc, active):
     assert np.all(ctl[2:] == 0) and ctl[0] == 0
 
 
+@pytest.mark.parametrize("T,I,topk,active", [(1, 1024, 3, 2), (2, 512, 8, 5)])
+def test_fused_decode_wide_two_launch_down_tiles_other_shapes(orc, T, I, topk, active):
+    """H = 4096 beyond the 4096/1024 top-8 step: top-3 of one token and two tokens at I = 512, both run as
+    two launches with 16-row down tiles: against the oracle with a NaN-poisoned workspace, and the control
+    block is never written past its shape word."""
+    H = 4096
+    print("fused decode two launches T=%d H=%d I=%d topk=%d" % (T, H, I, topk), flush=True)
+    assert one_launch_epoch_words(T, H, I, topk) == 0
+    c = wl.decode_case(H=H, I=I, topk=topk, n_slots=12, active=active, seed=4096 + T + I + topk, T=T)
+    dd = DevDecode(c)
+    dd.poison()
+    dd.run()
+    torch.cuda.synchronize()
+    ref, im = oracle_decode(c)
+    check_against_oracle(dd, ref, im)
+    ctl = dd.ws[dd.lay["ctl"]:dd.lay["total"]].view(torch.int32).cpu().numpy()
+    assert np.all(ctl[2:] == 0) and ctl[0] == 0
+
+
 def test_workspace_of_another_shape_sets_the_error_word(orc):
     """A workspace initialized for one shape and passed with another (large enough for both): the one-launch
     step sees the shape word disagree, waits on no hand-off word and sets the error word to 2; a fresh init
