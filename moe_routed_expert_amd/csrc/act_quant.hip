@@ -10,19 +10,22 @@
 //
 // MI355X design: one wavefront per (row, 1024 columns), from a 2D grid (column
 // groups x rows, rows taken in strides beyond 65535) so no index needs an
-// integer division.  The kernel is bound by its vector ALU work, not by HBM
-// (instruction counters: 0.7 of its time issuing VALU at 8 columns per lane),
-// so each lane owns 16 consecutive columns: the per-group scale, reciprocal
-// and amax and the addressing (a wave-uniform row base plus a 32-bit lane
-// offset) are then shared by twice the codes.  Waves that took 2, 4 or 8 rows
-// with all their loads in flight at once ran slower, not faster.  8 lanes form
+// integer division.  Each lane owns 16 consecutive columns: the per-group
+// scale, reciprocal and amax and the addressing (a wave-uniform row base plus a
+// 32-bit lane offset) are shared by 16 codes, and the exact-quotient test is
+// two integer operations per column, so VALU issue is well under the kernel's
+// time (instruction counters).  Waves that took 2, 4 or 8 rows with all their
+// loads in flight at once, or that requested the next row while quantizing the
+// current one (fewer, longer-lived workgroups), ran slower, not faster: the
+// kernel is bound by how many waves have loads in flight.  8 lanes form
 // one 128-column group, and the group amax is three DPP moves inside the wave,
 // so no LDS and no barrier is needed.  The 16 codes of a lane leave as one
 // 16-byte store.  The scale is amax/448 with
 // the correctly rounded fp32 division and each code is that of v/s rounded to
 // nearest even (clamped to +-448), matching the definition bit for bit in
-// IDENTITY mode; the quotient is v * (1/s) except near a code boundary, where
-// it is the exact division (e4m3_quot), so one division per lane replaces sixteen.
+// IDENTITY mode; the quotient is v * rcp(s) except near a code boundary, where
+// it is the exact division (e4m3_quot_near_boundary), so one division per lane
+// replaces sixteen.
 #include "device.h"
 #include "host.h"
 
@@ -86,21 +89,22 @@ __device__ __forceinline__ void quant_cols(const float (&v)[kColsPerLane], uint3
 #pragma unroll
     for (int k = 0; k < 4; k++) w[k] = 0u;
     if (s != 0.0f) {
-        // the quotients as v * (1/s), with one bit per column that needs the exact division (e4m3_quot's
-        // test); the rare columns that do are redone together afterwards, so the common path has no
-        // branch per column
-        const float r = 1.0f / s;
+        // the quotients as v * rcp(s); the rare columns next to a code boundary (e4m3_quot_near_boundary)
+        // are redone with the exact division afterwards, all together, so the common path has no branch
+        // per column.  Below s = 2^-100, rcp(s) may not be finite: every column takes the division.
+        const float r = __builtin_amdgcn_rcpf(s);
+        const bool tiny = s < 0x1p-100f;
         float q[kColsPerLane];
-        uint32_t exact = 0u;
+        bool redo = tiny;
 #pragma unroll
         for (int i = 0; i < kColsPerLane; i++) {
             q[i] = v[i] * r;
-            exact |= (uint32_t)e4m3_quot_needs_division(q[i]) << i;
+            redo = redo | e4m3_quot_near_boundary(q[i]);     // no short-circuit: no branch per column
         }
-        if (exact != 0u) {
+        if (redo) {
 #pragma unroll
             for (int i = 0; i < kColsPerLane; i++)
-                if (exact & (1u << i)) q[i] = v[i] / s;
+                if (tiny | e4m3_quot_near_boundary(q[i])) q[i] = v[i] / s;
         }
 #pragma unroll
         for (int k = 0; k < 4; k++) w[k] = enc4_e4m3(q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]);

@@ -33,21 +33,19 @@ __device__ __forceinline__ uint32_t enc2_e4m3(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false) & 0xFFFFu;
 }
 
-// v / s where only the e4m3 code of the correctly rounded quotient is wanted; r is 1/s correctly
-// rounded.  v * r is within 2.5 ulp of RN(v / s) (two roundings of relative size 2^-24 each, plus
-// RN's half ulp), and e4m3 codes change only at midpoints between e4m3 values, which in fp32 have
-// low 20 bits 0x80000 (normal range) and lie 2^20 ulp apart.  So v * r names the same code as
-// RN(v / s) unless its low bits lie within 16 of a midpoint's, or it is below the e4m3 normal range
-// (2^-6, where the code grid is finer), or not finite; those take the exact division.
-__device__ __forceinline__ bool e4m3_quot_needs_division(float q) {
-    const uint32_t b = __float_as_uint(q) & 0x7FFFFFFFu;
-    const bool edge = (b & 0xFFFFFu) - 0x7FFF0u <= 0x20u;
-    return b != 0u && (edge || b < 0x3C800000u || b >= 0x7F800000u);
-}
-
-__device__ __forceinline__ float e4m3_quot(float v, float s, float r) {
-    const float q = v * r;
-    return e4m3_quot_needs_division(q) ? v / s : q;
+// q = v * r, where r is 1/s to within 1 ulp (v_rcp_f32) and s >= 2^-100, stands for RN(v / s) when only
+// its e4m3 code is wanted.  q is within 3.5 ulp of RN(v / s) (r's ulp, the product's half ulp and RN's
+// half ulp), and e4m3 codes change only at midpoints between e4m3 values, which in fp32 have low 20 bits
+// 0x80000 in the e4m3 normal range (|q| >= 2^-6) and lie 2^20 ulp apart.  So q names the same code as
+// RN(v / s) unless its low 20 bits lie within 16 of 0x80000, or 0 < |q| < 2^-6 (where the code grid is
+// finer); those take the exact division.  A non-finite q comes from a non-finite v and gives the same
+// clamped code either way.  Two integer operations per test: (b << 12) + 0x80010000 is
+// ((low 20 bits) - 0x7FFF0) << 12, and (b << 1) - 2 drops the sign and maps 0 past the range.
+__device__ __forceinline__ bool e4m3_quot_near_boundary(float q) {
+    const uint32_t b = __float_as_uint(q);
+    const bool mid = (b << 12) + 0x80010000u < 0x21000u;
+    const bool small = (b << 1) - 2u < (0x3C800000u << 1) - 2u;
+    return mid | small;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
