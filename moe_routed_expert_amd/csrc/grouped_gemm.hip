@@ -246,7 +246,6 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
     const int64_t n0 = (int64_t)n_tile * C::BN;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const bool cols = FUSED || n0 + wv * CPW < N;   // a last 256-column tile may hold only 128 columns
-    const int q16 = (lane / 16) * 16;
     // weight fragment pointers: wave owns columns n0 + CPW*wave + [0, CPW), TPW 16-column sub-tiles.
     // The idle waves of a 128-column last tile read valid columns (their results are dropped), so
     // the loop has no branch around its loads.  Fused: sub-tile 0 is gate rows 128*n_tile + 16*wave +
@@ -527,7 +526,6 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
     const int nkb = (int)(K / 128);
     const int last = nkb - 1;
     const int nsteps = (nkb + S - 1) / S * S;
-    const int q16 = (lane / 16) * 16;
     const int kbl = lane < nkb ? lane : nkb - 1;
     const int sshift = 8 * (lane / 16);
     uint8_t* const sc_wave = sc_lds + wave * 32 * kScRow;
