@@ -130,9 +130,12 @@ int moe_gather_rows_scales(const void* src_q, int64_t src_q_stride,
  *   out_q [rows][q_stride] bytes, out_s [rows][s_stride] fp32 (ceil(n/128) used)
  *   Inputs must be finite.  IDENTITY mode is bit-exact with a correctly
  *   rounded division and round-to-nearest-even e4m3 encoding, and so are
- *   RELU_MUL and MUL (exact fp32 products); SILU, GELU and SIGMOID use the
- *   device expf / erff, so their codes may differ by one e4m3 step from a
- *   host evaluation.  An all-zero group gives s = +0 and q = 0x00 (a zeroed
+ *   RELU_MUL and MUL (exact fp32 products).  SILU and SIGMOID take the
+ *   sigmoid as rcp(1 + exp2(-g * log2 e)) from the hardware exp2 and
+ *   reciprocal (each within 1 ulp; 0 once 1 + e^-g exceeds 2^126, i.e. for
+ *   g below about -87.3), GELU the device erff, so their values differ from
+ *   the fp32 libm expressions of moe_act by a few ulp and a code may differ
+ *   by one e4m3 step, rarely.  An all-zero group gives s = +0 and q = 0x00 (a zeroed
  *   inactive-route tile stays zero, [inactive] opening section).
  */
 int moe_act_quant(const void* in, int in_dt, int64_t in_stride, int64_t rows, int64_t n, int act,

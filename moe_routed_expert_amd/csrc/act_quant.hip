@@ -95,16 +95,25 @@ __device__ __forceinline__ void quant_cols(const float (&v)[kColsPerLane], uint3
         const float r = __builtin_amdgcn_rcpf(s);
         const bool tiny = s < 0x1p-100f;
         float q[kColsPerLane];
-        bool redo = tiny;
+        // e4m3_quot_near_boundary of any column, as two minima over the columns of its two keys, so the
+        // common path builds no per-column flags
+        uint32_t kmid = 0xFFFFFFFFu, ksmall = 0xFFFFFFFFu;
 #pragma unroll
         for (int i = 0; i < kColsPerLane; i++) {
             q[i] = v[i] * r;
-            redo = redo | e4m3_quot_near_boundary(q[i]);     // no short-circuit: no branch per column
+            const uint32_t b = __float_as_uint(q[i]);
+            kmid = __builtin_elementwise_min(kmid, (b << 12) + 0x80010000u);
+            ksmall = __builtin_elementwise_min(ksmall, (b << 1) - 2u);
         }
-        if (redo) {
+        if (tiny | (kmid < 0x21000u) | (ksmall < (0x3C800000u << 1) - 2u)) {
+            // rare: the columns are tested again one by one (the asm keeps the compiler from carrying the
+            // first tests' per-column results through the common path)
 #pragma unroll
-            for (int i = 0; i < kColsPerLane; i++)
-                if (tiny | e4m3_quot_near_boundary(q[i])) q[i] = v[i] / s;
+            for (int i = 0; i < kColsPerLane; i++) {
+                float qi = q[i];
+                asm volatile("" : "+v"(qi));
+                if (tiny | e4m3_quot_near_boundary(qi)) q[i] = v[i] / s;
+            }
         }
 #pragma unroll
         for (int k = 0; k < 4; k++) w[k] = enc4_e4m3(q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]);
@@ -113,9 +122,9 @@ __device__ __forceinline__ void quant_cols(const float (&v)[kColsPerLane], uint3
 
 // A segment of 1024 columns that lies inside the row, with 16-byte aligned loads: no per-column bounds;
 // the row bases are wave-uniform and each lane adds its own 32-bit offset.
-template <int DT, bool GATED>
+template <int DT, int ACT>
 __device__ __forceinline__ void act_quant_segment(const void* __restrict__ in, int64_t in_stride, int64_t rows,
-                                                  int64_t n, int act, int64_t seg, int lane,
+                                                  int64_t n, int64_t seg, int lane,
                                                   uint8_t* __restrict__ out_q, int64_t q_stride,
                                                   float* __restrict__ out_s, int64_t s_stride) {
     constexpr int64_t esz = DT == kF32 ? 4 : 2;
@@ -123,14 +132,14 @@ __device__ __forceinline__ void act_quant_segment(const void* __restrict__ in, i
     const uint32_t q_off = (uint32_t)(lane * kColsPerLane);
     for (int64_t row = blockIdx.y; row < rows; row += gridDim.y) {
         const char* rowp = (const char*)in + (row * in_stride + seg * kColsPerWave) * esz;
-        const RawCols<DT> raw = load_cols<DT, GATED>(rowp, lane_off, n * esz);
+        const RawCols<DT> raw = load_cols<DT, ACT != 0>(rowp, lane_off, n * esz);
         float v[kColsPerLane];
         unpack_cols<DT>(raw.g, v);
-        if constexpr (GATED) {
+        if constexpr (ACT != 0) {
             float u[kColsPerLane];
             unpack_cols<DT>(raw.u, u);
 #pragma unroll
-            for (int i = 0; i < kColsPerLane; i++) v[i] = gated_act(act, v[i], u[i]);
+            for (int i = 0; i < kColsPerLane; i++) v[i] = gated_act_t<ACT>(v[i], u[i]);
         }
         uint32_t w[4];
         float s;
@@ -189,9 +198,20 @@ act_quant_kernel(const void* __restrict__ in, int64_t in_stride, int64_t rows, i
     // grid), so no index needs an integer division; the segment is wave-uniform
     const int64_t seg = (int64_t)blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (seg * kColsPerWave >= n) return;
-    if (VEC && (seg + 1) * kColsPerWave <= n)
-        act_quant_segment<DT, GATED>(in, in_stride, rows, n, act, seg, lane, out_q, q_stride, out_s, s_stride);
-    else
+    if (VEC && (seg + 1) * kColsPerWave <= n) {
+        // one wave-uniform switch on the activation, outside the row and column loops
+        if constexpr (!GATED) {
+            act_quant_segment<DT, 0>(in, in_stride, rows, n, seg, lane, out_q, q_stride, out_s, s_stride);
+        } else {
+            switch (act) {
+                case 1: act_quant_segment<DT, 1>(in, in_stride, rows, n, seg, lane, out_q, q_stride, out_s, s_stride); break;
+                case 2: act_quant_segment<DT, 2>(in, in_stride, rows, n, seg, lane, out_q, q_stride, out_s, s_stride); break;
+                case 3: act_quant_segment<DT, 3>(in, in_stride, rows, n, seg, lane, out_q, q_stride, out_s, s_stride); break;
+                case 4: act_quant_segment<DT, 4>(in, in_stride, rows, n, seg, lane, out_q, q_stride, out_s, s_stride); break;
+                default: act_quant_segment<DT, 5>(in, in_stride, rows, n, seg, lane, out_q, q_stride, out_s, s_stride); break;
+            }
+        }
+    } else
         act_quant_segment_any<DT, GATED>(in, in_stride, rows, n, act, seg * kColsPerWave + (int64_t)lane * kColsPerLane,
                                          lane, out_q, q_stride, out_s, s_stride);
 }

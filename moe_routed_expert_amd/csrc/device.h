@@ -86,15 +86,36 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, float v) {
     else ((uint16_t*)p)[i] = f32_to_f16(v);
 }
 
+// sigmoid(g) = 1 / (1 + e^-g) from the hardware exp2 (v_exp_f32) of -g*log2(e) and the hardware reciprocal
+// (v_rcp_f32), each within an ulp: 4 instructions instead of a libm-accurate expf and a correctly rounded
+// division (about 22).  Limits: g = +inf gives 1, g = -inf and g below about -88.7 give 0 (e^-g overflows, as
+// in fp32 libm); between -88.7 and -87.3 the true value is below the fp32 normal range and the reciprocal
+// returns 0.
+__device__ __forceinline__ float fast_sigmoid(float g) {
+    const float t = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+    return __builtin_amdgcn_rcpf(1.0f + t);
+}
+
 // Gated activation of gate g and up u in fp32 (moe_act values 1..5: SwiGLU, GEGLU with the exact GELU,
 // ReGLU, GLU, bilinear -- the five GLU variants), one expression each in a fixed order of operations.
+// ACT is a compile-time constant here, so a loop over elements carries no per-element switch.
+template <int ACT>
+__device__ __forceinline__ float gated_act_t(float g, float u) {
+    if constexpr (ACT == 1) return (g * fast_sigmoid(g)) * u;
+    else if constexpr (ACT == 2) return (g * (0.5f * (1.0f + erff(g * 0.70710678118654752f)))) * u;
+    else if constexpr (ACT == 3) return (g > 0.0f ? g : 0.0f) * u;
+    else if constexpr (ACT == 4) return fast_sigmoid(g) * u;
+    else return g * u;
+}
+
+// The same with the activation chosen at run time (one wave-uniform switch per element).
 __device__ __forceinline__ float gated_act(int act, float g, float u) {
     switch (act) {
-        case 1: return (g / (1.0f + expf(-g))) * u;
-        case 2: return (g * (0.5f * (1.0f + erff(g * 0.70710678118654752f)))) * u;
-        case 3: return (g > 0.0f ? g : 0.0f) * u;
-        case 4: return (1.0f / (1.0f + expf(-g))) * u;
-        default: return g * u;
+        case 1: return gated_act_t<1>(g, u);
+        case 2: return gated_act_t<2>(g, u);
+        case 3: return gated_act_t<3>(g, u);
+        case 4: return gated_act_t<4>(g, u);
+        default: return gated_act_t<5>(g, u);
     }
 }
 

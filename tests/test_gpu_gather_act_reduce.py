@@ -246,7 +246,8 @@ def test_act_quant_silu_mul_within_one_step(orc, dtype, rows, n):
     hq, hs = q.cpu().numpy(), s.cpu().numpy()
     assert np.all(hq[0] == 0) and np.all(hs[0].view(np.uint32) == 0)   # zero tile stays exactly zero
     assert np.allclose(hs, ref_s, rtol=1e-6, atol=0)
-    # device expf may differ from libm by an ulp: codes differ by at most one step, rarely
+    # the device's sigmoid (hardware exp2 and reciprocal) is within a few ulp of libm's: codes differ by at
+    # most one step, rarely
     dec = lambda c: orc.e4m3_decode(c).astype(np.float64)
     diff = hq != ref_q
     assert diff.mean() < 2e-3
@@ -259,7 +260,8 @@ def test_act_quant_silu_mul_within_one_step(orc, dtype, rows, n):
 def test_act_quant_other_gated_activations(orc, act, dtype):
     """GEGLU, ReGLU, GLU and bilinear against the oracle on the same input: ReGLU and bilinear are exact
     fp32 products, so codes and scales match bit for bit; GEGLU and GLU go through the device erff/expf,
-    so scales match to a few ulp and a code may move by one e4m3 step, rarely."""
+    so scales match to a few ulp and a code may move by one e4m3 step, rarely (GLU's sigmoid is the
+    hardware exp2 and reciprocal)."""
     rows, n = 37, 640
     g = torch.Generator().manual_seed(rows + n + act)
     c1 = (torch.randn((rows, 2 * n), generator=g) * 2).to(dtype)
