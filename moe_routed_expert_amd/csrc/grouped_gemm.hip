@@ -211,6 +211,64 @@ __device__ __forceinline__ void act_quant_epilogue(const GgArgs& g, v4f (&acc)[B
 // One tile: rows [row0, min(row0 + BM, row_end)) of expert `expert`, N tile n_tile (256 output
 // columns, or act group n_tile when FUSED).  The caller's workgroup runs it with all threads; it
 // leaves LDS free for the next tile (its last LDS read is before its last barrier).
+// Two output values of a 2-byte type packed into one word, the first in the low half.
+template <int OUT_DT>
+__device__ __forceinline__ uint32_t pack2_out(float x, float y) {
+    if constexpr (OUT_DT == kBF16) return (uint32_t)f32_to_bf16(x) | ((uint32_t)f32_to_bf16(y) << 16);
+    else return (uint32_t)f32_to_f16(x) | ((uint32_t)f32_to_f16(y) << 16);
+}
+
+// The epilogue of a plain (not fused) tile: this wave's results acc[m][c] (row m*16 + lane%16 of the tile,
+// columns 16c + 4*(lane/16) + 0..3 of the wave's 32) go to out [rows][out_stride] of OUT_DT.  With a 2-byte
+// output whose rows allow it, a permlane32 swap and a permlane16 swap of each word pair (gfx950 lane moves)
+// leave lane 16q + r with columns 8q..8q+7 of row r, so each lane writes 16 bytes and each store covers 64
+// bytes of 16 rows: with the 32-byte pieces of 8-byte stores, a 24576-route gate/up GEMM's output stores cost
+// about 1.5 times as much memory time.  The swaps run in every lane (full exec), outside the row test.
+// SWAP = false keeps the 8-byte stores (a tile whose registers are at their limit).
+template <int OUT_DT, int MS, int TPW, bool SWAP = true>
+__device__ __forceinline__ void store_tile_out(const GgArgs& g, const v4f (&acc)[MS][TPW], int row0, int row_end,
+                                               int64_t col0, bool cols, int lane) {
+    void* __restrict__ out = g.out;
+    const int64_t out_stride = g.out_stride;
+    if constexpr (SWAP && OUT_DT != kF32 && TPW == 2) {
+        if (out_stride % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) {
+            const int tile_rows = __builtin_amdgcn_readfirstlane(row_end - row0);
+#pragma unroll
+            for (int m = 0; m < MS; m++) {
+                if (m * 16 >= tile_rows) break;            // sub-tiles past the tile's rows (wave-uniform)
+                const auto s0 = __builtin_amdgcn_permlane32_swap(pack2_out<OUT_DT>(acc[m][0][0], acc[m][0][1]),
+                                                                 pack2_out<OUT_DT>(acc[m][1][0], acc[m][1][1]), false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(pack2_out<OUT_DT>(acc[m][0][2], acc[m][0][3]),
+                                                                 pack2_out<OUT_DT>(acc[m][1][2], acc[m][1][3]), false, false);
+                const auto t0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+                const auto t1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+                const int row = row0 + m * 16 + (lane & 15);
+                if (cols && row < row_end)
+                    *reinterpret_cast<uint4*>((uint16_t*)out + (int64_t)row * out_stride + col0 + 8 * (lane / 16)) =
+                        make_uint4(t0[0], t1[0], t0[1], t1[1]);
+            }
+            return;
+        }
+    }
+    const bool vec4 = (out_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(out) % (OUT_DT == kF32 ? 16 : 8) == 0);
+#pragma unroll
+    for (int m = 0; m < MS; m++) {
+        const int row = row0 + m * 16 + (lane & 15);
+        if (cols && row < row_end) {
+            const int64_t o = (int64_t)row * out_stride + col0 + 4 * (lane / 16);
+#pragma unroll
+            for (int c = 0; c < TPW; c++) {
+                if (vec4) {
+                    store4_from_f32<OUT_DT>(out, o + 16 * c, acc[m][c]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) store_from_f32<OUT_DT>(out, o + 16 * c + i, acc[m][c][i]);
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int OUT_DT, bool FUSED, bool W4>
 __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, int row0, int row_end, int n_tile) {
     const uint8_t* __restrict__ a_q = g.a_q;
@@ -452,28 +510,9 @@ __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, i
         act_quant_epilogue<BM>(g, acc, row0, row_end, n_tile, lane, wave);
         return;
     }
-    // ---- epilogue: lane holds row m*16 + lane%16, columns 4*(lane/16) + i of each 16-column sub-tile,
-    // stored as one 4-element vector where the output allows it ----
-    void* __restrict__ out = g.out;
-    const int64_t out_stride = g.out_stride;
-    const bool vec4 = (out_stride % 4 == 0) &&
-                      (reinterpret_cast<uintptr_t>(out) % (OUT_DT == kF32 ? 16 : 8) == 0);
-#pragma unroll
-    for (int m = 0; m < MS; m++) {
-        const int row = row0 + m * 16 + (lane & 15);
-        if (cols && row < row_end) {
-            const int64_t o = (int64_t)row * out_stride + n0 + wave * CPW + 4 * (lane / 16);
-#pragma unroll
-            for (int c = 0; c < TPW; c++) {
-                if (vec4) {
-                    store4_from_f32<OUT_DT>(out, o + 16 * c, acc[m][c]);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; i++) store_from_f32<OUT_DT>(out, o + 16 * c + i, acc[m][c][i]);
-                }
-            }
-        }
-    }
+    // ---- epilogue: lane holds row m*16 + lane%16, columns 4*(lane/16) + i of each 16-column sub-tile (the
+    // 32-row block-FP8 tile, at 128 registers, keeps 8-byte stores: the swapped words would spill) ----
+    store_tile_out<OUT_DT, MS, TPW, !(BM == 32 && !W4)>(g, acc, row0, row_end, n0 + wave * CPW, cols, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -788,26 +827,7 @@ __device__ __forceinline__ void grouped_gemm_walk128(const GgArgs& g, const int*
         if constexpr (FUSED) {
             act_quant_epilogue<BM>(g, acc, cur.row0, cur.row_end, cur.n_tile, lane, wave);
         } else {
-            void* __restrict__ out = g.out;
-            const int64_t out_stride = g.out_stride;
-            const bool vec4 = (out_stride % 4 == 0) &&
-                              (reinterpret_cast<uintptr_t>(out) % (OUT_DT == kF32 ? 16 : 8) == 0);
-#pragma unroll
-            for (int m = 0; m < MS; m++) {
-                const int row = cur.row0 + m * 16 + (lane & 15);
-                if (cols && row < cur.row_end) {
-                    const int64_t o = (int64_t)row * out_stride + n0 + wave * CPW + 4 * (lane / 16);
-#pragma unroll
-                    for (int c = 0; c < TPW; c++) {
-                        if (vec4) {
-                            store4_from_f32<OUT_DT>(out, o + 16 * c, acc[m][c]);
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 4; i++) store_from_f32<OUT_DT>(out, o + 16 * c + i, acc[m][c][i]);
-                        }
-                    }
-                }
-            }
+            store_tile_out<OUT_DT, MS, TPW>(g, acc, cur.row0, cur.row_end, n0 + wave * CPW, cols, lane);
         }
         if (!has_next) return;
         commit_chunk(cn);                            // this wave's reads of the chunk ended with its last step
