@@ -89,32 +89,10 @@ __device__ __forceinline__ void quant_cols(const float (&v)[kColsPerLane], uint3
 #pragma unroll
     for (int k = 0; k < 4; k++) w[k] = 0u;
     if (s != 0.0f) {
-        // the quotients as v * rcp(s); the rare columns next to a code boundary (e4m3_quot_near_boundary)
-        // are redone with the exact division afterwards, all together, so the common path has no branch
-        // per column.  Below s = 2^-100, rcp(s) may not be finite: every column takes the division.
-        const float r = __builtin_amdgcn_rcpf(s);
-        const bool tiny = s < 0x1p-100f;
+        // the quotients as v * rcp(s), the rare ones next to a code boundary redone by the exact division
+        // (e4m3_quotients), so the common path has no branch per column
         float q[kColsPerLane];
-        // e4m3_quot_near_boundary of any column, as two minima over the columns of its two keys, so the
-        // common path builds no per-column flags
-        uint32_t kmid = 0xFFFFFFFFu, ksmall = 0xFFFFFFFFu;
-#pragma unroll
-        for (int i = 0; i < kColsPerLane; i++) {
-            q[i] = v[i] * r;
-            const uint32_t b = __float_as_uint(q[i]);
-            kmid = __builtin_elementwise_min(kmid, (b << 12) + 0x80010000u);
-            ksmall = __builtin_elementwise_min(ksmall, (b << 1) - 2u);
-        }
-        if (tiny | (kmid < 0x21000u) | (ksmall < (0x3C800000u << 1) - 2u)) {
-            // rare: the columns are tested again one by one (the asm keeps the compiler from carrying the
-            // first tests' per-column results through the common path)
-#pragma unroll
-            for (int i = 0; i < kColsPerLane; i++) {
-                float qi = q[i];
-                asm volatile("" : "+v"(qi));
-                if (tiny | e4m3_quot_near_boundary(qi)) q[i] = v[i] / s;
-            }
-        }
+        e4m3_quotients(v, s, q);
 #pragma unroll
         for (int k = 0; k < 4; k++) w[k] = enc4_e4m3(q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]);
     }

@@ -48,6 +48,33 @@ __device__ __forceinline__ bool e4m3_quot_near_boundary(float q) {
     return mid | small;
 }
 
+// q[i] = RN(v[i] / s) as far as its e4m3 code goes, for N values sharing the scale s > 0: v * rcp(s), with
+// the rare quotients near a code boundary redone by the exact division (below s = 2^-100, where rcp(s) may
+// not be finite, all of them).  The common path tests the columns as two minima over e4m3_quot_near_boundary's
+// two keys, so it builds no per-column flags; the rare path tests them again one by one (the asm keeps the
+// compiler from carrying the first tests' per-column results through the common path).
+template <int N>
+__device__ __forceinline__ void e4m3_quotients(const float (&v)[N], float s, float (&q)[N]) {
+    const float r = __builtin_amdgcn_rcpf(s);
+    const bool tiny = s < 0x1p-100f;
+    uint32_t kmid = 0xFFFFFFFFu, ksmall = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        q[i] = v[i] * r;
+        const uint32_t b = __float_as_uint(q[i]);
+        kmid = __builtin_elementwise_min(kmid, (b << 12) + 0x80010000u);
+        ksmall = __builtin_elementwise_min(ksmall, (b << 1) - 2u);
+    }
+    if (tiny | (kmid < 0x21000u) | (ksmall < (0x3C800000u << 1) - 2u)) {
+#pragma unroll
+        for (int i = 0; i < N; i++) {
+            float qi = q[i];
+            asm volatile("" : "+v"(qi));
+            if (tiny | e4m3_quot_near_boundary(qi)) q[i] = v[i] / s;
+        }
+    }
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float((uint32_t)h << 16);
 }

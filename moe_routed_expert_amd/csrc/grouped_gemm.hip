@@ -163,20 +163,20 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* ldsw) {
 // Fused epilogue: acc[m][0] holds gate and acc[m][1] up for row m*16 + lane%16, act columns
 // 128*n_tile + 16*wave + 4*(lane/16) + i.  h = act(gate)*up in fp32; per row, the amax of the 128
 // columns (4 lanes by shuffle, then the 8 waves through LDS), s = amax/448 (correctly rounded), codes
-// e4m3(h/s) (zero codes when s == 0).
-template <int BM>
-__device__ __forceinline__ void act_quant_epilogue(const GgArgs& g, v4f (&acc)[BM / 16][2], int row0, int row_end,
-                                                   int n_tile, int lane, int wave) {
+// e4m3(h/s) (zero codes when s == 0) with moe_act_quant's quotients (e4m3_quotients), so the codes are
+// the same bits.  ACT is fixed per instantiation: no per-element switch.
+template <int BM, int ACT>
+__device__ __forceinline__ void act_quant_epilogue_t(const GgArgs& g, v4f (&acc)[BM / 16][2], int row0, int row_end,
+                                                     int n_tile, int lane, int wave, float (*amax_lds)[BM]) {
     using C = GgCfg<BM>;
     constexpr int MS = BM / 16;
-    __shared__ float amax_lds[C::WAVES][BM];
 #pragma unroll
     for (int m = 0; m < MS; m++) {
         float a = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const float gt = acc[m][0][i], up = acc[m][1][i];
-            acc[m][0][i] = gated_act(g.act, gt, up);             // h replaces gate
+            acc[m][0][i] = gated_act_t<ACT>(gt, up);             // h replaces gate
             a = __builtin_fmaxf(a, __builtin_fabsf(acc[m][0][i]));
         }
         a = __builtin_fmaxf(a, __shfl_xor(a, 16, kWave));
@@ -192,8 +192,13 @@ __device__ __forceinline__ void act_quant_epilogue(const GgArgs& g, v4f (&acc)[B
 #pragma unroll
         for (int w = 1; w < C::WAVES; w++) amax = __builtin_fmaxf(amax, amax_lds[w][rl]);
         const float s = amax / 448.0f;
-        const v4f h = acc[m][0];
-        const uint32_t code = s != 0.0f ? enc4_e4m3(h[0] / s, h[1] / s, h[2] / s, h[3] / s) : 0u;
+        uint32_t code = 0u;
+        if (s != 0.0f) {
+            const float h[4] = {acc[m][0][0], acc[m][0][1], acc[m][0][2], acc[m][0][3]};
+            float q[4];
+            e4m3_quotients(h, s, q);
+            code = enc4_e4m3(q[0], q[1], q[2], q[3]);
+        }
         const int row = row0 + rl;
         if (row < row_end) {
             uint8_t* q = g.q + (int64_t)row * g.q_stride + (int64_t)n_tile * 128 + 16 * wave + 4 * (lane / 16);
@@ -208,9 +213,20 @@ __device__ __forceinline__ void act_quant_epilogue(const GgArgs& g, v4f (&acc)[B
     }
 }
 
-// One tile: rows [row0, min(row0 + BM, row_end)) of expert `expert`, N tile n_tile (256 output
-// columns, or act group n_tile when FUSED).  The caller's workgroup runs it with all threads; it
-// leaves LDS free for the next tile (its last LDS read is before its last barrier).
+// The fused epilogue with the activation chosen once per tile (wave-uniform).
+template <int BM>
+__device__ __forceinline__ void act_quant_epilogue(const GgArgs& g, v4f (&acc)[BM / 16][2], int row0, int row_end,
+                                                   int n_tile, int lane, int wave) {
+    __shared__ float amax_lds[GgCfg<BM>::WAVES][BM];     // one table for all five forms
+    switch (g.act) {
+        case 1: act_quant_epilogue_t<BM, 1>(g, acc, row0, row_end, n_tile, lane, wave, amax_lds); break;
+        case 2: act_quant_epilogue_t<BM, 2>(g, acc, row0, row_end, n_tile, lane, wave, amax_lds); break;
+        case 3: act_quant_epilogue_t<BM, 3>(g, acc, row0, row_end, n_tile, lane, wave, amax_lds); break;
+        case 4: act_quant_epilogue_t<BM, 4>(g, acc, row0, row_end, n_tile, lane, wave, amax_lds); break;
+        default: act_quant_epilogue_t<BM, 5>(g, acc, row0, row_end, n_tile, lane, wave, amax_lds); break;
+    }
+}
+
 // Two output values of a 2-byte type packed into one word, the first in the low half.
 template <int OUT_DT>
 __device__ __forceinline__ uint32_t pack2_out(float x, float y) {
@@ -269,6 +285,9 @@ __device__ __forceinline__ void store_tile_out(const GgArgs& g, const v4f (&acc)
     }
 }
 
+// One tile: rows [row0, min(row0 + BM, row_end)) of expert `expert`, N tile n_tile (256 output
+// columns, or act group n_tile when FUSED).  The caller's workgroup runs it with all threads; it
+// leaves LDS free for the next tile (its last LDS read is before its last barrier).
 template <int BM, int OUT_DT, bool FUSED, bool W4>
 __device__ __forceinline__ void grouped_gemm_tile(const GgArgs& g, int expert, int row0, int row_end, int n_tile) {
     const uint8_t* __restrict__ a_q = g.a_q;
