@@ -100,6 +100,43 @@ def test_grouped_gemm_vs_oracle(orc, bm, odt):
     assert_close(got[:R], ref_as_f64(ref, odt), what="grouped gemm")
 
 
+@pytest.mark.parametrize("w4", [False, True])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+def test_grouped_gemm_2byte_outputs_are_the_rounded_f32(bm, w4):
+    """bf16 and f16 outputs equal torch's round-to-nearest-even of the same launch's f32 output, bit for bit,
+    at an output row stride that takes the 16-byte stores (lane swaps), one that takes 8-byte stores and
+    one that takes 2-byte stores; N = 384 leaves the second 256-column tile half empty, and nothing outside
+    the output is written."""
+    E, N, K = 5, 384, 512
+    counts = [3, 0, 40, 129, 17]
+    print("2-byte outputs BM=%d %s" % (bm, "mxfp4" if w4 else "bf8"), flush=True)
+    offs = np.zeros(E + 1, np.int32)
+    offs[1:] = np.cumsum(counts)
+    R = int(offs[-1])
+    a_q, a_s = wl.fp8_rows(R, K, seed=71 + bm, full_range=True)
+    aq, as_, od = a_q.to(dev()), a_s.to(dev()), to_dev(offs)
+    if w4:
+        w, ws = wl.mxfp4_weights(E, N, K, seed=72 + bm)
+        w, ws = w.to(dev()), ws.to(dev())
+        run = lambda out: m.mxfp4_grouped_gemm(aq, as_, w, ws, od, out, m_rows=R, block_m=bm)
+    else:
+        w, ws = wl.block_fp8_weights(E, N, K, seed=72 + bm)
+        w, ws = w.to(dev()), ws.to(dev())
+        run = lambda out: m.bf8_grouped_gemm(aq, as_, w, ws, out, mode=m.MOE_MODE_GROUPED, expert_offsets=od,
+                                             m_rows=R, block_m=bm)
+    ref = torch.empty((R, N), dtype=torch.float32, device=dev())
+    run(ref)
+    for odt in (torch.bfloat16, torch.float16):
+        want = ref.to(odt)
+        for pad in (0, 4, 1):
+            big = torch.full((R + 2, N + pad), float("nan"), dtype=odt, device=dev())
+            out = big[:R, :N]
+            run(out)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), want.view(torch.int16)), (odt, pad)
+            assert torch.all(torch.isnan(big[:, N:])) and torch.all(torch.isnan(big[R:])), (odt, pad)
+
+
 def test_grouped_gemm_integer_case_bit_exact(orc):
     E, N, K = 4, 384, 640
     counts = [20, 1, 0, 33]
