@@ -22,7 +22,8 @@
 //  * Per K step: p = W*A^T with a fresh 16x16x128 e4m3 MFMA (weights as the
 //    row operand, so a lane's four results are four columns of one A row),
 //    then acc += p * (a_s[row][kb] * w_s[kb]) in fp32 with one scale per lane;
-//    the epilogue stores the four columns as one vector.  All scales of the tile are
+//    the epilogue stores the four columns as one vector, or, for a 2-byte
+//    output, eight columns after two lane swaps (store_tile_out).  All scales of the tile are
 //    staged in LDS before the loop, and the loop issues no load behind a
 //    branch: vector loads retire in order, so a late small load or a load the
 //    compiler cannot count would make a step wait for every load in flight.
@@ -52,8 +53,8 @@
 //    of W13, so a lane holds gate and up of the same four columns of one row and
 //    forms h = act(gate)*up from the fp32 accumulators.  The group amax is a
 //    lane shuffle plus an 8-wave LDS max, then s = amax/448 and the codes
-//    e4m3(h/s) leave as one 4-byte store per lane; the [rows][2I] GEMM output
-//    is never written.
+//    e4m3(h/s) (moe_act_quant's quotients) leave as one 4-byte store per lane;
+//    the [rows][2I] GEMM output is never written.
 #include <atomic>
 
 #include "device.h"
