@@ -192,7 +192,8 @@ int moe_grouped_block_m(int64_t routes, int64_t experts, int64_t K, int mxfp4, i
  *        (DEVICE int32 [m_rows]) and A row r / a_row_div; a negative slot
  *        writes a +0 output row and reads no A, W or scales of that row.
  *        Meant for decode-sized row counts (every row streams its expert).
- *   Requirements: K % 128 == 0, N % 16 == 0; w_q, a_q and their strides
+ *   Requirements: K % 128 == 0, N % 16 == 0, m_rows <= 2^31 - 1 (every
+ *   grouped entry point: MOE_ERR_SHAPE beyond); w_q, a_q and their strides
  *   16-byte aligned (MOE_ERR_ALIGN otherwise).  Grouped mode also needs
  *   N % 128 == 0, 1 <= n_experts <= 1024 and K <= 8192 (a tile keeps all its
  *   K-block scales in LDS); MOE_ERR_SHAPE otherwise.  n_experts == 0 with NULL

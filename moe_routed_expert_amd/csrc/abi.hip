@@ -174,7 +174,7 @@ extern "C" int moe_bf8_grouped_gemm(const uint8_t* a_q, int64_t a_stride, const 
                                     void* out, int out_dt, int64_t out_stride, void* stream) {
     if (mode != MOE_MODE_GROUPED && mode != MOE_MODE_SLOT) return MOE_ERR_SHAPE;
     if (!dtype_ok(out_dt)) return MOE_ERR_DTYPE;
-    if (m_rows < 0 || n_experts < 0 || N <= 0 || K <= 0) return MOE_ERR_SHAPE;
+    if (m_rows < 0 || m_rows > 0x7FFFFFFF || n_experts < 0 || N <= 0 || K <= 0) return MOE_ERR_SHAPE;
     if (K % 128 != 0 || N % 16 != 0) return MOE_ERR_SHAPE;
     if (m_rows == 0) return MOE_OK;
     if (!out) return MOE_ERR_NULL;
@@ -215,7 +215,8 @@ extern "C" int moe_bf8_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_stri
                                               const int32_t* expert_offsets, int64_t m_rows, int32_t block_m,
                                               int act, uint8_t* out_q, int64_t q_stride, float* out_s,
                                               int64_t s_stride, void* stream) {
-    if (m_rows < 0 || n_experts < 1 || n_experts > 1024 || I < 128 || I % 128 || K < 128 || K % 128 || K > 8192)
+    if (m_rows < 0 || m_rows > 0x7FFFFFFF || n_experts < 1 || n_experts > 1024 || I < 128 || I % 128 || K < 128 ||
+        K % 128 || K > 8192)
         return MOE_ERR_SHAPE;
     if (act < MOE_ACT_SILU_MUL || act > MOE_ACT_MUL) return MOE_ERR_SHAPE;
     if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_SHAPE;
@@ -260,7 +261,8 @@ extern "C" int moe_mxfp4_grouped_gemm(const uint8_t* a_q, int64_t a_stride, cons
                                       int64_t m_rows, int32_t block_m, void* out, int out_dt, int64_t out_stride,
                                       void* stream) {
     if (!dtype_ok(out_dt)) return MOE_ERR_DTYPE;
-    if (m_rows < 0 || n_experts < 1 || n_experts > 1024 || N < 128 || N % 128 || K < 128 || K % 128 || K > 8192)
+    if (m_rows < 0 || m_rows > 0x7FFFFFFF || n_experts < 1 || n_experts > 1024 || N < 128 || N % 128 || K < 128 ||
+        K % 128 || K > 8192)
         return MOE_ERR_SHAPE;
     if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_SHAPE;
     if (m_rows == 0) return MOE_OK;
@@ -282,7 +284,8 @@ extern "C" int moe_mxfp4_grouped_gemm_act_quant(const uint8_t* a_q, int64_t a_st
                                                 const int32_t* expert_offsets, int64_t m_rows, int32_t block_m,
                                                 int act, uint8_t* out_q, int64_t q_stride, float* out_s,
                                                 int64_t s_stride, void* stream) {
-    if (m_rows < 0 || n_experts < 1 || n_experts > 1024 || I < 128 || I % 128 || K < 128 || K % 128 || K > 8192)
+    if (m_rows < 0 || m_rows > 0x7FFFFFFF || n_experts < 1 || n_experts > 1024 || I < 128 || I % 128 || K < 128 ||
+        K % 128 || K > 8192)
         return MOE_ERR_SHAPE;
     if (act < MOE_ACT_SILU_MUL || act > MOE_ACT_MUL) return MOE_ERR_SHAPE;
     if (block_m != 0 && block_m != 16 && block_m != 32 && block_m != 64 && block_m != 128) return MOE_ERR_SHAPE;

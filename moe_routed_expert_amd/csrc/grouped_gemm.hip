@@ -962,7 +962,8 @@ static int launch_grouped_walk(hipStream_t st, GgArgs g) {
     using C = GgCfg<BM>;
     if (g.N % 128 != 0 || (FUSED && g.N % 256 != 0)) return MOE_ERR_SHAPE;
     const int64_t n_tiles_n = FUSED ? g.N / 256 : ceil_div(g.N, C::BN);
-    if (g.m_rows > 0x7FFFFFFF || n_tiles_n * (ceil_div(g.m_rows, BM) + g.n_experts) > 0x7FFFFFFF - (1 << 20))
+    // m_rows fits an int (the entry points reject more); the tile count must too
+    if (n_tiles_n * (ceil_div((int64_t)g.m_rows, BM) + g.n_experts) > 0x7FFFFFFF - (1 << 20))
         return MOE_ERR_SHAPE;
     const int wgs = gg_resident_blocks<BM, OUT_DT, FUSED, W4, WALK>();
     if (wgs < kXcds) return MOE_ERR_HIP;

@@ -100,6 +100,12 @@ def test_gemm_argument_checks():
                  w_s_stride_e=2 * 65)
     assert gemm(mode=0, **big_k) == m.MOE_ERR_SHAPE          # grouped mode keeps K/128 <= 64 scales per tile
     assert gemm(mode=0, n_experts=1025, **big_k) == m.MOE_ERR_SHAPE
+    # more rows than an int holds: rejected before any row count is narrowed (both modes)
+    assert gemm(m_rows=2 ** 31) == m.MOE_ERR_SHAPE
+    assert gemm(mode=0, m_rows=2 ** 31 + 5) == m.MOE_ERR_SHAPE
+    L = m.lib()
+    assert L.moe_bf8_grouped_gemm_act_quant(FAKE, 256, FAKE, 2, FAKE, 256 * 256, 256, FAKE, 4, 2, 4, 128, 256, FAKE,
+                                            2 ** 31, 0, 1, FAKE, 128, FAKE, 1, None) == m.MOE_ERR_SHAPE
 
 
 def test_gather_act_reduce_argument_checks():
