@@ -397,7 +397,7 @@ int moe_route_prep(const float* logits, int64_t logits_stride, int64_t T, int64_
  *   w13_q [n_slots][2I][H] fp8 (gate rows 0..I-1, up rows I..2I-1), contiguous;
  *   w13_s [n_slots][ceil(2I/128)][ceil(H/128)] fp32;  w2_q [n_slots][H][I];
  *   w2_s [n_slots][ceil(H/128)][ceil(I/128)].
- *   Requirements: H % 128 == 0, I % 128 == 0, 1 <= topk <= 64,
+ *   Requirements: H % 128 == 0, I % 128 == 0, H and I <= 65536, 1 <= topk <= 64,
  *   T * topk <= 65535; 16-byte aligned weights and workspace, 4-byte aligned x.
  *   Launch shapes depend on (T, H, I, topk) and the device only, so one
  *   captured graph serves any slot/weight/x contents.  For small steps

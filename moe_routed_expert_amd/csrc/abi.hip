@@ -90,8 +90,8 @@ int weight_bank_ok(const uint8_t* w, int64_t w_stride_e, int64_t w_stride_n, int
 }
 
 bool decode_shape_ok(int64_t T, int64_t H, int64_t I, int64_t topk) {
-    return T >= 0 && H > 0 && I > 0 && topk >= 1 && topk <= 64 && H % 128 == 0 && I % 128 == 0 &&
-           T * topk <= 65535;
+    return T >= 0 && H > 0 && I > 0 && H <= 65536 && I <= 65536 && topk >= 1 && topk <= 64 && H % 128 == 0 &&
+           I % 128 == 0 && T * topk <= 65535;
 }
 
 // Scratch of moe_fused_decode_noalloc: a fixed device array standing in for the caller's workspace.  Each

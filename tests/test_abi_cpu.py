@@ -134,6 +134,8 @@ def test_fused_decode_workspace_and_checks():
     assert lay["total"] == m.fused_decode_workspace_size(1, 2048, 768, 8)
     assert all(v % 256 == 0 for v in lay.values())
     assert m.fused_decode_workspace_size(1, 2000, 768, 8) == 0          # H % 128
+    assert m.fused_decode_workspace_size(1, 2 ** 31, 768, 8) == 0       # H beyond 65536
+    assert m.fused_decode_workspace_size(1, 2048, 65536 + 128, 8) == 0  # I beyond 65536
     assert m.fused_decode_workspace_size(1, 2048, 768, 0) == 0          # topk >= 1
     size = lay["total"]
     args = [FAKE, 1, 2048, 768, 8, 1, FAKE, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, size, FAKE, None]
