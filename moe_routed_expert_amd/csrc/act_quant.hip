@@ -11,10 +11,8 @@
 // MI355X design: one wavefront per (row, 1024 columns), from a 2D grid (column
 // groups x rows, rows taken in strides beyond 65535) so no index needs an
 // integer division.  Each lane owns 16 consecutive columns: the per-group
-// scale, reciprocal and amax and the addressing (a wave-uniform row base plus a
-// 32-bit lane offset) are shared by 16 codes, and the exact-quotient test is
-// two integer operations per column, so VALU issue is well under the kernel's
-// time (instruction counters).  Waves that took 2, 4 or 8 rows with all their
+// scale, refined reciprocal and amax and the addressing (a wave-uniform row
+// base plus a 32-bit lane offset) are shared by 16 codes.  Waves that took 2, 4 or 8 rows with all their
 // loads in flight at once, or that requested the next row while quantizing the
 // current one (fewer, longer-lived workgroups), ran slower, not faster: the
 // kernel is bound by how many waves have loads in flight (it runs at 83-89 %
@@ -27,9 +25,9 @@
 // 16-byte store.  The scale is amax/448 with
 // the correctly rounded fp32 division and each code is that of v/s rounded to
 // nearest even (clamped to +-448), matching the definition bit for bit in
-// IDENTITY mode; the quotient is v * rcp(s) except near a code boundary, where
-// it is the exact division (e4m3_quotients), so one division per lane replaces
-// sixteen.
+// IDENTITY mode; the quotients take the correctly rounded division's own steps
+// without its range scaling (e4m3_codes: 5 operations each, no branch per
+// column), which give the same codes.
 #include "device.h"
 #include "host.h"
 
@@ -92,14 +90,8 @@ __device__ __forceinline__ void quant_cols(const float (&v)[kColsPerLane], uint3
     s = amax / 448.0f;
 #pragma unroll
     for (int k = 0; k < 4; k++) w[k] = 0u;
-    if (s != 0.0f) {
-        // the quotients as v * rcp(s), the rare ones next to a code boundary redone by the exact division
-        // (e4m3_quotients), so the common path has no branch per column
-        float q[kColsPerLane];
-        e4m3_quotients(v, s, q);
-#pragma unroll
-        for (int k = 0; k < 4; k++) w[k] = enc4_e4m3(q[4 * k], q[4 * k + 1], q[4 * k + 2], q[4 * k + 3]);
-    }
+    // the codes of RN(v / s) (e4m3_codes), no branch per column
+    if (s != 0.0f) e4m3_codes(v, s, w);
 }
 
 // A segment of 1024 columns that lies inside the row, with 16-byte aligned loads: no per-column bounds;

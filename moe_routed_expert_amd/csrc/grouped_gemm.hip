@@ -164,7 +164,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* ldsw) {
 // Fused epilogue: acc[m][0] holds gate and acc[m][1] up for row m*16 + lane%16, act columns
 // 128*n_tile + 16*wave + 4*(lane/16) + i.  h = act(gate)*up in fp32; per row, the amax of the 128
 // columns (4 lanes by shuffle, then the 8 waves through LDS), s = amax/448 (correctly rounded), codes
-// e4m3(h/s) (zero codes when s == 0) with moe_act_quant's quotients (e4m3_quotients), so the codes are
+// e4m3(h/s) (zero codes when s == 0) with moe_act_quant's e4m3_codes, so the codes are
 // the same bits.  ACT is fixed per instantiation: no per-element switch.
 template <int BM, int ACT>
 __device__ __forceinline__ void act_quant_epilogue_t(const GgArgs& g, v4f (&acc)[BM / 16][2], int row0, int row_end,
@@ -193,21 +193,19 @@ __device__ __forceinline__ void act_quant_epilogue_t(const GgArgs& g, v4f (&acc)
 #pragma unroll
         for (int w = 1; w < C::WAVES; w++) amax = __builtin_fmaxf(amax, amax_lds[w][rl]);
         const float s = amax / 448.0f;
-        uint32_t code = 0u;
+        uint32_t code[1] = {0u};
         if (s != 0.0f) {
             const float h[4] = {acc[m][0][0], acc[m][0][1], acc[m][0][2], acc[m][0][3]};
-            float q[4];
-            e4m3_quotients(h, s, q);
-            code = enc4_e4m3(q[0], q[1], q[2], q[3]);
+            e4m3_codes(h, s, code);
         }
         const int row = row0 + rl;
         if (row < row_end) {
             uint8_t* q = g.q + (int64_t)row * g.q_stride + (int64_t)n_tile * 128 + 16 * wave + 4 * (lane / 16);
             if (vec) {
-                *reinterpret_cast<uint32_t*>(q) = code;
+                *reinterpret_cast<uint32_t*>(q) = code[0];
             } else {
 #pragma unroll
-                for (int i = 0; i < 4; i++) q[i] = (uint8_t)(code >> (8 * i));
+                for (int i = 0; i < 4; i++) q[i] = (uint8_t)(code[0] >> (8 * i));
             }
             if (wave == 0 && lane < 16) g.s[(int64_t)row * g.s_stride + n_tile] = s;
         }
