@@ -190,8 +190,8 @@ def test_act_quant_identity_rounding_edges(orc):
 
 def test_act_quant_identity_quotients_near_code_boundaries(orc):
     """Groups with arbitrary scales whose values divide to within a few ulp of an e4m3 rounding midpoint
-    (and to midpoints exactly): the kernel's quotient shortcut must give the same codes as the exact
-    division, bit for bit."""
+    (and to midpoints exactly): the kernel's quotients (the division's steps without its range scaling)
+    must give the codes of the correctly rounded division, bit for bit."""
     rng = np.random.default_rng(5)
     rows, n = 64, 1024
     codes = np.arange(0, 0x7F, dtype=np.uint8)
