@@ -315,7 +315,7 @@ def gather_bench(torch, m, wl, k, tokens, topk, reps):
     gr = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gr, stream=torch.cuda.Stream()):
         run_all()
-    settle(torch, gr.replay)
+    n_settle = settle(torch, gr.replay)
     t = Timer(torch)
     for _ in range(reps):
         t.start()
@@ -325,7 +325,7 @@ def gather_bench(torch, m, wl, k, tokens, topk, reps):
     row = k + 4 * sets[0][1].shape[1]
     mp = sets[0][5]
     nbytes = len(mp) * row + len(set(mp.tolist())) * row
-    return dict(k=k, tokens=tokens, rows=len(mp), us_per_call=us, bytes=nbytes,
+    return dict(k=k, tokens=tokens, rows=len(mp), us_per_call=us, bytes=nbytes, settle_replays=n_settle, timed_replays=reps,
                 gbs=nbytes / (us * 1e-6) / 1e9, hbm_frac=nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS)
 
 
@@ -360,8 +360,8 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
     for name, (a_q, a_s, w_q, w_s, c, N, K) in {
             "gate_up": (a1_q, a1_s, w13_q, w13_s, c1, 2 * I, H),
             "down": (a2_q, a2_s, w2_q, w2_s, c2, H, I)}.items():
-        settle(torch, lambda: m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c, mode=m.MOE_MODE_GROUPED, expert_offsets=offs,
-                                                 w_packed=packed))
+        n_settle = settle(torch, lambda: m.bf8_grouped_gemm(a_q, a_s, w_q, w_s, c, mode=m.MOE_MODE_GROUPED,
+                                                            expert_offsets=offs, w_packed=packed))
         t = Timer(torch)
         for _ in range(steps):          # 2-3 GB of weights per call: cold by construction
             t.start()
@@ -375,12 +375,13 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
         attainable = min(FP8_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1000.0)
         out[name] = dict(us_median=us, tflops=tflops, fp8_peak_frac=tflops / FP8_PEAK_TFLOPS,
                          roofline_frac=tflops / attainable, arithmetic_intensity=ai, bytes=nbytes,
-                         hbm_gbs=nbytes / (us * 1e-6) / 1e9)
+                         hbm_gbs=nbytes / (us * 1e-6) / 1e9, settle_calls=n_settle, timed_calls=steps)
     # gate/up with the SiLU-mul requant fused into its epilogue, against the unfused pair (gate/up above
     # writing bf16 c1, then act_quant reading it)
     aq = torch.empty((R, I), dtype=torch.uint8, device=dev)
     as_ = torch.empty((R, I // 128), dtype=torch.float32, device=dev)
-    settle(torch, lambda: m.bf8_grouped_gemm_act_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_, w_packed=packed))
+    n_settle_f = settle(torch, lambda: m.bf8_grouped_gemm_act_quant(a1_q, a1_s, w13_q, w13_s, offs, aq, as_,
+                                                                   w_packed=packed))
     t = Timer(torch)
     for _ in range(steps):
         t.start()
@@ -396,7 +397,8 @@ def prefill_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=False):
     us_a = statistics.median(t.us())
     flops = 2.0 * R * 2 * I * H
     out["gate_up_act_quant"] = dict(us_median=us_f, tflops=flops / (us_f * 1e-6) / 1e12,
-                                     unfused_us=out["gate_up"]["us_median"] + us_a, act_quant_us=us_a)
+                                     unfused_us=out["gate_up"]["us_median"] + us_a, act_quant_us=us_a,
+                                     settle_calls=n_settle_f, timed_calls=steps)
     return dict(routes=R, experts=E, topk=topk, H=H, I=I, block_m=bm,
                 block_m_fused=m.grouped_block_m(R, E, H, packed=packed, fused=True),
                 block_m_down=m.grouped_block_m(R, E, I, packed=packed), **out)
@@ -427,7 +429,7 @@ def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=F
     }
     out = {}
     for name, (fn, N, K, out_bytes) in calls.items():
-        settle(torch, fn)
+        n_settle = settle(torch, fn)
         t = Timer(torch)
         for _ in range(steps):
             t.start()
@@ -441,7 +443,7 @@ def prefill_mxfp4_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=F
         attainable = min(FP8_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1000.0)
         out[name] = dict(us_median=us, tflops=tflops, fp8_peak_frac=tflops / FP8_PEAK_TFLOPS,
                          roofline_frac=tflops / attainable, arithmetic_intensity=ai, bytes=nbytes,
-                         hbm_gbs=nbytes / (us * 1e-6) / 1e9)
+                         hbm_gbs=nbytes / (us * 1e-6) / 1e9, settle_calls=n_settle, timed_calls=steps)
     return dict(routes=R, experts=E, topk=topk, H=H, I=I,
                 block_m=m.grouped_block_m(R, E, H, mxfp4=True, packed=packed),
                 block_m_fused=m.grouped_block_m(R, E, H, mxfp4=True, packed=packed, fused=True),
@@ -485,7 +487,7 @@ def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=F
         m.bf8_grouped_gemm(aq, as_, w2_q, w2_s, c2, mode=m.MOE_MODE_GROUPED, expert_offsets=offs, w_packed=packed)
         m.topk_reduce(c2, ids, w, out, route_rows=rr)
 
-    settle(torch, layer)
+    n_settle = settle(torch, layer)
     t = Timer(torch)
     for _ in range(steps):
         t.start()
@@ -494,7 +496,8 @@ def prefill_layer_bench(torch, m, wl, T, E, topk, H, I, steps, weights, packed=F
     us = statistics.median(t.us())
     flops = 2.0 * R * (2 * I * H + H * I)
     return dict(tokens=T, routes=R, experts=E, topk=topk, H=H, I=I, us_per_layer=us,
-                gemm_tflops=flops / (us * 1e-6) / 1e12, routing="uniform (iid N(0,1) logits)")
+                gemm_tflops=flops / (us * 1e-6) / 1e12, routing="uniform (iid N(0,1) logits)",
+                settle_calls=n_settle, timed_calls=steps)
 
 
 def prefill_all(torch, m, wl):
@@ -610,7 +613,7 @@ def route_prep_bench(torch, m, wl, T, E, topk, reps):
     gr = torch.cuda.CUDAGraph()
     with torch.cuda.graph(gr, stream=torch.cuda.Stream()):
         run_all()
-    settle(torch, gr.replay)
+    n_settle = settle(torch, gr.replay)
     t = Timer(torch)
     for _ in range(reps):
         t.start()
@@ -618,7 +621,8 @@ def route_prep_bench(torch, m, wl, T, E, topk, reps):
         t.stop()
     us = statistics.median(t.us()) / LAYERS
     nbytes = T * E * 4 + T * topk * (4 + 4 + 4 + 4) + T * topk * 4
-    return dict(tokens=T, experts=E, topk=topk, us_per_call=us, bytes=nbytes, gbs=nbytes / (us * 1e-6) / 1e9)
+    return dict(tokens=T, experts=E, topk=topk, us_per_call=us, bytes=nbytes, gbs=nbytes / (us * 1e-6) / 1e9,
+                settle_replays=n_settle, timed_replays=reps)
 
 
 def cpu_model():
