@@ -44,7 +44,9 @@ namespace moe {
 
 constexpr int kFdTile = 16;
 constexpr int kFdWaves = 8;
-constexpr int kFdUnroll = 1;          // K blocks per batch of the two-launch gate/up waves (1: four paced batches at H = 4096)
+// K blocks per batch of a gate/up wave, in both step forms: paced requests of one block finish the full
+// W13 flood sooner at 8/8 active, at some cost with fewer routes active
+constexpr int kFdUnroll = 1;
 constexpr int kFdMaxNkb2 = 8;          // I/128 handled with W2 rows held in registers
 constexpr int kDnRows = 8;             // W2 rows per narrow down tile
 constexpr int kWideDownTiles = 256;    // 16-row down tiles from this many tiles per step on (one per CU)
